@@ -1,0 +1,227 @@
+/*
+ * CPU oracle of the routed MoE FFN layer — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this; the product path never does.  It shares no code, header, table
+ * or constant with the HIP library.
+ *
+ * Plain loops, fp64 throughout, fixed ascending reduction order, built with
+ * -ffp-contract=off so no multiply-add is fused (the pages' kimi-k3-in-c
+ * engine pins its bits the same way: fixed summation order, no BLAS, no FMA
+ * contraction — translated README, "why no BLAS" and build-flags sections).
+ * OpenMP splits only independent outputs across threads; each output is
+ * reduced by one thread in one order, so the thread count changes no bit.
+ *
+ * What is computed (one MoE FFN layer; the pages' routed experts are MXFP4,
+ * "multiplied directly without dequantizing", 16 of 896 chosen per token,
+ * plus 2 always-on shared experts — review page "KDA/MLA/MoE" table and
+ * "at a glance" table; README "shard census"):
+ *   logits[t][e] = sum_i x[t][i] * Wr[e][i]
+ *   S_t          = the k experts with the largest logits (ties: lower id)
+ *   w[t][e]      = exp(l_e - m) / sum_{j in S_t} exp(l_j - m), m = max over S_t
+ *   per chosen (t, e):  g = Wg x,  u = Wu x,  h = silu(g) * u,  y = Wd h
+ *   shared:      s = sum over shared experts in order of the same FFN (bf16 W)
+ *   out[t]       = s[t] + sum over S_t in ascending expert id (w != 0) of w * y
+ *
+ * MXFP4 (the pages: 0.5 byte per E2M1 nibble + 1/32 byte of shared E8M0 scale
+ * per weight, README "shard census"): element value = E2M1(code) * 2^(s-127).
+ * Byte i of a packed row holds element 2i in its low nibble, 2i+1 in its high.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* E2M1 (OCP MX v1.0): bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
+ * Exponent field 0 is subnormal: 0.m * 2^0 = m * 0.5; otherwise
+ * 2^(e-1) * (1 + m/2). */
+double oracle_e2m1(int code) {
+  int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return sign ? -mag : mag;
+}
+
+/* E8M0 (OCP MX v1.0): 2^(s-127); the all-ones byte encodes NaN. */
+double oracle_e8m0(int s) {
+  if (s == 255) return NAN;
+  return ldexp(1.0, s - 127);
+}
+
+static double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Element (r, i) of a packed MXFP4 matrix with `cols` columns. */
+static double mx_elem(const uint8_t* q, const uint8_t* s, int cols, int64_t r, int i) {
+  uint8_t byte = q[r * (cols / 2) + i / 2];
+  int code = (i % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+  return oracle_e2m1(code) * oracle_e8m0(s[r * (cols / 32) + i / 32]);
+}
+
+/* Decode rows [r0, r0 + nr) of a packed MXFP4 matrix to fp64 (exact). */
+void oracle_mxfp4_decode(int64_t r0, int64_t nr, int cols, const uint8_t* q, const uint8_t* s,
+                         double* out) {
+  for (int64_t r = 0; r < nr; ++r)
+    for (int i = 0; i < cols; ++i) out[r * cols + i] = mx_elem(q, s, cols, r0 + r, i);
+}
+
+/* logits[t][e] = sum_{i ascending} x[t][i] * Wr[e][i]; x is fp64 (exact copy of
+ * bf16/fp32 inputs), Wr bf16. */
+void oracle_router_logits(int64_t T, int d, int E, const double* x, const uint16_t* wr,
+                          double* logits) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += x[t * d + i] * bf16_value(wr[(int64_t)e * d + i]);
+      logits[t * E + e] = acc;
+    }
+}
+
+/* a ranks before b: larger logit first, equal logits by lower id. */
+static int ranks_before(double la, int a, double lb, int b) {
+  return la > lb || (la == lb && a < b);
+}
+
+/* Top-k by (logit desc, id asc); idx rows in ascending expert id; w aligned. */
+void oracle_topk_softmax(int64_t T, int E, int k, const double* logits, int32_t* idx,
+                         double* w) {
+#pragma omp parallel
+  {
+    char* taken = (char*)malloc((size_t)E);
+    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      const double* l = logits + t * E;
+      memset(taken, 0, (size_t)E);
+      for (int r = 0; r < k; ++r) { /* r-th best among the not yet taken */
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+          if (!taken[e] && (best < 0 || ranks_before(l[e], e, l[best], best))) best = e;
+        taken[best] = 1;
+        sel[r] = best;
+      }
+      double m = l[sel[0]];
+      int pos = 0;
+      for (int e = 0; e < E; ++e) /* ascending id */
+        if (taken[e]) idx[t * k + pos++] = e;
+      double z = 0.0;
+      for (int r = 0; r < k; ++r) z += exp(l[idx[t * k + r]] - m);
+      for (int r = 0; r < k; ++r) w[t * k + r] = exp(l[idx[t * k + r]] - m) / z;
+    }
+    free(taken);
+    free(sel);
+  }
+}
+
+/* Counting sort of the T*k (token, slot) pairs by expert, stable in pair
+ * order: counts[e], offsets[e] = sum_{e' < e} counts[e'] (E+1 entries),
+ * sorted_pair[p] = t*k + slot of the p-th pair, pair_pos its inverse. */
+void oracle_permute(int64_t T, int E, int k, const int32_t* idx, int32_t* counts,
+                    int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos) {
+  int64_t P = T * k;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p) counts[idx[p]]++;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int64_t p = 0; p < P; ++p) {
+    int e = idx[p];
+    int32_t pos = offsets[e] + fill[e]++;
+    sorted_pair[pos] = (int32_t)p;
+    pair_pos[p] = pos;
+  }
+  free(fill);
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One MXFP4 expert over n activation rows x [n][d]:
+ *   g_j = sum_i Wg[j][i] x_i, u_j = sum_i Wu[j][i] x_i   (i ascending)
+ *   h_j = silu(g_j) u_j
+ *   y_o = sum_j Wd[o][j] h_j                             (j ascending)
+ * w13 [2f][d/2] codes with w13s [2f][d/32] (rows 0..f-1 gate, f..2f-1 up);
+ * w2 [d][f/2] with w2s [d][f/32].  h (optional, [n][f]) receives h. */
+void oracle_mxfp4_ffn(int d, int f, const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2,
+                      const uint8_t* w2s, int64_t n, const double* x, double* y, double* h_out) {
+  double* g = (double*)malloc(sizeof(double) * (size_t)(n * f));
+  double* u = (double*)malloc(sizeof(double) * (size_t)(n * f));
+  double* h = (double*)malloc(sizeof(double) * (size_t)(n * f));
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * (size_t)(d > f ? d : f));
+#pragma omp for schedule(static)
+    for (int j = 0; j < 2 * f; ++j) {
+      oracle_mxfp4_decode(j, 1, d, w13, w13s, row);
+      for (int64_t r = 0; r < n; ++r) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += row[i] * x[r * d + i];
+        if (j < f) g[r * f + j] = acc;
+        else u[r * f + (j - f)] = acc;
+      }
+    }
+#pragma omp for schedule(static)
+    for (int64_t q = 0; q < n * f; ++q) h[q] = silu(g[q]) * u[q];
+#pragma omp for schedule(static)
+    for (int o = 0; o < d; ++o) {
+      oracle_mxfp4_decode(o, 1, f, w2, w2s, row);
+      for (int64_t r = 0; r < n; ++r) {
+        double acc = 0.0;
+        for (int j = 0; j < f; ++j) acc += row[j] * h[r * f + j];
+        y[r * d + o] = acc;
+      }
+    }
+    free(row);
+  }
+  if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)(n * f));
+  free(g);
+  free(u);
+  free(h);
+}
+
+/* One bf16 expert (the always-on shared experts): same FFN with
+ * w13 [2f][d] and w2 [d][f] bf16. */
+void oracle_bf16_ffn(int d, int f, const uint16_t* w13, const uint16_t* w2, int64_t n,
+                     const double* x, double* y) {
+  double* g = (double*)malloc(sizeof(double) * (size_t)(n * f));
+  double* u = (double*)malloc(sizeof(double) * (size_t)(n * f));
+  double* h = (double*)malloc(sizeof(double) * (size_t)(n * f));
+#pragma omp parallel for schedule(static)
+  for (int j = 0; j < 2 * f; ++j)
+    for (int64_t r = 0; r < n; ++r) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += bf16_value(w13[(int64_t)j * d + i]) * x[r * d + i];
+      if (j < f) g[r * f + j] = acc;
+      else u[r * f + (j - f)] = acc;
+    }
+  for (int64_t q = 0; q < n * f; ++q) h[q] = silu(g[q]) * u[q];
+#pragma omp parallel for schedule(static)
+  for (int o = 0; o < d; ++o)
+    for (int64_t r = 0; r < n; ++r) {
+      double acc = 0.0;
+      for (int j = 0; j < f; ++j) acc += bf16_value(w2[(int64_t)o * f + j]) * h[r * f + j];
+      y[r * d + o] = acc;
+    }
+  free(g);
+  free(u);
+  free(h);
+}
+
+/* out[t][o] = shared[t][o] (or 0 when shared is NULL), then for slots in
+ * order (ascending expert id) with w != 0: += w * y_perm[pair_pos[t*k+slot]][o]. */
+void oracle_combine(int64_t T, int d, int k, const double* y_perm, const int32_t* pair_pos,
+                    const double* w, const double* shared, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int o = 0; o < d; ++o) {
+      double acc = shared ? shared[t * d + o] : 0.0;
+      for (int s = 0; s < k; ++s) {
+        double ws = w[t * k + s];
+        if (ws != 0.0) acc += ws * y_perm[(int64_t)pair_pos[t * k + s] * d + o];
+      }
+      out[t * d + o] = acc;
+    }
+}
