@@ -1,0 +1,212 @@
+/*
+ * k3moe — one routed Mixture-of-Experts FFN layer on MXFP4 experts, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the MoE block of the Kimi-K3-style model the pages describe:
+ * per token, a router picks 16 of 896 routed experts, each expert is a gated
+ * FFN whose weights are MXFP4 (4-bit E2M1 codes with one E8M0 scale per 32
+ * weights, multiplied directly rather than expanded to a dense copy), and 2
+ * always-on shared experts are added for every token (kimi-k3-in-c review
+ * page, "at a glance" and "KDA/MLA/MoE" tables; translated README, "shard
+ * census"; explainer page, "reduction one").  The routing rule, the gated
+ * activation and the combine order taken here are:
+ *   logits[t][e] = sum_i x[t][i] Wr[e][i]
+ *   S_t          = k largest logits, ties to the lower expert id
+ *   w[t][e]      = exp(l_e) / sum_{j in S_t} exp(l_j)     (softmax over S_t)
+ *   y_(t,e)      = Wd_e (silu(Wg_e x_t) * (Wu_e x_t)),    silu(z) = z / (1 + e^-z)
+ *   out[t]       = (shared_0(x_t) + shared_1(x_t) + ...)
+ *                  + sum over S_t in ascending expert id, skipping w = 0, of w y
+ * (the pages' own model uses sigmoid scores with a selection-only bias and a
+ * bounded-tanh gate; this library implements the softmax / SiLU form).
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers unless stated; the caller
+ *     allocates and owns every buffer (weights, activations, outputs,
+ *     workspace, diagnostics).  The library allocates nothing, keeps no
+ *     mutable global state and may run concurrently on different streams
+ *     when the workspaces differ.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  A call validates
+ *     its arguments on the host, enqueues its kernels on `stream` and returns
+ *     without synchronising; buffers must stay valid until the work is done.
+ *   - Validation happens before any launch: a non-OK status means nothing was
+ *     enqueued (except K3MOE_EHIP, where earlier kernels of the same call may
+ *     have been enqueued).  No call aborts, exits or throws.
+ *   - Base pointers must be 16-byte aligned (K3MOE_EALIGN otherwise).
+ *   - Results are deterministic: the same inputs give the same bits on every
+ *     run, and a token's outputs do not depend on the other tokens of the
+ *     batch as long as the batch stays within one path class
+ *     (k3moe_path_class).
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum k3moe_status {
+  K3MOE_OK = 0,
+  K3MOE_EINVAL = 1,       /* NULL required pointer, negative or inconsistent sizes */
+  K3MOE_ESHAPE = 2,       /* shape outside the supported set (see k3moe_shape) */
+  K3MOE_EALIGN = 3,       /* a base pointer is not 16-byte aligned */
+  K3MOE_EWORKSPACE = 4,   /* workspace NULL or smaller than k3moe_workspace_bytes() */
+  K3MOE_EUNSUPPORTED = 5, /* dtype / weight-format combination not implemented */
+  K3MOE_EHIP = 6          /* a HIP launch failed; k3moe_last_error() has the detail */
+} k3moe_status;
+
+/* Activation / output element types. */
+enum { K3MOE_F32 = 0, K3MOE_BF16 = 1 };
+/* Expert weight formats. */
+enum { K3MOE_FMT_MXFP4 = 0, K3MOE_FMT_BF16 = 1 };
+/* Operation ids for k3moe_workspace_bytes(). */
+enum {
+  K3MOE_OP_ROUTE = 0,
+  K3MOE_OP_PERMUTE = 1,
+  K3MOE_OP_EXPERT_FFN = 2,
+  K3MOE_OP_SHARED_FFN = 3,
+  K3MOE_OP_COMBINE = 4,
+  K3MOE_OP_LAYER = 5
+};
+/* Path classes (k3moe_path_class). */
+enum { K3MOE_PATH_GEMV = 0, K3MOE_PATH_MFMA = 1 };
+
+/* Device diagnostic counters: an int32 array of K3MOE_DIAG_COUNT entries the
+ * caller zeroes; calls that take `diag` add to it (NULL = not collected).
+ * A non-zero BAD_EXPERT_IDS or NONFINITE_LOGITS means the call finished but
+ * its results are not to be trusted. */
+enum {
+  K3MOE_DIAG_RECHECKED_TOKENS = 0, /* tokens whose top-k set was decided by the
+                                      exact fp64 re-evaluation of near-tied logits */
+  K3MOE_DIAG_NONFINITE_LOGITS = 1, /* NaN/inf router logits seen */
+  K3MOE_DIAG_BAD_EXPERT_IDS = 2,   /* expert ids outside [0, E) given to permute
+                                      (such pairs are dropped) */
+  K3MOE_DIAG_RESERVED = 3,
+  K3MOE_DIAG_COUNT = 4
+};
+
+/* Problem shape.  Supported set: 0 <= T (T = 0 is an empty batch: every call
+ * returns K3MOE_OK and enqueues nothing), T * k < 2^31; 32 <= d <= 16384 and
+ * d % 32 == 0; 32 <= f <= 16384 and f % 32 == 0; 1 <= k <= min(E, 64);
+ * E <= 1024; 0 <= n_shared <= 8; f_shared % 32 == 0 (>= 32 when n_shared > 0);
+ * x_dtype, out_dtype in {K3MOE_F32, K3MOE_BF16}. */
+typedef struct k3moe_shape {
+  int64_t T;         /* tokens */
+  int32_t d;         /* hidden size */
+  int32_t f;         /* routed expert intermediate size */
+  int32_t E;         /* routed experts */
+  int32_t k;         /* experts chosen per token */
+  int32_t n_shared;  /* always-on shared experts */
+  int32_t f_shared;  /* shared expert intermediate size */
+  int32_t x_dtype;   /* activations x [T][d] */
+  int32_t out_dtype; /* layer output [T][d] */
+} k3moe_shape;
+
+/* A bank of experts, expert-major (each expert's bytes contiguous).
+ * MXFP4 (routed experts):
+ *   w13       [n][2f][d/2]  u8, packed E2M1 codes; rows 0..f-1 gate, f..2f-1 up
+ *   w13_scale [n][2f][d/32] u8, E8M0 (value 2^(s-127); 255 = NaN)
+ *   w2        [n][d][f/2]   u8
+ *   w2_scale  [n][d][f/32]  u8
+ *   Byte i of a row holds element 2i in its low nibble, 2i+1 in its high
+ *   nibble; elements 32b..32b+31 share scale byte b of the row.
+ * BF16 (shared experts): w13 [n][2f][d], w2 [n][d][f] bf16; scales NULL. */
+typedef struct k3moe_expert_bank {
+  int32_t format;    /* K3MOE_FMT_MXFP4 or K3MOE_FMT_BF16 */
+  int32_t n_experts;
+  int32_t d, f;
+  const void* w13;
+  const void* w13_scale;
+  const void* w2;
+  const void* w2_scale;
+} k3moe_expert_bank;
+
+typedef struct k3moe_layer_weights {
+  const void* w_router;      /* [E][d] bf16 */
+  k3moe_expert_bank routed;  /* MXFP4, n_experts = E, f = shape.f */
+  k3moe_expert_bank shared;  /* BF16, n_experts = n_shared, f = shape.f_shared */
+} k3moe_layer_weights;
+
+/* Bytes of workspace `op` needs for `shape` (0 for an invalid shape).  The
+ * workspace pointer must be 256-byte aligned. */
+size_t k3moe_workspace_bytes(const k3moe_shape* shape, int op);
+
+/* Bytes of an MXFP4 matrix of rows x cols: rows * cols * 17 / 32 (half a byte
+ * per E2M1 code plus one E8M0 byte per 32 weights — the 0.53125 bytes per
+ * weight of the pages' shard census).  Host-only helper. */
+uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols);
+
+/* Which path class a call with this shape takes (K3MOE_PATH_GEMV for
+ * memory-bound decode batches, K3MOE_PATH_MFMA for large batches). */
+int k3moe_path_class(const k3moe_shape* shape);
+
+/* Router + top-k + softmax.
+ * x [T][d] (x_dtype), w_router [E][d] bf16 ->
+ *   topk_idx [T][k] int32, each row in ascending expert id;
+ *   topk_w   [T][k] fp32, aligned with topk_idx, summing to 1 per token;
+ *   logits   [T][E] fp32 (optional, NULL = not written).
+ * The chosen set equals the set an exact evaluation of the logits in fp64
+ * (ascending i) picks: near-ties at the k/k+1 boundary are re-evaluated
+ * exactly on the device (counted in diag[K3MOE_DIAG_RECHECKED_TOKENS]).
+ * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_ROUTE). */
+k3moe_status k3moe_route(const k3moe_shape* shape, const void* x, const void* w_router,
+                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* diag,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Counting sort of the T*k (token, slot) pairs by expert, stable in pair
+ * order (pair p = t*k + slot):
+ *   counts [E], offsets [E+1] (exclusive prefix sum, offsets[E] = T*k),
+ *   sorted_pair [T*k]: sorted_pair[q] = pair at sorted position q,
+ *   pair_pos    [T*k]: its inverse.
+ * Exact integer results.  An id outside [0, E), or an id repeated within a
+ * token's row, is dropped (its pair_pos is -1, sorted positions past
+ * offsets[E] hold -1) and counted in diag[K3MOE_DIAG_BAD_EXPERT_IDS].
+ * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_PERMUTE). */
+k3moe_status k3moe_permute(const k3moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                           int32_t* diag, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Routed expert FFN on an MXFP4 bank (n_experts = E):
+ *   y [T*k][d] fp32, row q = expert e's FFN of token sorted_pair[q] / k,
+ *   where e is the expert whose range offsets[e] .. offsets[e+1] holds q;
+ *   unweighted.  offsets and sorted_pair as written by k3moe_permute.
+ * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_EXPERT_FFN). */
+k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank* bank,
+                              const void* x, const int32_t* offsets, const int32_t* sorted_pair,
+                              float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Shared experts on a BF16 bank (n_experts = n_shared, f = f_shared):
+ *   y [T][d] fp32 = sum over the bank's experts in order of each expert's FFN.
+ * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_SHARED_FFN). */
+k3moe_status k3moe_shared_ffn(const k3moe_shape* shape, const k3moe_expert_bank* bank,
+                              const void* x, float* y, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Fixed-order combine:
+ *   out[t][o] = shared_y[t][o] (0 when shared_y is NULL)
+ *               + sum over slots s ascending with topk_w[t][s] != 0 of
+ *                 topk_w[t][s] * y_perm[pair_pos[t*k+s]][o]
+ * y_perm [T*k][d] fp32, pair_pos [T*k], topk_w [T][k] fp32,
+ * out [T][d] in out_dtype (bf16 by round-to-nearest-even). */
+k3moe_status k3moe_combine(const k3moe_shape* shape, const float* y_perm, const int32_t* pair_pos,
+                           const float* topk_w, const float* shared_y, void* out, void* stream);
+
+/* The whole layer: route, permute, routed experts, shared experts, combine.
+ * Bit-identical to calling the five stages above in sequence on the same
+ * stream.  out [T][d] in out_dtype.
+ * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_LAYER). */
+k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* weights,
+                         const void* x, void* out, int32_t* diag, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* k3moe_status_str(k3moe_status status);
+/* Detail of the last non-OK status returned on the calling thread. */
+const char* k3moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* K3MOE_H */

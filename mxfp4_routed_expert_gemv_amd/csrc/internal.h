@@ -1,0 +1,83 @@
+// Host-side internal interface of libk3moe: kernel launchers (implemented in
+// the .hip files) and the workspace layout shared by the entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/k3moe.h"
+
+namespace k3 {
+
+// Token count up to which a call takes the decode (GEMV) path class.
+constexpr int64_t kGemvMaxT = 64;
+// Tokens per permute chunk (one workgroup, one bit per token in LDS masks).
+constexpr int kPermChunk = 256;
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Carves a workspace into 256-byte aligned pieces (or only sums their sizes
+// when base is NULL).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+struct RouteWs {
+  double* logits;   // [T][E] fp64
+  float* lbound;    // [T][E] bound on |logit - exact fp64 sequential logit|
+};
+struct PermuteWs {
+  int32_t* chunk_base;  // [nchunks][E]
+};
+struct ExpertWs {
+  int32_t* active;    // [E] experts with at least one pair, ascending
+  int32_t* n_active;  // [1]
+  float* h;           // [P][f]
+};
+struct SharedWs {
+  float* h;           // [T][n_shared][f_shared]
+};
+struct LayerWs {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  float* y_perm;
+  float* shared_y;
+  void* scratch;      // shared by the stage workspaces (stages run in order)
+  size_t scratch_bytes;
+};
+
+RouteWs carve_route(const k3moe_shape& s, void* ws, size_t* bytes);
+PermuteWs carve_permute(const k3moe_shape& s, void* ws, size_t* bytes);
+ExpertWs carve_expert(const k3moe_shape& s, void* ws, size_t* bytes);
+SharedWs carve_shared(const k3moe_shape& s, void* ws, size_t* bytes);
+LayerWs carve_layer(const k3moe_shape& s, void* ws, size_t* bytes);
+
+// Launchers: enqueue on `st`, return hipSuccess or the launch error.
+hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, int32_t* idx,
+                        float* w, float* logits_out, int32_t* diag, const RouteWs& ws,
+                        hipStream_t st);
+hipError_t launch_permute(const k3moe_shape& s, const int32_t* idx, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                          int32_t* diag, const PermuteWs& ws, hipStream_t st);
+hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
+                             const int32_t* offsets, const int32_t* sorted_pair, float* y,
+                             const ExpertWs& ws, hipStream_t st);
+hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
+                             float* y, const SharedWs& ws, hipStream_t st);
+hipError_t launch_combine(const k3moe_shape& s, const float* y_perm, const int32_t* pair_pos,
+                          const float* topk_w, const float* shared_y, void* out, hipStream_t st);
+
+}  // namespace k3

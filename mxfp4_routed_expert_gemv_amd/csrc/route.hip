@@ -1,0 +1,259 @@
+// Router logits, top-k and softmax weights.
+//
+// Routing follows the pages' MoE layer (16 of 896 experts per token —
+// kimi-k3-in-c review, "at a glance" table) with softmax weights renormalised
+// over the chosen experts.  The chosen SET must equal what an exact fp64
+// evaluation of the logits in ascending-i order picks, bit for bit, so:
+//   1. the logits are computed in fp64 (bf16 x bf16 and fp32 x bf16 products
+//      are exact in fp64) together with a rigorous bound on their distance to
+//      the sequential fp64 value;
+//   2. the top-k kernel selects by (logit desc, id asc) and checks that every
+//      chosen expert beats every other expert by more than the two bounds;
+//      when that fails it re-evaluates the undecided experts sequentially in
+//      fp64, ascending i — the exact same operations as the oracle, hence the
+//      same bits — and selects among them.
+#include "internal.h"
+#include "kern_common.h"
+
+#include <limits.h>
+
+namespace k3 {
+namespace {
+
+// One wave per expert row; loops over tokens.  Per lane: 8-element chunks
+// c = lane, lane+64, ...; fp64 sequential partial over the lane's chunks,
+// then a fixed butterfly over the wave.
+template <bool XF32>
+__global__ __launch_bounds__(256) void router_gemv_f64(const void* __restrict__ x,
+                                                       const uint16_t* __restrict__ wr,
+                                                       double* __restrict__ logits,
+                                                       float* __restrict__ lbound, int T, int d,
+                                                       int E) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int nc = d / 8;
+  const uint16_t* wrow = wr + (size_t)e * d;
+  for (int t = 0; t < T; ++t) {
+    double acc = 0.0;
+    float aabs = 0.0f;
+    for (int c = lane; c < nc; c += kWave) {
+      const uint4 wv = ldg16(wrow + (size_t)c * 8);
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+      float xf[8];
+      if (XF32) {
+        const float* xr = static_cast<const float*>(x) + (size_t)t * d + (size_t)c * 8;
+        const uint4 a = ldg16(xr), b = ldg16(xr + 4);
+        xf[0] = __uint_as_float(a.x); xf[1] = __uint_as_float(a.y);
+        xf[2] = __uint_as_float(a.z); xf[3] = __uint_as_float(a.w);
+        xf[4] = __uint_as_float(b.x); xf[5] = __uint_as_float(b.y);
+        xf[6] = __uint_as_float(b.z); xf[7] = __uint_as_float(b.w);
+      } else {
+        const uint16_t* xr = static_cast<const uint16_t*>(x) + (size_t)t * d + (size_t)c * 8;
+        const uint4 a = ldg16(xr);
+        const uint32_t xw[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { xf[2 * q] = bf16_lo(xw[q]); xf[2 * q + 1] = bf16_hi(xw[q]); }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float w0 = bf16_lo(ww[q]), w1 = bf16_hi(ww[q]);
+        acc += (double)xf[2 * q] * (double)w0;      // exact product, rounded sum
+        acc += (double)xf[2 * q + 1] * (double)w1;
+        aabs += fabsf(xf[2 * q] * w0) + fabsf(xf[2 * q + 1] * w1);
+      }
+    }
+    acc = wave_sum(acc);
+    aabs = wave_sum(aabs);
+    if (lane == 0) {
+      // |acc - exact| <= (d/64 + 6) u S and |oracle - exact| <= d u S with
+      // u = 2^-53 and S = sum|p| <= 1.01 aabs (aabs is an fp32 sum of
+      // rounded |products|, d <= 16384).
+      const double bnd = (2.0 * d + 64.0) * 0x1p-53 * (double)aabs * 1.02;
+      logits[(size_t)t * E + e] = acc;
+      lbound[(size_t)t * E + e] = (float)bnd;
+    }
+  }
+}
+
+constexpr int kMaxJ = 16;  // E <= 1024 = 16 per lane
+
+__device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void wave_argmax(double& v, int& id) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(id, o, kWave);
+    if (better(ov, oi, v, id)) { v = ov; id = oi; }
+  }
+}
+
+// Exact sequential fp64 logit: the oracle's operation sequence.
+template <bool XF32>
+__device__ double exact_logit(const void* x, const uint16_t* wr, int t, int e, int d) {
+  const uint16_t* wrow = wr + (size_t)e * d;
+  double acc = 0.0;
+  if (XF32) {
+    const float* xr = static_cast<const float*>(x) + (size_t)t * d;
+    for (int i = 0; i < d; ++i)
+      acc += (double)xr[i] * (double)__uint_as_float((uint32_t)wrow[i] << 16);
+  } else {
+    const uint16_t* xr = static_cast<const uint16_t*>(x) + (size_t)t * d;
+    for (int i = 0; i < d; ++i)
+      acc += (double)__uint_as_float((uint32_t)xr[i] << 16) *
+             (double)__uint_as_float((uint32_t)wrow[i] << 16);
+  }
+  return acc;
+}
+
+// One wave (= one workgroup) per token.
+template <bool XF32>
+__global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ logits,
+                                                   const float* __restrict__ lbound,
+                                                   const void* __restrict__ x,
+                                                   const uint16_t* __restrict__ wr,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ w_out,
+                                                   float* __restrict__ logits_out,
+                                                   int32_t* __restrict__ diag, int T, int d, int E,
+                                                   int k) {
+  __shared__ double candL[1024];
+  __shared__ int candId[1024];
+  __shared__ int candTaken[1024];
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  const int nj = (E + kWave - 1) / kWave;
+  const double* lrow = logits + (size_t)t * E;
+  const float* brow = lbound + (size_t)t * E;
+
+  double v[kMaxJ];
+  float b[kMaxJ];
+  int nonfin = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j) {
+    const int e = lane + kWave * j;
+    v[j] = -INFINITY;
+    b[j] = 0.0f;
+    if (j < nj && e < E) {
+      double lv = lrow[e];
+      if (!isfinite(lv)) ++nonfin;
+      if (logits_out) logits_out[(size_t)t * E + e] = (float)lv;
+      v[j] = isnan(lv) ? -INFINITY : lv;
+      b[j] = brow[e];
+    }
+  }
+  nonfin = wave_sum(nonfin);
+  if (lane == 0 && nonfin && diag) atomicAdd(&diag[K3MOE_DIAG_NONFINITE_LOGITS], nonfin);
+
+  // k rounds of wave argmax by (logit desc, id asc).
+  uint32_t taken = 0;
+  int my_id = -1;  // lane r < k holds the r-th chosen expert
+  for (int r = 0; r < k; ++r) {
+    double bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j) {
+      const int e = lane + kWave * j;
+      if (j < nj && e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+    if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
+    if (lane == r) my_id = bi;
+  }
+
+  // Certificate: every chosen expert's lower bound beats every other
+  // expert's upper bound.  Otherwise the undecided ones are re-evaluated.
+  double lo = INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j)
+    if ((taken >> j) & 1u) lo = fmin(lo, v[j] - (double)b[j]);
+  const double tau = wave_min(lo);
+  uint32_t cand = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j) {
+    const int e = lane + kWave * j;
+    if (j < nj && e < E && !((taken >> j) & 1u) && v[j] + (double)b[j] >= tau) cand |= 1u << j;
+  }
+  const int nout = wave_sum((int)__popc(cand));
+  if (nout > 0) {
+    // Undecided: the chosen ones plus the challengers.  Gather their ids in
+    // ascending id order (lane-major within j), evaluate each exactly.
+    const uint32_t all = cand | taken;
+    int n = 0;
+    for (int j = 0; j < nj; ++j) {
+      const bool mine = (all >> j) & 1u;
+      const unsigned long long bal = __ballot(mine);
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (mine) candId[n + before] = lane + kWave * j;
+      n += __popcll(bal);
+    }
+    __syncthreads();
+    for (int q = lane; q < n; q += kWave) {
+      candL[q] = exact_logit<XF32>(x, wr, t, candId[q], d);
+      candTaken[q] = 0;
+    }
+    __syncthreads();
+    for (int r = 0; r < k; ++r) {
+      double bv = -INFINITY;
+      int bi = INT_MAX, bq = -1;
+      for (int q = lane; q < n; q += kWave)
+        if (!candTaken[q] && better(candL[q], candId[q], bv, bi)) { bv = candL[q]; bi = candId[q]; bq = q; }
+      int owner = bq;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const double ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        const int oq = __shfl_xor(owner, o, kWave);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; owner = oq; }
+      }
+      if (lane == 0) candTaken[owner] = 1;
+      if (lane == r) my_id = bi;
+      __syncthreads();
+    }
+    if (lane == 0 && diag) atomicAdd(&diag[K3MOE_DIAG_RECHECKED_TOKENS], 1);
+  }
+
+  // Ascending-id order and softmax over the chosen logits.
+  int rank = 0;
+  for (int r = 0; r < k; ++r) {
+    const int other = __shfl(my_id, r, kWave);
+    if (lane < k && other < my_id) ++rank;
+  }
+  const double lv = lane < k ? lrow[my_id] : -INFINITY;
+  const double m = wave_max(lv);
+  const double ex = lane < k ? exp(lv - m) : 0.0;
+  const double z = wave_sum(ex);
+  if (lane < k) {
+    idx_out[(size_t)t * k + rank] = my_id;
+    w_out[(size_t)t * k + rank] = (float)(ex / z);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, int32_t* idx,
+                        float* w, float* logits_out, int32_t* diag, const RouteWs& ws,
+                        hipStream_t st) {
+  const int T = (int)s.T;
+  const bool xf32 = s.x_dtype == K3MOE_F32;
+  const dim3 g1((s.E + 3) / 4);
+  if (xf32)
+    router_gemv_f64<true><<<g1, 256, 0, st>>>(x, wr, ws.logits, ws.lbound, T, s.d, s.E);
+  else
+    router_gemv_f64<false><<<g1, 256, 0, st>>>(x, wr, ws.logits, ws.lbound, T, s.d, s.E);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (xf32)
+    topk_softmax<true><<<T, 64, 0, st>>>(ws.logits, ws.lbound, x, wr, idx, w, logits_out, diag,
+                                         T, s.d, s.E, s.k);
+  else
+    topk_softmax<false><<<T, 64, 0, st>>>(ws.logits, ws.lbound, x, wr, idx, w, logits_out, diag,
+                                          T, s.d, s.E, s.k);
+  return hipGetLastError();
+}
+
+}  // namespace k3

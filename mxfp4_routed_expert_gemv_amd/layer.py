@@ -1,0 +1,117 @@
+"""Torch-facing convenience over the C ABI: holds a layer's device weights,
+allocates outputs and workspaces with torch, and calls the library.  Every
+computation happens in libk3moe's kernels; this file only marshals."""
+import torch
+
+from . import (BF16, DIAG_COUNT, F32, FMT_BF16, FMT_MXFP4, OP_COMBINE, OP_EXPERT_FFN, OP_LAYER,
+               OP_PERMUTE, OP_ROUTE, OP_SHARED_FFN, k3moe_combine, k3moe_expert_ffn,
+               k3moe_layer, k3moe_path_class, k3moe_permute, k3moe_route, k3moe_shared_ffn,
+               k3moe_workspace_bytes, make_bank, make_shape, make_weights)
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class MoELayer:
+    """One routed MoE FFN layer.  routed: dict of uint8 tensors w13 [E][2f][d/2],
+    w13_scale [E][2f][d/32], w2 [E][d][f/2], w2_scale [E][d][f/32]; shared:
+    dict of bf16 tensors w13 [S][2fs][d], w2 [S][d][fs] (or empty)."""
+
+    def __init__(self, w_router, routed: dict, shared: dict, k: int,
+                 out_dtype=torch.bfloat16):
+        self.w_router = w_router
+        self.routed = routed
+        self.shared = shared
+        self.E, two_f, half_d = routed["w13"].shape
+        self.f, self.d = two_f // 2, half_d * 2
+        self.k = k
+        self.n_shared = shared["w13"].shape[0] if shared else 0
+        self.f_shared = shared["w13"].shape[1] // 2 if shared else 0
+        self.out_dtype = out_dtype
+        self.routed_bank = make_bank(FMT_MXFP4, self.E, self.d, self.f, routed["w13"],
+                                     routed["w13_scale"], routed["w2"], routed["w2_scale"])
+        self.shared_bank = make_bank(FMT_BF16, self.n_shared, self.d, self.f_shared,
+                                     shared.get("w13"), None, shared.get("w2"), None)
+        self.weights = make_weights(w_router, self.routed_bank, self.shared_bank)
+
+    # ------------------------------------------------------------ helpers
+    def shape(self, T: int, x_dtype=torch.bfloat16, out_dtype=None):
+        out_dtype = self.out_dtype if out_dtype is None else out_dtype
+        return make_shape(T, self.d, self.f, self.E, self.k, self.n_shared, self.f_shared,
+                          _DT[x_dtype], _DT[out_dtype])
+
+    def workspace(self, shape, op):
+        n = k3moe_workspace_bytes(shape, op)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.w_router.device)
+
+    def path_class(self, T: int, x_dtype=torch.bfloat16) -> int:
+        return k3moe_path_class(self.shape(T, x_dtype))
+
+    def _dev(self):
+        return self.w_router.device
+
+    # ------------------------------------------------------------- stages
+    def route(self, x, want_logits=False, diag=None, stream=None):
+        T = x.shape[0]
+        s = self.shape(T, x.dtype)
+        idx = torch.empty((T, self.k), dtype=torch.int32, device=self._dev())
+        w = torch.empty((T, self.k), dtype=torch.float32, device=self._dev())
+        logits = torch.empty((T, self.E), dtype=torch.float32, device=self._dev()) if want_logits else None
+        k3moe_route(s, x, self.w_router, idx, w, logits, diag, self.workspace(s, OP_ROUTE), stream)
+        return idx, w, logits
+
+    def permute(self, idx, diag=None, stream=None):
+        T = idx.shape[0]
+        s = self.shape(T)
+        P = T * self.k
+        counts = torch.empty(self.E, dtype=torch.int32, device=self._dev())
+        offsets = torch.empty(self.E + 1, dtype=torch.int32, device=self._dev())
+        sp = torch.empty(max(P, 1), dtype=torch.int32, device=self._dev())
+        pp = torch.empty(max(P, 1), dtype=torch.int32, device=self._dev())
+        k3moe_permute(s, idx, counts, offsets, sp, pp, diag, self.workspace(s, OP_PERMUTE), stream)
+        return counts, offsets, sp[:P], pp[:P]
+
+    def expert_ffn(self, x, offsets, sorted_pair, stream=None):
+        T = x.shape[0]
+        s = self.shape(T, x.dtype)
+        y = torch.empty((max(T * self.k, 1), self.d), dtype=torch.float32, device=self._dev())
+        k3moe_expert_ffn(s, self.routed_bank, x, offsets, sorted_pair, y,
+                         self.workspace(s, OP_EXPERT_FFN), stream)
+        return y[:T * self.k]
+
+    def shared_ffn(self, x, stream=None):
+        T = x.shape[0]
+        s = self.shape(T, x.dtype)
+        y = torch.empty((max(T, 1), self.d), dtype=torch.float32, device=self._dev())
+        k3moe_shared_ffn(s, self.shared_bank, x, y, self.workspace(s, OP_SHARED_FFN), stream)
+        return y[:T]
+
+    def combine(self, y_perm, pair_pos, topk_w, shared_y, out_dtype=None, stream=None):
+        T = topk_w.shape[0]
+        s = self.shape(T, torch.bfloat16, out_dtype)
+        dt = self.out_dtype if out_dtype is None else out_dtype
+        out = torch.empty((max(T, 1), self.d), dtype=dt, device=self._dev())
+        k3moe_combine(s, y_perm, pair_pos, topk_w, shared_y, out, stream)
+        return out[:T]
+
+    def __call__(self, x, out_dtype=None, diag=None, workspace=None, stream=None, out=None):
+        T = x.shape[0]
+        s = self.shape(T, x.dtype, out_dtype)
+        dt = self.out_dtype if out_dtype is None else out_dtype
+        if out is None:
+            out = torch.empty((max(T, 1), self.d), dtype=dt, device=self._dev())
+        if workspace is None:
+            workspace = self.workspace(s, OP_LAYER)
+        k3moe_layer(s, self.weights, x, out, diag, workspace, stream)
+        return out[:T]
+
+    def staged(self, x, out_dtype=None, stream=None):
+        """The five stages called one by one (route, permute, routed experts,
+        shared experts, combine); returns every intermediate."""
+        diag = torch.zeros(DIAG_COUNT, dtype=torch.int32, device=self._dev())
+        idx, w, logits = self.route(x, want_logits=True, diag=diag, stream=stream)
+        counts, offsets, sp, pp = self.permute(idx, diag=diag, stream=stream)
+        y = self.expert_ffn(x, offsets, sp, stream=stream)
+        sh = self.shared_ffn(x, stream=stream) if self.n_shared else None
+        out = self.combine(y, pp, w, sh, out_dtype=out_dtype, stream=stream)
+        return dict(idx=idx, w=w, logits=logits, counts=counts, offsets=offsets, sorted_pair=sp,
+                    pair_pos=pp, y_perm=y, shared_y=sh, out=out, diag=diag)

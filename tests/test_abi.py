@@ -1,0 +1,143 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, sizes workspaces, and rejects every invalid argument with the
+documented status before launching anything (no device is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, golden
+
+k3 = pytest.importorskip("mxfp4_routed_expert_gemv_amd")
+
+HEADER = os.path.join(ROOT, "include", "k3moe.h")
+
+EINVAL, ESHAPE, EALIGN, EWORKSPACE, EUNSUPPORTED = 1, 2, 3, 4, 5
+FAKE = 0x10000   # an aligned address that is never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(k3moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(k3.lib, n), n
+    assert sorted(k3.EXPORTS) == names
+
+
+def big_shape(T=1, **kw):
+    a = dict(T=T, d=7168, f=2048, E=896, k=16, n_shared=2, f_shared=2048, x_dtype=k3.BF16,
+             out_dtype=k3.BF16)
+    a.update(kw)
+    return k3.make_shape(**a)
+
+
+def test_mxfp4_bytes_matches_pages_accounting():
+    g = golden("pages_byte_accounting.json")
+    # the pages' expert: 33,030,144 weights at 0.53125 B each = 17,547,264 B
+    assert g["expert_params"] * g["bytes_per_weight"] == g["expert_bytes"]
+    # an MXFP4 matrix whose element count is the pages' expert parameter count
+    assert k3.k3moe_mxfp4_bytes(1, g["expert_params"]) == g["expert_bytes"]
+    assert k3.k3moe_mxfp4_bytes(3 * 7168, 1536) == g["expert_bytes"]   # 3 x d x f', d = 7168
+    assert g["experts_per_layer"] * g["moe_layers"] == g["experts_total"]
+    # the census prints 1.447 TB for 1.44646e12 B: within one unit of its last digit
+    assert abs(g["experts_total"] * g["expert_bytes"] / 1e12 - g["routed_set_tb"]) < 1e-3
+    assert abs(g["experts_per_token"] * g["expert_bytes"] / 1e9 - g["ladder_row1_gb_read"]) < 5e-3
+    # this layer's expert: gate/up [2f][d] + down [d][f]
+    per_expert = k3.k3moe_mxfp4_bytes(2 * 2048, 7168) + k3.k3moe_mxfp4_bytes(7168, 2048)
+    assert per_expert == 23_396_352
+    assert 16 * per_expert == 374_341_632
+
+
+def test_workspace_sizes():
+    s = big_shape(T=1)
+    for op in range(6):
+        n = k3.k3moe_workspace_bytes(s, op)
+        assert n % 256 == 0
+    assert k3.k3moe_workspace_bytes(s, k3.OP_LAYER) >= 16 * 7168 * 4
+    assert k3.k3moe_workspace_bytes(s, k3.OP_COMBINE) == 0
+    assert k3.k3moe_workspace_bytes(big_shape(T=0), k3.OP_LAYER) == 0
+    assert k3.k3moe_workspace_bytes(big_shape(d=100), k3.OP_LAYER) == 0
+    assert k3.k3moe_workspace_bytes(s, 99) == 0
+
+
+def _route(shape, x=FAKE, wr=FAKE, idx=FAKE, w=FAKE, ws=(FAKE * 256, 1 << 40)):
+    return k3.lib.k3moe_route(ctypes.byref(shape), x, wr, idx, w, None, None, ws[0], ws[1], None)
+
+
+def test_route_validation():
+    assert _route(big_shape(T=-1)) == EINVAL
+    assert k3.lib.k3moe_route(None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, None) == EINVAL
+    assert _route(big_shape(d=7170)) == ESHAPE
+    assert _route(big_shape(d=16)) == ESHAPE
+    assert _route(big_shape(f=2050)) == ESHAPE
+    assert _route(big_shape(k=0)) == ESHAPE
+    assert _route(big_shape(k=897)) == ESHAPE
+    assert _route(big_shape(E=2000)) == ESHAPE
+    assert _route(big_shape(T=1 << 28)) == ESHAPE          # T * k >= 2^31
+    assert _route(big_shape(x_dtype=7)) == EUNSUPPORTED
+    assert _route(big_shape(out_dtype=3)) == EUNSUPPORTED
+    assert _route(big_shape(), x=None) == EINVAL
+    assert _route(big_shape(), wr=FAKE + 8) == EALIGN
+    assert _route(big_shape(), ws=(None, 0)) == EWORKSPACE
+    assert _route(big_shape(), ws=(FAKE * 256, 16)) == EWORKSPACE
+    assert _route(big_shape(), ws=(FAKE * 256 + 64, 1 << 40)) == EALIGN
+    assert "workspace" in k3.lib.k3moe_last_error().decode()
+    assert _route(big_shape(T=0)) == 0                     # empty batch: nothing to do
+
+
+def test_bank_and_layer_validation():
+    s = big_shape()
+    good = k3.make_bank(k3.FMT_MXFP4, 896, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
+    bf = k3.make_bank(k3.FMT_BF16, 896, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
+    wrong_n = k3.make_bank(k3.FMT_MXFP4, 895, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
+    no_scale = k3.make_bank(k3.FMT_MXFP4, 896, 7168, 2048, FAKE, None, FAKE, FAKE)
+
+    def ffn(bank):
+        return k3.lib.k3moe_expert_ffn(ctypes.byref(s), ctypes.byref(bank), FAKE, FAKE, FAKE,
+                                       FAKE, FAKE * 256, 1 << 40, None)
+    assert ffn(bf) == EUNSUPPORTED
+    assert ffn(wrong_n) == EINVAL
+    assert ffn(no_scale) == EINVAL
+    assert k3.lib.k3moe_expert_ffn(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE * 256,
+                                   1 << 40, None) == EINVAL
+    sh_ok = k3.make_bank(k3.FMT_BF16, 2, 7168, 2048, FAKE, None, FAKE, None)
+    sh_bad = k3.make_bank(k3.FMT_MXFP4, 2, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
+    assert k3.lib.k3moe_shared_ffn(ctypes.byref(s), ctypes.byref(sh_bad), FAKE, FAKE,
+                                   FAKE * 256, 1 << 40, None) == EUNSUPPORTED
+    w_ok = k3.make_weights(FAKE, good, sh_ok)
+
+    def layer(weights, x=FAKE, out=FAKE, ws=(FAKE * 256, 1 << 40), shape=s):
+        return k3.lib.k3moe_layer(ctypes.byref(shape), ctypes.byref(weights), x, out, None,
+                                  ws[0], ws[1], None)
+    assert layer(k3.make_weights(None, good, sh_ok)) == EINVAL
+    assert layer(k3.make_weights(FAKE, bf, sh_ok)) == EUNSUPPORTED
+    assert layer(k3.make_weights(FAKE, good, k3.make_bank(k3.FMT_BF16, 1, 7168, 2048, FAKE, None, FAKE, None))) == EINVAL
+    assert layer(w_ok, out=None) == EINVAL
+    assert layer(w_ok, x=FAKE + 4) == EALIGN
+    assert layer(w_ok, ws=(FAKE * 256, 1024)) == EWORKSPACE
+    assert layer(w_ok, shape=big_shape(T=0)) == 0
+    assert k3.lib.k3moe_layer(ctypes.byref(s), None, FAKE, FAKE, None, FAKE * 256, 1 << 40,
+                              None) == EINVAL
+
+
+def test_permute_and_combine_validation():
+    s = big_shape(T=4)
+    assert k3.lib.k3moe_permute(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, None, FAKE * 256,
+                                1 << 40, None) == EINVAL
+    assert k3.lib.k3moe_permute(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                                None) == EWORKSPACE
+    assert k3.lib.k3moe_combine(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None) == EINVAL
+    assert k3.lib.k3moe_combine(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE + 2, FAKE, None) == EALIGN
+
+
+def test_status_strings_and_path_class():
+    for code in range(7):
+        assert k3.lib.k3moe_status_str(code)
+    assert k3.k3moe_path_class(big_shape(T=1)) == k3.PATH_GEMV
+    assert k3.k3moe_path_class(big_shape(T=64)) == k3.PATH_GEMV

@@ -1,0 +1,307 @@
+"""GPU parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Routing ids, counts, offsets, sorted pairs and positions must be equal; fp32
+intermediates and outputs within 2e-3 x RMS of the oracle; bf16 outputs within
+that plus one bf16 ulp; every result bit-identical run to run, between the
+whole-layer call and the five staged calls, and for a token alone versus
+inside a batch of the same path class.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import gen.device
+import oracle
+from gpu_util import (W_TOL, assert_close, assert_close_bf16, check_permutation_properties,
+                      k3layer, log, oracle_expert, require_gpu, sample_tokens, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def _full_oracle(cfg, orc, x_host):
+    bank = gen.routed_bank(cfg)
+    return orc.layer(x_host, gen.router(cfg), lambda e: {k: v[e] for k, v in bank.items()},
+                     gen.shared_bank(cfg) if cfg.n_shared else None, cfg.k, cfg.E)
+
+
+def _compare_full(r, ref, cfg, out_dtype):
+    assert np.array_equal(to_np(r["idx"]), ref["idx"]), "expert ids differ"
+    assert np.max(np.abs(to_np(r["w"]) - ref["w"])) <= W_TOL
+    assert np.array_equal(to_np(r["counts"]), ref["counts"])
+    assert np.array_equal(to_np(r["offsets"]), ref["offsets"])
+    assert np.array_equal(to_np(r["sorted_pair"]), ref["sorted_pair"])
+    assert np.array_equal(to_np(r["pair_pos"]), ref["pair_pos"])
+    assert_close(to_np(r["logits"]), ref["logits"], "logits")
+    assert_close(to_np(r["y_perm"]), ref["y_perm"], "y_perm")
+    if cfg.n_shared:
+        assert_close(to_np(r["shared_y"]), ref["shared_y"], "shared_y")
+    if out_dtype == "bf16":
+        assert_close_bf16(to_np(r["out"]), ref["out"], "out")
+    else:
+        assert_close(to_np(r["out"]), ref["out"], "out")
+
+
+# ------------------------------------------------------------------ tiny layer
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_tiny_layer_parity(orc, out_dtype):
+    require_gpu()
+    cfg = gen.get("tiny")
+    log(f"case tiny T={cfg.T} out={out_dtype}")
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, out_dtype)
+    r = L.staged(wl.x)
+    ref = _full_oracle(cfg, orc, gen.x(cfg))
+    _compare_full(r, ref, cfg, out_dtype)
+    # whole layer == staged, and run-to-run, bit for bit
+    out1 = L(wl.x)
+    out2 = L(wl.x)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.uint8), r["out"].view(torch.uint8))
+    assert torch.equal(out1.view(torch.uint8), out2.view(torch.uint8))
+    assert to_np(r["diag"])[1:3].tolist() == [0, 0]
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 64, 255, 256, 257, 600])
+def test_tiny_ragged_batches(orc, T):
+    """Ragged token counts across the permute chunk (256) and the token
+    loops of the expert kernels (4 per step)."""
+    require_gpu()
+    cfg = gen.get("tiny").with_tokens(T)
+    log(f"case tiny T={T}")
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    r = L.staged(wl.x)
+    ref = _full_oracle(cfg, orc, gen.x(cfg))
+    _compare_full(r, ref, cfg, "f32")
+
+
+def test_tiny_batch_composition_and_order():
+    """A token's output bits do not depend on the rest of the batch: alone,
+    as a prefix, shuffled."""
+    require_gpu()
+    cfg = gen.get("tiny").with_tokens(37)
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    full = L(wl.x)
+    perm = torch.randperm(37, generator=torch.Generator().manual_seed(1)).to(wl.x.device)
+    shuffled = L(wl.x[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(shuffled, full[perm])
+    for t in (0, 5, 36):
+        alone = L(wl.x[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(alone[0], full[t]), t
+    prefix = L(wl.x[:9].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(prefix, full[:9])
+
+
+def test_hand_worked_two_experts(orc):
+    """The closed-form 1-token / 2-expert layer (hand-worked fixture), both
+    nibble positions, through the C ABI."""
+    require_gpu()
+    import oracle_pins
+    from conftest import golden
+    from mxfp4_routed_expert_gemv_amd.layer import MoELayer
+    g = golden("hand_two_experts.json")
+    for col in g["columns"]:
+        x, wr, experts = oracle_pins._hand_case(col)
+        dev = "cuda"
+        routed = {k: torch.from_numpy(np.stack([e[k] for e in experts])).to(dev)
+                  for k in experts[0]}
+        L = MoELayer(torch.from_numpy(wr.view(np.int16)).to(dev).view(torch.bfloat16), routed, {},
+                     k=2, out_dtype=torch.float32)
+        r = L.staged(torch.from_numpy(x).to(dev))
+        out = to_np(r["out"])
+        assert np.array_equal(to_np(r["idx"]), [[0, 1]])
+        assert np.allclose(out, g["out"], rtol=1e-5, atol=0), (col, out[0, :4])
+
+
+def test_edge_ids_and_empty_batch():
+    """Permute drops ids outside [0, E) and repeated ids (counted in diag,
+    position -1); an empty batch is a no-op."""
+    require_gpu()
+    cfg = gen.get("tiny")
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    idx = torch.tensor([[0, 3, 5, 7], [2, 2, 9, 40], [15, -1, 1, 0]], dtype=torch.int32,
+                       device="cuda")
+    diag = torch.zeros(4, dtype=torch.int32, device="cuda")
+    counts, offsets, sp, pp = L.permute(idx, diag=diag)
+    torch.cuda.synchronize()
+    assert to_np(diag)[2] == 3
+    ppn = to_np(pp)
+    assert ppn[5] == -1 and ppn[7] == -1 and ppn[9] == -1 and ppn[4] >= 0
+    valid = [(p, e) for p, e in enumerate(idx.cpu().numpy().ravel()) if ppn[p] >= 0]
+    assert to_np(offsets)[-1] == len(valid) == 9
+    order = sorted(valid, key=lambda pe: (pe[1], pe[0]))
+    assert to_np(sp)[:9].tolist() == [p for p, _ in order]
+    assert to_np(sp)[9:].tolist() == [-1, -1, -1]
+    empty = L(wl.x[:0])
+    assert empty.shape == (0, cfg.d)
+
+
+def test_k_equals_E_and_k_one(orc):
+    require_gpu()
+    base = gen.get("tiny")
+    for k in (1, base.E):
+        cfg = gen.configs.LayerConfig(**{**base.__dict__, "k": k, "name": f"tiny_k{k}"})
+        wl = gen.device.build(cfg)
+        L = k3layer(wl, "f32")
+        r = L.staged(wl.x)
+        ref = _full_oracle(cfg, orc, gen.x(cfg))
+        _compare_full(r, ref, cfg, "f32")
+
+
+def test_zero_weight_expert_contributes_nothing(orc):
+    """An expert whose routing weight underflows to 0 is skipped, even with
+    NaN weights (scale byte 255)."""
+    require_gpu()
+    cfg = gen.get("tiny")
+    x = gen.x(cfg).copy()
+    x[:, 0] = 1.0
+    wr = gen.router(cfg).copy()
+    wr[:, 0] = 0
+    wr[3, 0] = gen.f64_to_bf16_bits(2000.0)
+    wr[9, 0] = gen.f64_to_bf16_bits(1000.0)
+    bank = gen.routed_bank(cfg)
+    bank["w2_scale"][9] = 255
+    bank["w13_scale"][9] = 255
+    sh = gen.shared_bank(cfg)
+    ref = orc.layer(x, wr, lambda e: {k: v[e] for k, v in bank.items()}, sh, cfg.k, cfg.E)
+    from mxfp4_routed_expert_gemv_amd.layer import MoELayer
+    dev = "cuda"
+    L = MoELayer(torch.from_numpy(wr.view(np.int16)).to(dev).view(torch.bfloat16),
+                 {k: torch.from_numpy(v).to(dev) for k, v in bank.items()},
+                 {k: torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
+                  for k, v in sh.items()}, cfg.k, out_dtype=torch.float32)
+    r = L.staged(torch.from_numpy(x).to(dev))
+    assert np.array_equal(to_np(r["idx"]), ref["idx"])
+    out = to_np(r["out"])
+    assert np.all(np.isfinite(out))
+    assert_close(out, ref["out"], "out with a NaN expert at weight 0")
+
+
+def test_nonfinite_logits_are_counted():
+    require_gpu()
+    cfg = gen.get("tiny")
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    x = wl.x.clone()
+    x[1, 5] = float("inf")
+    diag = torch.zeros(4, dtype=torch.int32, device="cuda")
+    L.route(x, diag=diag)
+    torch.cuda.synchronize()
+    assert to_np(diag)[1] > 0
+
+
+def test_device_generator_matches_host():
+    """The device fill of the routed bank equals the host generator byte for
+    byte (sampled experts of the full-size bank)."""
+    require_gpu()
+    cfg = gen.get("decode_b1")
+    sz = gen.routed_sizes(cfg)
+    for e in (0, 447, 895):
+        host = gen.routed_expert(cfg, e)
+        for name, n in sz.items():
+            buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+            kk = gen.key(cfg.seed, gen._routed_streams(cfg)[name])
+            lib = gen._load_dev()
+            if name.endswith("scale"):
+                rc = lib.k3gen_dev_scales(kk, e * n, n, cfg.scale_lo, cfg.scale_hi, buf.data_ptr(), 0)
+            else:
+                rc = lib.k3gen_dev_bytes(kk, e * n, n, buf.data_ptr(), 0)
+            assert rc == 0
+            torch.cuda.synchronize()
+            assert np.array_equal(buf.cpu().numpy(), host[name].ravel()), (e, name)
+
+
+# ------------------------------------------------------------- full-size layer
+@pytest.fixture(scope="module")
+def big():
+    """Device weights of the full-size layer (d = 7168, f = 2048, 896 experts,
+    2 shared), shared by the decode and prefill workloads."""
+    require_gpu()
+    cfg = gen.get("decode_b1")
+    log("building full-size layer weights on device")
+    wl = gen.device.build(cfg)
+    torch.cuda.synchronize()
+    return wl
+
+
+def _run_big(big, cfg, orc, n_sample):
+    from mxfp4_routed_expert_gemv_amd.layer import MoELayer
+    x_host = gen.x(cfg)
+    x = gen.device.activations(cfg)
+    wr_host = gen.router(cfg)
+    wr = gen.device._to_dev_bf16(wr_host, "cuda") if cfg.zipf_s is not None else big.w_router
+    L = MoELayer(wr, big.routed, big.shared, cfg.k, out_dtype=torch.bfloat16)
+    log(f"case {cfg.name}: T={cfg.T} path={L.path_class(cfg.T)}")
+    r = L.staged(x)
+    out_layer = L(x)
+    torch.cuda.synchronize()
+    assert torch.equal(out_layer.view(torch.int16), r["out"].view(torch.int16))
+    log(f"  diag = {to_np(r['diag']).tolist()}")
+    assert to_np(r["diag"])[1:3].tolist() == [0, 0]
+
+    # routing: every token's ids against the oracle, bit for bit
+    logits, idx, w = orc.route(oracle.to_f64(x_host), wr_host, cfg.k)
+    g_idx = to_np(r["idx"])
+    assert np.array_equal(g_idx, idx), f"{int(np.sum(np.any(g_idx != idx, axis=1)))} tokens differ"
+    assert np.max(np.abs(to_np(r["w"]) - w)) <= W_TOL
+    assert_close(to_np(r["logits"]), logits, "logits")
+    counts, offsets, sp, pp = orc.permute(idx, cfg.E)
+    assert np.array_equal(to_np(r["counts"]), counts)
+    assert np.array_equal(to_np(r["offsets"]), offsets)
+    assert np.array_equal(to_np(r["sorted_pair"]), sp)
+    assert np.array_equal(to_np(r["pair_pos"]), pp)
+    nz = counts[counts > 0]
+    log(f"  experts touched {nz.size}, pairs/expert max {nz.max()} min {nz.min()}")
+
+    # values: sampled tokens, every stage, against the oracle
+    toks = sample_tokens(cfg.T, n_sample)
+    out_ref, sh_ref, y_ref = orc.token_outputs(x_host[toks], idx[toks], w[toks],
+                                               oracle_expert(cfg), gen.shared_bank(cfg))
+    y_gpu = to_np(r["y_perm"])
+    pp_g = to_np(r["pair_pos"])
+    y_rows = np.stack([y_gpu[pp_g[t * cfg.k:(t + 1) * cfg.k]] for t in toks])
+    assert_close(y_rows.reshape(-1, cfg.d), y_ref.reshape(-1, cfg.d), "y_perm (sampled)")
+    assert_close(to_np(r["shared_y"])[toks], sh_ref, "shared_y (sampled)")
+    assert_close_bf16(to_np(r["out"])[toks], out_ref, "out (sampled)")
+    return r, L, x
+
+
+def test_decode_b1(big, orc):
+    r, L, x = _run_big(big, gen.get("decode_b1"), orc, 1)
+    # fp32 output too, under the strict bar
+    out32 = L(x, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(to_np(out32)))
+
+
+def test_decode_b64(big, orc):
+    r, L, x = _run_big(big, gen.get("decode_b64"), orc, 6)
+    # batch composition: token 0 alone equals token 0 of the batch, bit for bit
+    alone = L(x[:1].contiguous())
+    full = L(x)
+    torch.cuda.synchronize()
+    assert torch.equal(alone[0].view(torch.int16), full[0].view(torch.int16))
+
+
+def test_prefill_4096(big, orc):
+    _run_big(big, gen.get("prefill_4096"), orc, 4)
+
+
+def test_prefill_16384_zipf(big, orc):
+    r, _, _ = _run_big(big, gen.get("prefill_16384_zipf"), orc, 4)
+    counts = to_np(r["counts"])
+    srt = np.sort(counts)
+    gini = 1 - 2 * np.sum(np.cumsum(srt) / srt.sum()) / srt.size + 1 / srt.size
+    log(f"  zipf histogram: max {counts.max()} min {counts.min()} gini {gini:.3f}")
+    assert counts.max() > 1000
