@@ -62,6 +62,7 @@ def _load_host():
 def _load_dev():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (bind to the HIP runtime torch loaded; see the binding)
         from . import build as _b
         if not os.path.exists(_b.DEV_LIB):
             raise RuntimeError(f"{_b.DEV_LIB} is not built; run gen.build.build()")

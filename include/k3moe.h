@@ -177,6 +177,18 @@ k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank*
                               const void* x, const int32_t* offsets, const int32_t* sorted_pair,
                               float* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two halves of k3moe_expert_ffn, one kernel each (same kernels, same
+ * bits):
+ * gate/up + SiLU-GLU:  h [T*k][f] fp32, row q = silu(Wg x) * (Wu x) of
+ *   expert e on token sorted_pair[q] / k (e as for k3moe_expert_ffn);
+ * down:  y [T*k][d] fp32, row q = Wd_e h[q].
+ * No workspace. */
+k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_bank* bank,
+                                 const void* x, const int32_t* offsets,
+                                 const int32_t* sorted_pair, float* h, void* stream);
+k3moe_status k3moe_expert_down(const k3moe_shape* shape, const k3moe_expert_bank* bank,
+                               const float* h, const int32_t* offsets, float* y, void* stream);
+
 /* Shared experts on a BF16 bank (n_experts = n_shared, f = f_shared):
  *   y [T][d] fp32 = sum over the bank's experts in order of each expert's FFN.
  * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_SHARED_FFN). */

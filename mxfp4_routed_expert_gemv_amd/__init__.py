@@ -27,8 +27,9 @@ DIAG_COUNT = 4
 STATUS = {0: "K3MOE_OK", 1: "K3MOE_EINVAL", 2: "K3MOE_ESHAPE", 3: "K3MOE_EALIGN",
           4: "K3MOE_EWORKSPACE", 5: "K3MOE_EUNSUPPORTED", 6: "K3MOE_EHIP"}
 EXPORTS = ["k3moe_workspace_bytes", "k3moe_mxfp4_bytes", "k3moe_path_class", "k3moe_route",
-           "k3moe_permute", "k3moe_expert_ffn", "k3moe_shared_ffn", "k3moe_combine",
-           "k3moe_layer", "k3moe_status_str", "k3moe_last_error"]
+           "k3moe_permute", "k3moe_expert_ffn", "k3moe_expert_gateup", "k3moe_expert_down",
+           "k3moe_shared_ffn", "k3moe_combine", "k3moe_layer", "k3moe_status_str",
+           "k3moe_last_error"]
 
 
 class Shape(ctypes.Structure):
@@ -56,6 +57,10 @@ class K3moeError(RuntimeError):
 
 
 def _load():
+    # torch's HIP runtime first: when torch is used in the same process,
+    # libk3moe must bind to the runtime torch already loaded (same soname)
+    # rather than bring a second copy that then finds no device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build()); "
                           "the layer has no implementation other than the HIP library")
@@ -74,6 +79,10 @@ def _load():
     lib.k3moe_permute.argtypes = [SP, P, P, P, P, P, P, P, S, P]
     lib.k3moe_expert_ffn.restype = ctypes.c_int
     lib.k3moe_expert_ffn.argtypes = [SP, ctypes.POINTER(ExpertBank), P, P, P, P, P, S, P]
+    lib.k3moe_expert_gateup.restype = ctypes.c_int
+    lib.k3moe_expert_gateup.argtypes = [SP, ctypes.POINTER(ExpertBank), P, P, P, P, P]
+    lib.k3moe_expert_down.restype = ctypes.c_int
+    lib.k3moe_expert_down.argtypes = [SP, ctypes.POINTER(ExpertBank), P, P, P, P]
     lib.k3moe_shared_ffn.restype = ctypes.c_int
     lib.k3moe_shared_ffn.argtypes = [SP, ctypes.POINTER(ExpertBank), P, P, P, S, P]
     lib.k3moe_combine.restype = ctypes.c_int
@@ -155,6 +164,17 @@ def k3moe_expert_ffn(shape, bank: ExpertBank, x, offsets, sorted_pair, y, worksp
     _check(lib.k3moe_expert_ffn(ctypes.byref(shape), ctypes.byref(bank), _addr(x),
                                 _addr(offsets), _addr(sorted_pair), _addr(y), wp, wb,
                                 _stream(stream)))
+
+
+def k3moe_expert_gateup(shape, bank: ExpertBank, x, offsets, sorted_pair, h, stream=None):
+    _check(lib.k3moe_expert_gateup(ctypes.byref(shape), ctypes.byref(bank), _addr(x),
+                                   _addr(offsets), _addr(sorted_pair), _addr(h),
+                                   _stream(stream)))
+
+
+def k3moe_expert_down(shape, bank: ExpertBank, h, offsets, y, stream=None):
+    _check(lib.k3moe_expert_down(ctypes.byref(shape), ctypes.byref(bank), _addr(h),
+                                 _addr(offsets), _addr(y), _stream(stream)))
 
 
 def k3moe_shared_ffn(shape, bank: ExpertBank, x, y, workspace=None, stream=None):

@@ -129,7 +129,8 @@ RouteWs carve_route(const k3moe_shape& s, void* ws, size_t* bytes) {
 PermuteWs carve_permute(const k3moe_shape& s, void* ws, size_t* bytes) {
   Carver c(ws);
   PermuteWs r;
-  const size_t nchunks = (size_t)((s.T + kPermChunk - 1) / kPermChunk);
+  const int ch = permute_chunk_tokens(s.k);
+  const size_t nchunks = (size_t)((s.T + ch - 1) / ch);
   r.chunk_base = c.take<int32_t>(nchunks * s.E);
   if (bytes) *bytes = c.off;
   return r;
@@ -138,8 +139,6 @@ PermuteWs carve_permute(const k3moe_shape& s, void* ws, size_t* bytes) {
 ExpertWs carve_expert(const k3moe_shape& s, void* ws, size_t* bytes) {
   Carver c(ws);
   ExpertWs r;
-  r.active = c.take<int32_t>(s.E);
-  r.n_active = c.take<int32_t>(1);
   r.h = c.take<float>((size_t)s.T * s.k * s.f);
   if (bytes) *bytes = c.off;
   return r;
@@ -272,6 +271,35 @@ k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank*
   return hip_status(launch_expert_ffn(s, *bank, x, offsets, sorted_pair, y, ws,
                                       static_cast<hipStream_t>(stream)),
                     "k3moe_expert_ffn launch");
+}
+
+k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_bank* bank,
+                                 const void* x, const int32_t* offsets,
+                                 const int32_t* sorted_pair, float* h, void* stream) {
+  K3_CHECK(check_shape(shape));
+  const k3moe_shape& s = *shape;
+  K3_CHECK(check_routed_bank(s, bank));
+  if (s.T == 0) return ok();
+  K3_CHECK(need_ptr(x, "x"));
+  K3_CHECK(need_ptr(offsets, "offsets"));
+  K3_CHECK(need_ptr(sorted_pair, "sorted_pair"));
+  K3_CHECK(need_ptr(h, "h"));
+  return hip_status(launch_expert_gateup(s, *bank, x, offsets, sorted_pair, h,
+                                         static_cast<hipStream_t>(stream)),
+                    "k3moe_expert_gateup launch");
+}
+
+k3moe_status k3moe_expert_down(const k3moe_shape* shape, const k3moe_expert_bank* bank,
+                               const float* h, const int32_t* offsets, float* y, void* stream) {
+  K3_CHECK(check_shape(shape));
+  const k3moe_shape& s = *shape;
+  K3_CHECK(check_routed_bank(s, bank));
+  if (s.T == 0) return ok();
+  K3_CHECK(need_ptr(h, "h"));
+  K3_CHECK(need_ptr(offsets, "offsets"));
+  K3_CHECK(need_ptr(y, "y"));
+  return hip_status(launch_expert_down(s, *bank, h, offsets, y, static_cast<hipStream_t>(stream)),
+                    "k3moe_expert_down launch");
 }
 
 k3moe_status k3moe_shared_ffn(const k3moe_shape* shape, const k3moe_expert_bank* bank,

@@ -21,16 +21,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int o = (int)(i - t * dq) * 4;
   float4 acc = shared_y ? *reinterpret_cast<const float4*>(shared_y + t * d + o)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < k; ++s) {
-    const float w = topk_w[t * k + s];
-    const int pp = pair_pos[t * k + s];
-    if (w != 0.0f && pp >= 0) {
-      const float4 v = *reinterpret_cast<const float4*>(y_perm + (size_t)pp * d + o);
-      acc.x = __builtin_fmaf(w, v.x, acc.x);
-      acc.y = __builtin_fmaf(w, v.y, acc.y);
-      acc.z = __builtin_fmaf(w, v.z, acc.z);
-      acc.w = __builtin_fmaf(w, v.w, acc.w);
+  // Slots in groups of 8: every load of a group is issued before the first
+  // multiply-add (dropped pairs read row 0 and are skipped), so the k row
+  // loads overlap instead of forming a chain.
+  constexpr int G = 8;
+  for (int s0 = 0; s0 < k; s0 += G) {
+    float w[G];
+    int pp[G];
+    float4 v[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const bool in = s0 + u < k;
+      w[u] = in ? topk_w[t * k + s0 + u] : 0.0f;
+      pp[u] = in ? pair_pos[t * k + s0 + u] : -1;
     }
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      v[u] = *reinterpret_cast<const float4*>(y_perm + (size_t)(pp[u] >= 0 ? pp[u] : 0) * d + o);
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (w[u] != 0.0f && pp[u] >= 0) {
+        acc.x = __builtin_fmaf(w[u], v[u].x, acc.x);
+        acc.y = __builtin_fmaf(w[u], v[u].y, acc.y);
+        acc.z = __builtin_fmaf(w[u], v[u].z, acc.z);
+        acc.w = __builtin_fmaf(w[u], v[u].w, acc.w);
+      }
   }
   if (OUT_BF16) {
     uint2 pk;

@@ -10,202 +10,494 @@
 // wave are combined by a fixed butterfly.  Every (token, output) reduction
 // has the same order whatever else is in the batch.
 //
-// Work unit: one wave = (active expert, group of R output rows); the wave
-// loops over that expert's tokens, MT at a time, so a weight row is fetched
-// from HBM once per call however many tokens chose the expert.
+// Routed kernels are persistent: each workgroup lists the experts that have
+// pairs (in LDS, once), and each wave walks work items (expert, group of
+// output rows) with a stride of the grid, issuing the next item's weight loads
+// before computing the current one, so a wave always has a weight tile in
+// flight.  A weight row is fetched from HBM once per call however many tokens
+// chose the expert: the item loops over the expert's tokens with its rows held
+// in registers.
 #include "internal.h"
 #include "kern_common.h"
 
 namespace k3 {
 namespace {
 
-// ------------------------------------------------------------ active experts
-// Experts with at least one pair, in ascending id; one workgroup (E <= 1024).
-__global__ __launch_bounds__(1024) void build_active(const int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ active,
-                                                     int32_t* __restrict__ n_active, int E) {
-  __shared__ int sums[1024];
-  const int e = threadIdx.x;
-  const int flag = (e < E && offsets[e + 1] > offsets[e]) ? 1 : 0;
-  sums[e] = flag;
+// ---------------------------------------------------------------- reductions
+// Transposed butterfly over the wave for NV values per lane (NV a power of 2,
+// <= 64).  At distance DIST a lane keeps half of its values and adds its
+// partner's copy of them, so after log2(64) steps lane l holds the full sum
+// of value index l >> (6 - log2 NV).  Every value is summed with the same
+// pairing sequence (32, 16, 8, 4, 2, 1) as a plain butterfly, hence the same
+// bits, whatever NV is.
+template <int NV, int DIST>
+struct XReduce {
+  static __device__ __forceinline__ void run(float* v, int lane) {
+    if constexpr (NV > 1) {
+      constexpr int H = NV / 2;
+      const bool up = (lane & DIST) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float send = up ? v[i] : v[H + i];
+        const float keep = up ? v[H + i] : v[i];
+        v[i] = keep + __shfl_xor(send, DIST, kWave);
+      }
+      if constexpr (DIST > 1) XReduce<H, DIST / 2>::run(v, lane);
+    } else {
+      v[0] = v[0] + __shfl_xor(v[0], DIST, kWave);
+      if constexpr (DIST > 1) XReduce<1, DIST / 2>::run(v, lane);
+    }
+  }
+};
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
+// ------------------------------------------------------- work-item metadata
+// Loads here are never guarded: out-of-range lanes read a clamped, valid
+// address and their value is discarded.  A guarded load gets a basic block of
+// its own and is waited on before the next one is issued.
+
+// Per workgroup, in LDS: the experts that have pairs (ascending), their
+// sorted-pair ranges and the tokens of their first NTOK pairs.
+template <int NTOK>
+struct Meta {
+  int n_act;
+  int act[1024];
+  int tok[NTOK > 0 ? NTOK : 1][1024];
+};
+
+// 256 threads.  offsets has E + 1 entries; E <= 1024.
+template <int NTOK>
+__device__ __forceinline__ void stage_meta(const int32_t* __restrict__ offsets,
+                                           const int32_t* __restrict__ sorted_pair, int E, int k,
+                                           Meta<NTOK>& m, int* sums) {
+  const int tid = threadIdx.x;
+  int o[5];
+#pragma unroll
+  for (int u = 0; u < 5; ++u) o[u] = offsets[min(tid * 4 + u, E)];
+  int f[4], c = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    f[u] = (tid * 4 + u < E && o[u + 1] > o[u]) ? 1 : 0;
+    c += f[u];
+  }
+  sums[tid] = c;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int add = (e >= o) ? sums[e - o] : 0;
+  for (int dd = 1; dd < 256; dd <<= 1) {
+    const int add = tid >= dd ? sums[tid - dd] : 0;
     __syncthreads();
-    sums[e] += add;
+    sums[tid] += add;
     __syncthreads();
   }
-  if (flag) active[sums[e] - 1] = e;
-  if (e == 1023) *n_active = sums[1023];
+  int pos = sums[tid] - c;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (f[u]) m.act[pos++] = tid * 4 + u;
+  if (tid == 255) m.n_act = sums[255];
+  __syncthreads();
+  if constexpr (NTOK > 0) {
+    const int n = m.n_act;
+    if (n > 0) {
+      int tk[4][NTOK];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = m.act[min(tid + 256 * u, n - 1)];
+        const int q0 = offsets[e], q1 = offsets[e + 1] - 1;
+#pragma unroll
+        for (int mt = 0; mt < NTOK; ++mt) tk[u][mt] = sorted_pair[min(q0 + mt, q1)];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (tid + 256 * u < n)
+#pragma unroll
+          for (int mt = 0; mt < NTOK; ++mt) m.tok[mt][tid + 256 * u] = tk[u][mt] / k;
+    }
+    __syncthreads();
+  }
+}
+
+// Copy n16 16-byte words of one activation row into LDS (256 threads).
+__device__ __forceinline__ void stage_row(const uint4* __restrict__ src, int n16, uint4* dst) {
+  constexpr int U = 8;  // up to 2048 words (32 KB)
+  uint4 t[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) t[u] = src[min((int)threadIdx.x + 256 * u, n16 - 1)];
+  // Out-of-range threads rewrite the last word with its own value: stores
+  // stay unconditional, so the loads above are all issued before any wait.
+#pragma unroll
+  for (int u = 0; u < U; ++u) dst[min((int)threadIdx.x + 256 * u, n16 - 1)] = t[u];
+}
+
+// Persistent walk over work items: item it goes to wave it mod (#waves).
+// Overlap of one wave's loads with another's decode comes from occupancy
+// (several waves per SIMD), not from per-wave register double buffering:
+// under register pressure the allocator reuses registers that are still the
+// destinations of in-flight loads, and the wait that forces drains the
+// prefetch.
+template <class Op>
+__device__ __forceinline__ void walk_items_single(const Op& op, int n_items) {
+  typename Op::Regs A;
+  const int GW = gridDim.x * (blockDim.x >> 6);
+  for (int it = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); it < n_items; it += GW) {
+    op.load(it, A);
+    op.compute(it, A);
+  }
+}
+
+// Double-buffered variant: the loads of a wave's next item are issued before
+// its current item is computed.
+template <class Op>
+__device__ __forceinline__ void walk_items(const Op& op, int n_items) {
+  typename Op::Regs A, B;
+  const int GW = gridDim.x * (blockDim.x >> 6);
+  int it = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (it >= n_items) return;
+  op.load(it, A);
+  while (true) {
+    int nx = it + GW;
+    if (nx < n_items) op.load(nx, B);
+    op.compute(it, A);
+    if (nx >= n_items) return;
+    it = nx;
+    nx = it + GW;
+    if (nx < n_items) op.load(nx, A);
+    op.compute(it, B);
+    if (nx >= n_items) return;
+    it = nx;
+  }
 }
 
 template <bool XF32>
 struct XBlock;  // one 32-element activation block
 template <>
 struct XBlock<false> {
+  static constexpr int W = 4;   // 16-byte words per block
   uint4 v[4];
   __device__ __forceinline__ void load(const void* x, size_t elem) {
     const uint16_t* p = static_cast<const uint16_t*>(x) + elem;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = ldg16(p + 8 * i);
   }
+  __device__ __forceinline__ void load_lds(const uint4* xs, int b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = xs[b * 4 + i];
+  }
   __device__ __forceinline__ float dot(const uint4& c) const { return block_dot_bf16(c, v); }
 };
 template <>
 struct XBlock<true> {
+  static constexpr int W = 8;
   uint4 v[8];
   __device__ __forceinline__ void load(const void* x, size_t elem) {
     const float* p = static_cast<const float*>(x) + elem;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = ldg16(p + 4 * i);
   }
+  __device__ __forceinline__ void load_lds(const uint4* xs, int b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = xs[b * 8 + i];
+  }
   __device__ __forceinline__ float dot(const uint4& c) const { return block_dot_f32(c, v); }
 };
 
 // ------------------------------------------------------ routed gate/up (MXFP4)
-// h[p][j] = silu(g) * u for the R gate rows j = rg*R .. rg*R+R-1 of expert e
-// and the matching up rows f + j, for every sorted pair p of e.
-template <int R, int MT, int NU, bool XF32>
-__global__ __launch_bounds__(256) void gemv_gateup_mxfp4(
-    const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, const void* __restrict__ x,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pair,
-    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-    float* __restrict__ h, int d, int f, int k, int rgroups) {
-  constexpr int NR = 2 * R;
-  const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int j = wid / rgroups, rg = wid - j * rgroups;
-  if (j >= *n_active) return;
-  const int e = active[j];
-  const int p0 = offsets[e], p1 = offsets[e + 1];
-  const int nb = d >> 5;
-  const size_t rb = (size_t)(d >> 1), sb = (size_t)nb;
-  const uint8_t* qe = w13 + (size_t)e * 2 * f * rb;
-  const uint8_t* se = w13s + (size_t)e * 2 * f * sb;
-  int rows[NR];
-#pragma unroll
-  for (int r = 0; r < R; ++r) { rows[r] = rg * R + r; rows[R + r] = f + rg * R + r; }
+// Item (j, rg): gate rows rg*R .. rg*R+R-1 of the j-th active expert and the
+// matching up rows f + ...; for every sorted pair p of that expert,
+// h[p][row] = silu(g) * u.  Lane l owns scale blocks l, l+64, ... (NU per
+// pass).  XLDS: the batch is one token whose row sits in LDS.
+template <int R, int MT, int NU, bool XF32, bool XLDS>
+struct GateUpOp {
+  static constexpr int NR = 2 * R;
+  static constexpr int NV = NR * MT;
+  const uint8_t* w13;
+  const uint8_t* w13s;
+  const void* x;
+  const int32_t* sorted_pair;
+  float* h;
+  const Meta<XLDS ? 0 : MT>* meta;
+  const uint4* xs;
+  int d, f, k, rgroups;
 
-  for (int p = p0; p < p1; p += MT) {
-    float acc[NR][MT];
-    size_t xoff[MT];
-    bool tv[MT];
+  const int32_t* offsets;
+
+  struct Regs {
+    uint4 q[NU][NR];
+    uint32_t s[NU][NR];
+    int p0, p1;
+  };
+
+  __device__ __forceinline__ void load_blocks(int e, int rg, int b0, Regs& r) const {
+    const int lane = threadIdx.x & 63, nb = d >> 5;
+    const size_t rb = (size_t)(d >> 1), sb = (size_t)nb;
+    const uint8_t* qe = w13 + (size_t)e * 2 * f * rb;
+    const uint8_t* se = w13s + (size_t)e * 2 * f * sb;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      tv[mt] = p + mt < p1;
-      xoff[mt] = tv[mt] ? (size_t)(sorted_pair[p + mt] / k) * d : 0;
+    for (int u = 0; u < NU; ++u) {
+      const int b = min(b0 + lane + kWave * u, nb - 1);
 #pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r][mt] = 0.0f;
+      for (int i = 0; i < NR; ++i) {
+        const size_t row = (size_t)(i < R ? rg * R + i : f + rg * R + i - R);
+        r.q[u][i] = ldg16(qe + row * rb + (size_t)b * 16);
+        r.s[u][i] = se[row * sb + b];
+      }
     }
-    for (int b0 = 0; b0 < nb; b0 += kWave * NU) {
-      uint4 cq[NU][NR];
-      uint32_t cs[NU][NR];
+  }
+
+  __device__ __forceinline__ void load(int it, Regs& r) const {
+    const int j = it / rgroups, rg = it - j * rgroups, e = meta->act[j];
+    r.p0 = offsets[e];   // issued before the weights: waiting for them keeps
+    r.p1 = offsets[e + 1];  // the weight loads in flight
+    load_blocks(e, rg, 0, r);
+  }
+
+  __device__ __forceinline__ void compute(int it, Regs& r) const {
+    const int lane = threadIdx.x & 63, nb = d >> 5;
+    const int j = it / rgroups, rg = it - j * rgroups, e = meta->act[j];
+    const int p0 = r.p0, p1 = r.p1;
+    for (int p = p0; p < p1; p += MT) {
+      float v[NV];
+      size_t xo[MT];
+      bool tv[MT];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int b = b0 + lane + kWave * u;
-        if (b < nb) {
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            cq[u][r] = ldg16(qe + rows[r] * rb + (size_t)b * 16);
-            cs[u][r] = se[rows[r] * sb + b];
-          }
-        }
+      for (int mt = 0; mt < MT; ++mt) {
+        tv[mt] = p + mt < p1;
+        int tok = 0;
+        if (!XLDS) tok = (p == p0) ? meta->tok[mt][j] : sorted_pair[min(p + mt, p1 - 1)] / k;
+        xo[mt] = (size_t)tok * d;
       }
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int b = b0 + lane + kWave * u;
-        if (b < nb) {
+      for (int i = 0; i < NV; ++i) v[i] = 0.0f;
+      for (int b0 = 0; b0 < nb; b0 += kWave * NU) {
+        if (b0 > 0) load_blocks(e, rg, b0, r);   // rows longer than one pass
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int bu = b0 + lane + kWave * u;
+          const bool ok = bu < nb;
+          const int b = min(bu, nb - 1);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             if (!tv[mt]) continue;
             XBlock<XF32> xb;
-            xb.load(x, xoff[mt] + (size_t)b * 32);
+            if (XLDS) xb.load_lds(xs, b);
+            else xb.load(x, xo[mt] + (size_t)b * 32);
 #pragma unroll
-            for (int r = 0; r < NR; ++r) acc[r][mt] = __builtin_fmaf(xb.dot(cq[u][r]), e8m0_to_f32(cs[u][r]), acc[r][mt]);
+            for (int i = 0; i < NR; ++i) {
+              const float t = __builtin_fmaf(xb.dot(r.q[u][i]), e8m0_to_f32(r.s[u][i]),
+                                             v[i * MT + mt]);
+              v[i * MT + mt] = ok ? t : v[i * MT + mt];
+              // one row's 32 decoded weights live at a time
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
+      if (nb > kWave * NU && p + MT < p1) load_blocks(e, rg, 0, r);
+      XReduce<NV, 32>::run(v, lane);
+      // lane l now holds value index l >> (6 - log2 NV): gate rows in the
+      // lower half of the lanes, the matching up rows 32 lanes higher.
+      const float uval = __shfl_xor(v[0], 32, kWave);
+      constexpr int SH = 6 - ilog2(NV);
+      const int idx = lane >> SH;
+      if (lane < 32 && (lane & ((1 << SH) - 1)) == 0) {
+        const int i = idx / MT, mt = idx - i * MT;
+        if (p + mt < p1) h[(size_t)(p + mt) * f + rg * R + i] = silu_mul(v[0], uval);
+      }
     }
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[r][mt] = wave_sum(acc[r][mt]);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (lane == r * MT + mt && tv[mt])
-          h[(size_t)(p + mt) * f + rg * R + r] = silu_mul(acc[r][mt], acc[R + r][mt]);
+  }
+};
+
+template <int R, int MT, int NU, bool XF32, bool XLDS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void gateup_persistent(GateUpOp<R, MT, NU, XF32, XLDS> op, const int32_t* __restrict__ offsets,
+                       int E) {
+  __shared__ Meta<XLDS ? 0 : MT> meta;
+  __shared__ int sums[256];
+  extern __shared__ uint4 xs[];   // the token's row when XLDS (dynamic size)
+  if (XLDS) stage_row(static_cast<const uint4*>(op.x), op.d * (XF32 ? 4 : 2) / 16, xs);
+  stage_meta<XLDS ? 0 : MT>(offsets, op.sorted_pair, E, op.k, meta, sums);
+  op.meta = &meta;
+  op.xs = xs;
+  walk_items_single(op, meta.n_act * op.rgroups);
+}
+
+// ----------------------------------------- routed gate/up, one token (MXFP4)
+// The decode batch of one token: its row sits in LDS, and an item is one gate
+// row with its up row.  The blocks of the two rows are walked in pairs with
+// two register sets used in turn (the loads of the next block are issued
+// before the current block is decoded), so only two blocks are live and the
+// wave keeps a small register footprint: several waves per SIMD then overlap
+// one wave's HBM wait with another's decode.  Per lane the blocks are summed
+// in the same order (lane, lane+64, ...) as the batched kernel, with the same
+// reduction tree, so a token's bits do not depend on the batch.
+struct RowPair {
+  uint4 qg, qu;
+  uint32_t sg, su;
+};
+
+template <bool XF32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void gateup_t1(const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s,
+               const void* __restrict__ x, const int32_t* __restrict__ offsets,
+               float* __restrict__ h, int d, int f, int E) {
+  __shared__ Meta<0> meta;
+  __shared__ int sums[256];
+  extern __shared__ uint4 xs[];
+  stage_row(static_cast<const uint4*>(x), d * (XF32 ? 4 : 2) / 16, xs);
+  stage_meta<0>(offsets, nullptr, E, 1, meta, sums);
+  const int lane = threadIdx.x & 63, nb = d >> 5;
+  const size_t rb = (size_t)(d >> 1), sb = (size_t)nb;
+  const int n_items = meta.n_act * f;
+  const int GW = gridDim.x * 4;
+  for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < n_items; it += GW) {
+    const int j = it / f, row = it - j * f, e = meta.act[j];
+    const int p = offsets[e];
+    const uint8_t* qg = w13 + ((size_t)e * 2 * f + row) * rb;
+    const uint8_t* qu = qg + (size_t)f * rb;
+    const uint8_t* sg = w13s + ((size_t)e * 2 * f + row) * sb;
+    const uint8_t* su = sg + (size_t)f * sb;
+    auto load = [&](int b, RowPair& r) {
+      const int c = min(b, nb - 1);
+      r.qg = ldg16(qg + (size_t)c * 16);
+      r.qu = ldg16(qu + (size_t)c * 16);
+      r.sg = sg[c];
+      r.su = su[c];
+    };
+    float v[2] = {0.0f, 0.0f};
+    auto step = [&](int b, const RowPair& r) {
+      XBlock<XF32> xb;
+      xb.load_lds(xs, min(b, nb - 1));
+      const float tg = __builtin_fmaf(xb.dot(r.qg), e8m0_to_f32(r.sg), v[0]);
+      const float tu = __builtin_fmaf(xb.dot(r.qu), e8m0_to_f32(r.su), v[1]);
+      v[0] = b < nb ? tg : v[0];
+      v[1] = b < nb ? tu : v[1];
+    };
+    RowPair A, B;
+    load(lane, A);
+#pragma unroll 1
+    for (int b = lane; b - lane < nb; b += 2 * kWave) {
+      load(b + kWave, B);
+      step(b, A);
+      load(b + 2 * kWave, A);
+      step(b + kWave, B);
+    }
+    XReduce<2, 32>::run(v, lane);
+    const float uval = __shfl_xor(v[0], 32, kWave);
+    if (lane == 0) h[(size_t)p * f + row] = silu_mul(v[0], uval);
   }
 }
 
 // --------------------------------------------------------- routed down (MXFP4)
-// y[p][o] = sum_j Wd[e][o][j] h[p][j] for rows o = rg*R .. rg*R+R-1.
+// Item (j, rg): rows o = rg*R .. rg*R+R-1 of the j-th active expert;
+// y[p][o] = sum_j Wd[e][o][j] h[p][j] for every sorted pair p of the expert.
+// The h blocks of the item's first MT pairs are fetched with its weights.
 template <int R, int MT, int NU>
-__global__ __launch_bounds__(256) void gemv_down_mxfp4(
-    const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s, const float* __restrict__ h,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, float* __restrict__ y, int d, int f, int rgroups) {
-  const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int j = wid / rgroups, rg = wid - j * rgroups;
-  if (j >= *n_active) return;
-  const int e = active[j];
-  const int p0 = offsets[e], p1 = offsets[e + 1];
-  const int nb = f >> 5;
-  const size_t rb = (size_t)(f >> 1), sb = (size_t)nb;
-  const uint8_t* qe = w2 + (size_t)e * d * rb;
-  const uint8_t* se = w2s + (size_t)e * d * sb;
-  const int o0 = rg * R;
+struct DownOp {
+  static constexpr int NV = R * MT;
+  const uint8_t* w2;
+  const uint8_t* w2s;
+  const float* h;
+  float* y;
+  const Meta<0>* meta;
+  int d, f, rgroups;
 
-  for (int p = p0; p < p1; p += MT) {
-    float acc[R][MT];
-    bool tv[MT];
+  const int32_t* offsets;
+
+  struct Regs {
+    uint4 q[NU][R];
+    uint32_t s[NU][R];
+    uint4 hv[MT][NU][8];
+    int p0, p1;
+  };
+
+  __device__ __forceinline__ void load_blocks(int e, int rg, int b0, Regs& r) const {
+    const int lane = threadIdx.x & 63, nb = f >> 5;
+    const size_t rb = (size_t)(f >> 1), sb = (size_t)nb;
+    const uint8_t* qe = w2 + (size_t)e * d * rb;
+    const uint8_t* se = w2s + (size_t)e * d * sb;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int b = min(b0 + lane + kWave * u, nb - 1);
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const size_t row = (size_t)(rg * R + i);
+        r.q[u][i] = ldg16(qe + row * rb + (size_t)b * 16);
+        r.s[u][i] = se[row * sb + b];
+      }
+    }
+  }
+
+  __device__ __forceinline__ void load_h(int p, int p1, int b0, Regs& r) const {
+    const int lane = threadIdx.x & 63, nb = f >> 5;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      tv[mt] = p + mt < p1;
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r][mt] = 0.0f;
-    }
-    for (int b0 = 0; b0 < nb; b0 += kWave * NU) {
-      uint4 cq[NU][R];
-      uint32_t cs[NU][R];
+      const float* hp = h + (size_t)min(p + mt, p1 - 1) * f;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const int b = b0 + lane + kWave * u;
-        if (b < nb) {
+        const int b = min(b0 + lane + kWave * u, nb - 1);
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            cq[u][r] = ldg16(qe + (size_t)(o0 + r) * rb + (size_t)b * 16);
-            cs[u][r] = se[(size_t)(o0 + r) * sb + b];
-          }
-        }
+        for (int i = 0; i < 8; ++i) r.hv[mt][u][i] = ldg16(hp + (size_t)b * 32 + 4 * i);
       }
+    }
+  }
+
+  __device__ __forceinline__ void load(int it, Regs& r) const {
+    const int j = it / rgroups, rg = it - j * rgroups, e = meta->act[j];
+    r.p0 = offsets[e];
+    r.p1 = offsets[e + 1];
+    load_blocks(e, rg, 0, r);
+    load_h(r.p0, r.p1, 0, r);
+  }
+
+  __device__ __forceinline__ void compute(int it, Regs& r) const {
+    const int lane = threadIdx.x & 63, nb = f >> 5;
+    const int j = it / rgroups, rg = it - j * rgroups, e = meta->act[j];
+    const int p0 = r.p0, p1 = r.p1;
+    for (int p = p0; p < p1; p += MT) {
+      float v[NV];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int b = b0 + lane + kWave * u;
-        if (b < nb) {
+      for (int i = 0; i < NV; ++i) v[i] = 0.0f;
+      for (int b0 = 0; b0 < nb; b0 += kWave * NU) {
+        if (b0 > 0) load_blocks(e, rg, b0, r);
+        if (b0 > 0 || p > p0) load_h(p, p1, b0, r);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const bool ok = b0 + lane + kWave * u < nb;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            if (!tv[mt]) continue;
+            if (p + mt >= p1) continue;
             XBlock<true> hb;
-            hb.load(h, (size_t)(p + mt) * f + (size_t)b * 32);
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r][mt] = __builtin_fmaf(hb.dot(cq[u][r]), e8m0_to_f32(cs[u][r]), acc[r][mt]);
+            for (int i = 0; i < 8; ++i) hb.v[i] = r.hv[mt][u][i];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+              const float t = __builtin_fmaf(hb.dot(r.q[u][i]), e8m0_to_f32(r.s[u][i]),
+                                             v[i * MT + mt]);
+              v[i * MT + mt] = ok ? t : v[i * MT + mt];
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
+      if (nb > kWave * NU && p + MT < p1) load_blocks(e, rg, 0, r);
+      XReduce<NV, 32>::run(v, lane);
+      constexpr int SH = 6 - ilog2(NV);
+      const int idx = lane >> SH;
+      if ((lane & ((1 << SH) - 1)) == 0) {
+        const int i = idx / MT, mt = idx - i * MT;
+        if (p + mt < p1) y[(size_t)(p + mt) * d + rg * R + i] = v[0];
+      }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[r][mt] = wave_sum(acc[r][mt]);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (lane == r * MT + mt && tv[mt]) y[(size_t)(p + mt) * d + o0 + r] = acc[r][mt];
   }
+};
+
+template <int R, int MT, int NU>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void down_persistent(DownOp<R, MT, NU> op, const int32_t* __restrict__ offsets, int E) {
+  __shared__ Meta<0> meta;
+  __shared__ int sums[256];
+  stage_meta<0>(offsets, nullptr, E, 1, meta, sums);
+  op.meta = &meta;
+  walk_items_single(op, meta.n_act * op.rgroups);
 }
 
 // ------------------------------------------------------- shared experts (bf16)
@@ -238,22 +530,17 @@ __global__ __launch_bounds__(256) void gemv_gateup_bf16(const uint16_t* __restri
                                                         const void* __restrict__ x,
                                                         float* __restrict__ hs, int T, int d,
                                                         int fs, int S, int rgroups) {
-  constexpr int NR = 2 * R;
+  constexpr int NR = 2 * R, NV = NR * MT;
   const int lane = threadIdx.x & 63;
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int s = wid / rgroups, rg = wid - s * rgroups;
   if (s >= S) return;
   const int nc = d >> 3;
   const uint16_t* we = w13 + (size_t)s * 2 * fs * d;
-  int rows[NR];
-#pragma unroll
-  for (int r = 0; r < R; ++r) { rows[r] = rg * R + r; rows[R + r] = fs + rg * R + r; }
   for (int t0 = 0; t0 < T; t0 += MT) {
-    float acc[NR][MT];
+    float v[NV];
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[r][mt] = 0.0f;
+    for (int i = 0; i < NV; ++i) v[i] = 0.0f;
     for (int c0 = 0; c0 < nc; c0 += kWave * NU) {
       uint4 wv[NU][NR];
 #pragma unroll
@@ -261,7 +548,10 @@ __global__ __launch_bounds__(256) void gemv_gateup_bf16(const uint16_t* __restri
         const int c = c0 + lane + kWave * u;
         if (c < nc)
 #pragma unroll
-          for (int r = 0; r < NR; ++r) wv[u][r] = ldg16(we + (size_t)rows[r] * d + (size_t)c * 8);
+          for (int i = 0; i < NR; ++i) {
+            const size_t row = (size_t)(i < R ? rg * R + i : fs + rg * R + i - R);
+            wv[u][i] = ldg16(we + row * d + (size_t)c * 8);
+          }
       }
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
@@ -271,21 +561,19 @@ __global__ __launch_bounds__(256) void gemv_gateup_bf16(const uint16_t* __restri
           for (int mt = 0; mt < MT; ++mt)
             if (t0 + mt < T)
 #pragma unroll
-              for (int r = 0; r < NR; ++r)
-                acc[r][mt] = chunk_dot<XF32>(wv[u][r], x, (size_t)(t0 + mt) * d + (size_t)c * 8,
-                                             acc[r][mt]);
+              for (int i = 0; i < NR; ++i)
+                v[i * MT + mt] = chunk_dot<XF32>(wv[u][i], x, (size_t)(t0 + mt) * d + (size_t)c * 8,
+                                                 v[i * MT + mt]);
       }
     }
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[r][mt] = wave_sum(acc[r][mt]);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (lane == r * MT + mt && t0 + mt < T)
-          hs[((size_t)(t0 + mt) * S + s) * fs + rg * R + r] = silu_mul(acc[r][mt], acc[R + r][mt]);
+    XReduce<NV, 32>::run(v, lane);
+    const float uval = __shfl_xor(v[0], 32, kWave);
+    constexpr int SH = 6 - ilog2(NV);
+    const int idx = lane >> SH;
+    if (lane < 32 && (lane & ((1 << SH) - 1)) == 0) {
+      const int i = idx / MT, mt = idx - i * MT;
+      if (t0 + mt < T) hs[((size_t)(t0 + mt) * S + s) * fs + rg * R + i] = silu_mul(v[0], uval);
+    }
   }
 }
 
@@ -295,20 +583,21 @@ __global__ __launch_bounds__(256) void gemv_down_bf16(const uint16_t* __restrict
                                                       const float* __restrict__ hs,
                                                       float* __restrict__ y, int T, int d, int fs,
                                                       int S, int rgroups) {
+  constexpr int NV = R * MT;
   const int lane = threadIdx.x & 63;
   const int rg = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rg >= rgroups) return;
   const int nc = fs >> 3;
   const int o0 = rg * R;
+  constexpr int SH = 6 - ilog2(NV);
+  const int idx = lane >> SH;
   for (int t0 = 0; t0 < T; t0 += MT) {
-    float tot[R][MT];
+    float tot = 0.0f;
     for (int s = 0; s < S; ++s) {
       const uint16_t* we = w2 + (size_t)s * d * fs;
-      float acc[R][MT];
+      float v[NV];
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[r][mt] = 0.0f;
+      for (int i = 0; i < NV; ++i) v[i] = 0.0f;
       for (int c0 = 0; c0 < nc; c0 += kWave * NU) {
         uint4 wv[NU][R];
 #pragma unroll
@@ -316,7 +605,7 @@ __global__ __launch_bounds__(256) void gemv_down_bf16(const uint16_t* __restrict
           const int c = c0 + lane + kWave * u;
           if (c < nc)
 #pragma unroll
-            for (int r = 0; r < R; ++r) wv[u][r] = ldg16(we + (size_t)(o0 + r) * fs + (size_t)c * 8);
+            for (int i = 0; i < R; ++i) wv[u][i] = ldg16(we + (size_t)(o0 + i) * fs + (size_t)c * 8);
         }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -326,69 +615,102 @@ __global__ __launch_bounds__(256) void gemv_down_bf16(const uint16_t* __restrict
             for (int mt = 0; mt < MT; ++mt)
               if (t0 + mt < T)
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-                  acc[r][mt] = chunk_dot<true>(wv[u][r], hs,
-                                               ((size_t)(t0 + mt) * S + s) * fs + (size_t)c * 8,
-                                               acc[r][mt]);
+                for (int i = 0; i < R; ++i)
+                  v[i * MT + mt] = chunk_dot<true>(wv[u][i], hs,
+                                                   ((size_t)(t0 + mt) * S + s) * fs + (size_t)c * 8,
+                                                   v[i * MT + mt]);
         }
       }
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const float v = wave_sum(acc[r][mt]);
-          tot[r][mt] = (s == 0) ? v : tot[r][mt] + v;
-        }
+      XReduce<NV, 32>::run(v, lane);
+      tot = (s == 0) ? v[0] : tot + v[0];   // lane keeps one (row, token) total
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (lane == r * MT + mt && t0 + mt < T) y[(size_t)(t0 + mt) * d + o0 + r] = tot[r][mt];
+    if ((lane & ((1 << SH) - 1)) == 0) {
+      const int i = idx / MT, mt = idx - i * MT;
+      if (t0 + mt < T) y[(size_t)(t0 + mt) * d + o0 + i] = tot;
+    }
   }
 }
 
 inline unsigned blocks_for_waves(int64_t waves) { return (unsigned)((waves + 3) / 4); }
 
-template <int MT>
-hipError_t routed_launch(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
-                         const int32_t* offsets, const int32_t* sorted_pair, float* y,
-                         const ExpertWs& ws, hipStream_t st) {
-  constexpr int RG = 2, RD = 8;
+inline int64_t max_active(const k3moe_shape& s) {
   const int64_t P = s.T * s.k;
-  const int64_t max_active = P < s.E ? P : s.E;
-  const int rg_gu = s.f / RG, rg_dn = s.d / RD;
-  const uint8_t* w13 = static_cast<const uint8_t*>(bank.w13);
-  const uint8_t* w13s = static_cast<const uint8_t*>(bank.w13_scale);
-  const uint8_t* w2 = static_cast<const uint8_t*>(bank.w2);
-  const uint8_t* w2s = static_cast<const uint8_t*>(bank.w2_scale);
-  const unsigned g1 = blocks_for_waves(max_active * rg_gu);
-  if (s.x_dtype == K3MOE_F32)
-    gemv_gateup_mxfp4<RG, MT, 4, true><<<g1, 256, 0, st>>>(w13, w13s, x, offsets, sorted_pair,
-                                                           ws.active, ws.n_active, ws.h, s.d, s.f,
-                                                           s.k, rg_gu);
-  else
-    gemv_gateup_mxfp4<RG, MT, 4, false><<<g1, 256, 0, st>>>(w13, w13s, x, offsets, sorted_pair,
-                                                            ws.active, ws.n_active, ws.h, s.d,
-                                                            s.f, s.k, rg_gu);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const unsigned g2 = blocks_for_waves(max_active * rg_dn);
-  gemv_down_mxfp4<RD, (MT > 2 ? 2 : MT), 1><<<g2, 256, 0, st>>>(
-      w2, w2s, ws.h, offsets, ws.active, ws.n_active, y, s.d, s.f, rg_dn);
-  return hipGetLastError();
+  return P < s.E ? P : s.E;
+}
+
+// Persistent grid: enough workgroups for every item, at most `per_cu` per CU.
+inline unsigned persistent_grid(int64_t items, int per_cu) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  const int64_t cap = (int64_t)cus * per_cu;
+  const int64_t need = (items + 3) / 4;
+  return (unsigned)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+template <int R, int MT, bool XF32, bool XLDS>
+void gateup_launch(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
+                   const int32_t* offsets, const int32_t* sorted_pair, float* h, hipStream_t st) {
+  constexpr int NU = 4;
+  const int rg = s.f / R;
+  const unsigned g = persistent_grid(max_active(s) * rg, 4);
+  GateUpOp<R, MT, NU, XF32, XLDS> op{static_cast<const uint8_t*>(bank.w13),
+                                     static_cast<const uint8_t*>(bank.w13_scale), x, sorted_pair,
+                                     h, nullptr, nullptr, s.d, s.f, s.k, rg, offsets};
+  const size_t lds = XLDS ? (size_t)s.d * (XF32 ? 4 : 2) : 0;
+  gateup_persistent<<<g, 256, lds, st>>>(op, offsets, s.E);
+}
+
+template <int R, int MT>
+void down_launch(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
+                 const int32_t* offsets, float* y, hipStream_t st) {
+  constexpr int NU = 1;
+  const int rg = s.d / R;
+  const unsigned g = persistent_grid(max_active(s) * rg, 4);
+  DownOp<R, MT, NU> op{static_cast<const uint8_t*>(bank.w2),
+                       static_cast<const uint8_t*>(bank.w2_scale), h, y, nullptr, s.d, s.f, rg,
+                       offsets};
+  down_persistent<<<g, 256, 0, st>>>(op, offsets, s.E);
 }
 
 }  // namespace
 
+hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& bank,
+                                const void* x, const int32_t* offsets,
+                                const int32_t* sorted_pair, float* h, hipStream_t st) {
+  // One token: its row is staged in LDS (up to 32 KB).  Items loop over their
+  // expert's tokens one at a time with the weight rows held in registers.
+  const bool f32 = s.x_dtype == K3MOE_F32;
+  const size_t row_bytes = (size_t)s.d * (f32 ? 4 : 2);
+  if (s.T == 1 && row_bytes <= 32768) {
+    const unsigned g = persistent_grid((int64_t)s.k * s.f, 4);
+    const uint8_t* w13 = static_cast<const uint8_t*>(bank.w13);
+    const uint8_t* w13s = static_cast<const uint8_t*>(bank.w13_scale);
+    if (f32) gateup_t1<true><<<g, 256, row_bytes, st>>>(w13, w13s, x, offsets, h, s.d, s.f, s.E);
+    else gateup_t1<false><<<g, 256, row_bytes, st>>>(w13, w13s, x, offsets, h, s.d, s.f, s.E);
+  } else if (f32) {
+    gateup_launch<1, 1, true, false>(s, bank, x, offsets, sorted_pair, h, st);
+  } else {
+    gateup_launch<1, 1, false, false>(s, bank, x, offsets, sorted_pair, h, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
+                              const int32_t* offsets, float* y, hipStream_t st) {
+  if (s.T == 1) down_launch<4, 1>(s, bank, h, offsets, y, st);
+  else down_launch<4, 1>(s, bank, h, offsets, y, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                              const int32_t* offsets, const int32_t* sorted_pair, float* y,
                              const ExpertWs& ws, hipStream_t st) {
-  build_active<<<1, 1024, 0, st>>>(offsets, ws.active, ws.n_active, s.E);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_expert_gateup(s, bank, x, offsets, sorted_pair, ws.h, st);
   if (err != hipSuccess) return err;
-  if (s.T == 1) return routed_launch<1>(s, bank, x, offsets, sorted_pair, y, ws, st);
-  return routed_launch<4>(s, bank, x, offsets, sorted_pair, y, ws, st);
+  return launch_expert_down(s, bank, ws.h, offsets, y, st);
 }
 
 hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,

@@ -12,8 +12,8 @@ namespace k3 {
 
 // Token count up to which a call takes the decode (GEMV) path class.
 constexpr int64_t kGemvMaxT = 64;
-// Tokens per permute chunk (one workgroup, one bit per token in LDS masks).
-constexpr int kPermChunk = 256;
+// Tokens per chunk of the large-batch permute (one bit per token in LDS masks).
+int permute_chunk_tokens(int k);
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -39,8 +39,6 @@ struct PermuteWs {
   int32_t* chunk_base;  // [nchunks][E]
 };
 struct ExpertWs {
-  int32_t* active;    // [E] experts with at least one pair, ascending
-  int32_t* n_active;  // [1]
   float* h;           // [P][f]
 };
 struct SharedWs {
@@ -72,6 +70,11 @@ hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr,
 hipError_t launch_permute(const k3moe_shape& s, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                           int32_t* diag, const PermuteWs& ws, hipStream_t st);
+hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& bank,
+                                const void* x, const int32_t* offsets,
+                                const int32_t* sorted_pair, float* h, hipStream_t st);
+hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
+                              const int32_t* offsets, float* y, hipStream_t st);
 hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                              const int32_t* offsets, const int32_t* sorted_pair, float* y,
                              const ExpertWs& ws, hipStream_t st);

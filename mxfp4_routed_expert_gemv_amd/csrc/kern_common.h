@@ -111,6 +111,44 @@ __device__ __forceinline__ double wave_max(double v) {
   return v;
 }
 
+// DPP move of a 64-bit value (two 32-bit halves); lanes whose source lies
+// outside the row, or whose row is masked off, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK,
+                                                            0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL,
+                                                            ROW_MASK, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum of an unsigned 64-bit value over the wave, returned to every lane
+// (row_shr 1/2/4/8 within rows of 16, then row_bcast 15 and 31 carry the row
+// maxima to lane 63; 0 is the identity).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0x111, 0xF>(v); v = o > v ? o : v;
+  o = dpp_u64<0x112, 0xF>(v); v = o > v ? o : v;
+  o = dpp_u64<0x114, 0xF>(v); v = o > v ? o : v;
+  o = dpp_u64<0x118, 0xF>(v); v = o > v ? o : v;
+  o = dpp_u64<0x142, 0xA>(v); v = o > v ? o : v;
+  o = dpp_u64<0x143, 0xC>(v); v = o > v ? o : v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Order-preserving map of a non-NaN double to uint64 (a < b iff key(a) <
+// key(b)); every key is > 0, so 0 can stand for "no value".
+__device__ __forceinline__ uint64_t order_key(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double key_value(uint64_t k) {
+  const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)u);
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
   // silu(g) * u with silu(g) = g / (1 + e^-g); for g < -88.7 e^-g is +inf
   // and the quotient is -0, never NaN.

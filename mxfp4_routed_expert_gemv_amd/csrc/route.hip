@@ -21,14 +21,16 @@ namespace k3 {
 namespace {
 
 // One wave per expert row; loops over tokens.  Per lane: 8-element chunks
-// c = lane, lane+64, ...; fp64 sequential partial over the lane's chunks,
-// then a fixed butterfly over the wave.
+// c = lane, lane+64, ..., up to 16 per pass, all loads of a pass issued before
+// the arithmetic; fp64 sequential partial over the lane's chunks, then a
+// fixed butterfly over the wave.
 template <bool XF32>
 __global__ __launch_bounds__(256) void router_gemv_f64(const void* __restrict__ x,
                                                        const uint16_t* __restrict__ wr,
                                                        double* __restrict__ logits,
                                                        float* __restrict__ lbound, int T, int d,
                                                        int E) {
+  constexpr int U = 16;
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= E) return;
@@ -37,30 +39,46 @@ __global__ __launch_bounds__(256) void router_gemv_f64(const void* __restrict__ 
   for (int t = 0; t < T; ++t) {
     double acc = 0.0;
     float aabs = 0.0f;
-    for (int c = lane; c < nc; c += kWave) {
-      const uint4 wv = ldg16(wrow + (size_t)c * 8);
-      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-      float xf[8];
-      if (XF32) {
-        const float* xr = static_cast<const float*>(x) + (size_t)t * d + (size_t)c * 8;
-        const uint4 a = ldg16(xr), b = ldg16(xr + 4);
-        xf[0] = __uint_as_float(a.x); xf[1] = __uint_as_float(a.y);
-        xf[2] = __uint_as_float(a.z); xf[3] = __uint_as_float(a.w);
-        xf[4] = __uint_as_float(b.x); xf[5] = __uint_as_float(b.y);
-        xf[6] = __uint_as_float(b.z); xf[7] = __uint_as_float(b.w);
-      } else {
-        const uint16_t* xr = static_cast<const uint16_t*>(x) + (size_t)t * d + (size_t)c * 8;
-        const uint4 a = ldg16(xr);
-        const uint32_t xw[4] = {a.x, a.y, a.z, a.w};
+    for (int c0 = 0; c0 < nc; c0 += kWave * U) {
+      uint4 wv[U], xa[U], xb[U];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { xf[2 * q] = bf16_lo(xw[q]); xf[2 * q + 1] = bf16_hi(xw[q]); }
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + lane + kWave * u;
+        if (c < nc) {
+          wv[u] = ldg16(wrow + (size_t)c * 8);
+          if (XF32) {
+            const float* xr = static_cast<const float*>(x) + (size_t)t * d + (size_t)c * 8;
+            xa[u] = ldg16(xr);
+            xb[u] = ldg16(xr + 4);
+          } else {
+            xa[u] = ldg16(static_cast<const uint16_t*>(x) + (size_t)t * d + (size_t)c * 8);
+          }
+        }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float w0 = bf16_lo(ww[q]), w1 = bf16_hi(ww[q]);
-        acc += (double)xf[2 * q] * (double)w0;      // exact product, rounded sum
-        acc += (double)xf[2 * q + 1] * (double)w1;
-        aabs += fabsf(xf[2 * q] * w0) + fabsf(xf[2 * q + 1] * w1);
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + lane + kWave * u;
+        if (c < nc) {
+          const uint32_t ww[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+          float xf[8];
+          if (XF32) {
+            xf[0] = __uint_as_float(xa[u].x); xf[1] = __uint_as_float(xa[u].y);
+            xf[2] = __uint_as_float(xa[u].z); xf[3] = __uint_as_float(xa[u].w);
+            xf[4] = __uint_as_float(xb[u].x); xf[5] = __uint_as_float(xb[u].y);
+            xf[6] = __uint_as_float(xb[u].z); xf[7] = __uint_as_float(xb[u].w);
+          } else {
+            const uint32_t xw[4] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { xf[2 * q] = bf16_lo(xw[q]); xf[2 * q + 1] = bf16_hi(xw[q]); }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float w0 = bf16_lo(ww[q]), w1 = bf16_hi(ww[q]);
+            acc = __builtin_fma((double)xf[2 * q], (double)w0, acc);      // exact product
+            acc = __builtin_fma((double)xf[2 * q + 1], (double)w1, acc);
+            aabs = aabs + fabsf(xf[2 * q] * w0) + fabsf(xf[2 * q + 1] * w1);
+          }
+        }
       }
     }
     acc = wave_sum(acc);
@@ -82,16 +100,8 @@ __device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-__device__ __forceinline__ void wave_argmax(double& v, int& id) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double ov = __shfl_xor(v, o, kWave);
-    const int oi = __shfl_xor(id, o, kWave);
-    if (better(ov, oi, v, id)) { v = ov; id = oi; }
-  }
-}
-
-// Exact sequential fp64 logit: the oracle's operation sequence.
+// Exact sequential fp64 logit: the oracle's operation sequence (products are
+// exact in fp64, so multiply-add fusion cannot change a bit).
 template <bool XF32>
 __device__ double exact_logit(const void* x, const uint16_t* wr, int t, int e, int d) {
   const uint16_t* wrow = wr + (size_t)e * d;
@@ -99,17 +109,29 @@ __device__ double exact_logit(const void* x, const uint16_t* wr, int t, int e, i
   if (XF32) {
     const float* xr = static_cast<const float*>(x) + (size_t)t * d;
     for (int i = 0; i < d; ++i)
-      acc += (double)xr[i] * (double)__uint_as_float((uint32_t)wrow[i] << 16);
+      acc = __builtin_fma((double)xr[i], (double)__uint_as_float((uint32_t)wrow[i] << 16), acc);
   } else {
     const uint16_t* xr = static_cast<const uint16_t*>(x) + (size_t)t * d;
     for (int i = 0; i < d; ++i)
-      acc += (double)__uint_as_float((uint32_t)xr[i] << 16) *
-             (double)__uint_as_float((uint32_t)wrow[i] << 16);
+      acc = __builtin_fma((double)__uint_as_float((uint32_t)xr[i] << 16),
+                          (double)__uint_as_float((uint32_t)wrow[i] << 16), acc);
   }
   return acc;
 }
 
-// One wave (= one workgroup) per token.
+// Lane-local best not-yet-taken entry by (key desc, j asc); jb = -1 if none.
+__device__ __forceinline__ void lane_best(const uint64_t (&key)[kMaxJ], uint32_t taken,
+                                          uint64_t& kb, int& jb) {
+  kb = 0;
+  jb = -1;
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j)
+    if (!((taken >> j) & 1u) && key[j] > kb) { kb = key[j]; jb = j; }
+}
+
+// One wave (= one workgroup) per token.  Lane l holds experts l + 64 j as
+// order-preserving 64-bit keys; each of k rounds takes the wave maximum with
+// DPP, ties between lanes going to the lower expert id.
 template <bool XF32>
 __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ logits,
                                                    const float* __restrict__ lbound,
@@ -123,6 +145,7 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
   __shared__ double candL[1024];
   __shared__ int candId[1024];
   __shared__ int candTaken[1024];
+  __shared__ int chosen[1024];
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
   if (t >= T) return;
@@ -130,39 +153,47 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
   const double* lrow = logits + (size_t)t * E;
   const float* brow = lbound + (size_t)t * E;
 
-  double v[kMaxJ];
+  uint64_t key[kMaxJ];
   float b[kMaxJ];
   int nonfin = 0;
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) {
     const int e = lane + kWave * j;
-    v[j] = -INFINITY;
+    key[j] = 0;
     b[j] = 0.0f;
     if (j < nj && e < E) {
-      double lv = lrow[e];
+      const double lv = lrow[e];
       if (!isfinite(lv)) ++nonfin;
       if (logits_out) logits_out[(size_t)t * E + e] = (float)lv;
-      v[j] = isnan(lv) ? -INFINITY : lv;
+      key[j] = order_key(isnan(lv) ? -INFINITY : lv);
       b[j] = brow[e];
     }
   }
   nonfin = wave_sum(nonfin);
   if (lane == 0 && nonfin && diag) atomicAdd(&diag[K3MOE_DIAG_NONFINITE_LOGITS], nonfin);
 
-  // k rounds of wave argmax by (logit desc, id asc).
   uint32_t taken = 0;
-  int my_id = -1;  // lane r < k holds the r-th chosen expert
+  uint64_t kb;
+  int jb;
+  lane_best(key, taken, kb, jb);
   for (int r = 0; r < k; ++r) {
-    double bv = -INFINITY;
-    int bi = INT_MAX;
+    const uint64_t m = wave_max_u64(kb);
+    const unsigned long long tied = __ballot(jb >= 0 && kb == m);
+    int wl, wj;
+    if (__popcll(tied) == 1) {
+      wl = __ffsll((long long)tied) - 1;
+      wj = __builtin_amdgcn_readlane(jb, wl);
+    } else {  // equal logits in several lanes: the lowest expert id wins
+      int id = (jb >= 0 && kb == m) ? lane + kWave * jb : INT_MAX;
 #pragma unroll
-    for (int j = 0; j < kMaxJ; ++j) {
-      const int e = lane + kWave * j;
-      if (j < nj && e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
+      for (int o = 32; o > 0; o >>= 1) id = min(id, __shfl_xor(id, o, kWave));
+      wl = id & 63;
+      wj = id >> 6;
     }
-    wave_argmax(bv, bi);
-    if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
-    if (lane == r) my_id = bi;
+    if (lane == wl) {
+      taken |= 1u << wj;
+      lane_best(key, taken, kb, jb);
+    }
   }
 
   // Certificate: every chosen expert's lower bound beats every other
@@ -170,18 +201,18 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
   double lo = INFINITY;
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j)
-    if ((taken >> j) & 1u) lo = fmin(lo, v[j] - (double)b[j]);
+    if ((taken >> j) & 1u) lo = fmin(lo, key_value(key[j]) - (double)b[j]);
   const double tau = wave_min(lo);
   uint32_t cand = 0;
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) {
     const int e = lane + kWave * j;
-    if (j < nj && e < E && !((taken >> j) & 1u) && v[j] + (double)b[j] >= tau) cand |= 1u << j;
+    if (j < nj && e < E && !((taken >> j) & 1u) && key_value(key[j]) + (double)b[j] >= tau)
+      cand |= 1u << j;
   }
   const int nout = wave_sum((int)__popc(cand));
   if (nout > 0) {
-    // Undecided: the chosen ones plus the challengers.  Gather their ids in
-    // ascending id order (lane-major within j), evaluate each exactly.
+    // Undecided: the chosen ones plus the challengers, evaluated exactly.
     const uint32_t all = cand | taken;
     int n = 0;
     for (int j = 0; j < nj; ++j) {
@@ -191,6 +222,7 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
       if (mine) candId[n + before] = lane + kWave * j;
       n += __popcll(bal);
     }
+    for (int q = lane; q < 1024; q += kWave) chosen[q] = 0;
     __syncthreads();
     for (int q = lane; q < n; q += kWave) {
       candL[q] = exact_logit<XF32>(x, wr, t, candId[q], d);
@@ -210,26 +242,40 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
         const int oq = __shfl_xor(owner, o, kWave);
         if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; owner = oq; }
       }
-      if (lane == 0) candTaken[owner] = 1;
-      if (lane == r) my_id = bi;
+      if (lane == 0) { candTaken[owner] = 1; chosen[bi] = 1; }
       __syncthreads();
+    }
+    taken = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j) {
+      const int e = lane + kWave * j;
+      if (j < nj && e < E && chosen[e]) taken |= 1u << j;
     }
     if (lane == 0 && diag) atomicAdd(&diag[K3MOE_DIAG_RECHECKED_TOKENS], 1);
   }
 
-  // Ascending-id order and softmax over the chosen logits.
-  int rank = 0;
-  for (int r = 0; r < k; ++r) {
-    const int other = __shfl(my_id, r, kWave);
-    if (lane < k && other < my_id) ++rank;
-  }
-  const double lv = lane < k ? lrow[my_id] : -INFINITY;
-  const double m = wave_max(lv);
-  const double ex = lane < k ? exp(lv - m) : 0.0;
-  const double z = wave_sum(ex);
-  if (lane < k) {
-    idx_out[(size_t)t * k + rank] = my_id;
-    w_out[(size_t)t * k + rank] = (float)(ex / z);
+  // Softmax over the chosen logits; outputs in ascending expert id.
+  uint64_t kmax = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j)
+    if (((taken >> j) & 1u) && key[j] > kmax) kmax = key[j];
+  const double m = key_value(wave_max_u64(kmax));
+  double zl = 0.0;
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j)
+    if ((taken >> j) & 1u) zl += exp(key_value(key[j]) - m);
+  const double z = wave_sum(zl);
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j) {
+    const bool mine = (taken >> j) & 1u;   // never set for j >= nj
+    const unsigned long long bal = __ballot(mine);
+    if (mine) {
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      idx_out[(size_t)t * k + pos] = lane + kWave * j;
+      w_out[(size_t)t * k + pos] = (float)(exp(key_value(key[j]) - m) / z);
+    }
+    base += __popcll(bal);
   }
 }
 

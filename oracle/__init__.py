@@ -59,7 +59,12 @@ class Oracle:
         lib.oracle_mxfp4_ffn.argtypes = [_I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P]
         lib.oracle_bf16_ffn.argtypes = [_I32, _I32, _P, _P, _I64, _P, _P]
         lib.oracle_combine.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
+        lib.oracle_threads.restype = _I32
+        lib.oracle_threads.argtypes = []
         self.lib = lib
+
+    def threads(self) -> int:
+        return self.lib.oracle_threads()
 
     # ------------------------------------------------------------ formats
     def e2m1(self, code: int) -> float:

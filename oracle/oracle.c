@@ -28,9 +28,13 @@
  * Byte i of a packed row holds element 2i in its low nibble, 2i+1 in its high.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads an OpenMP region of the oracle uses. */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* E2M1 (OCP MX v1.0): bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
  * Exponent field 0 is subnormal: 0.m * 2^0 = m * 0.5; otherwise

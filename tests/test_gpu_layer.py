@@ -159,6 +159,22 @@ def test_k_equals_E_and_k_one(orc):
         _compare_full(r, ref, cfg, "f32")
 
 
+@pytest.mark.parametrize("E,k,T", [(96, 24, 300), (40, 16, 700), (64, 64, 70)])
+def test_wide_routing_chunked_permute(orc, E, k, T):
+    """More experts per token than the decode shapes: exercises both chunk
+    sizes of the large-batch permute (256 tokens for k <= 16, 64 above)."""
+    require_gpu()
+    base = gen.get("tiny")
+    cfg = gen.configs.LayerConfig(**{**base.__dict__, "E": E, "k": k, "T": T,
+                                     "name": f"tiny_E{E}_k{k}_T{T}"})
+    log(f"case {cfg.name}")
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    r = L.staged(wl.x)
+    ref = _full_oracle(cfg, orc, gen.x(cfg))
+    _compare_full(r, ref, cfg, "f32")
+
+
 def test_zero_weight_expert_contributes_nothing(orc):
     """An expert whose routing weight underflows to 0 is skipped, even with
     NaN weights (scale byte 255)."""
