@@ -386,6 +386,65 @@ void gateup_t1(const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s
   }
 }
 
+// ------------------------------------------- routed down, one token (MXFP4)
+// A workgroup takes a chunk of 128 output rows of one active expert, stages
+// that expert's h row (the token's, f floats) in LDS once, and its waves walk
+// items of 4 rows each.  Per lane the blocks are summed in the same order, and
+// reduced with the same tree, as the batched kernel.
+constexpr int kDownT1Rows = 4, kDownT1Chunk = 128;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void down_t1(const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
+             const float* __restrict__ h, const int32_t* __restrict__ offsets,
+             float* __restrict__ y, int d, int f, int E) {
+  constexpr int R = kDownT1Rows;
+  __shared__ Meta<0> meta;
+  __shared__ int sums[256];
+  extern __shared__ uint4 hs[];   // f floats
+  stage_meta<0>(offsets, nullptr, E, 1, meta, sums);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nb = f >> 5;
+  const size_t rb = (size_t)(f >> 1), sb = (size_t)nb;
+  const int chunks = d / kDownT1Chunk;
+  const int n_chunks = meta.n_act * chunks;
+  for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const int j = c / chunks, e = meta.act[j];
+    const int o0 = (c - j * chunks) * kDownT1Chunk;
+    const int p = offsets[e];
+    __syncthreads();   // the previous chunk's h is no longer read
+    stage_row(reinterpret_cast<const uint4*>(h + (size_t)p * f), f / 4, hs);
+    __syncthreads();
+#pragma unroll 1
+    for (int o = o0 + wave * R; o < o0 + kDownT1Chunk; o += 4 * R) {
+      const uint8_t* qe = w2 + ((size_t)e * d + o) * rb;
+      const uint8_t* se = w2s + ((size_t)e * d + o) * sb;
+      float v[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) v[i] = 0.0f;
+#pragma unroll 1
+      for (int b0 = 0; b0 < nb; b0 += kWave) {
+        const int bu = b0 + lane, b = min(bu, nb - 1);
+        uint4 q[R];
+        uint32_t sc[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          q[i] = ldg16(qe + (size_t)i * rb + (size_t)b * 16);
+          sc[i] = se[(size_t)i * sb + b];
+        }
+        XBlock<true> hb;
+        hb.load_lds(hs, b);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const float t = __builtin_fmaf(hb.dot(q[i]), e8m0_to_f32(sc[i]), v[i]);
+          v[i] = bu < nb ? t : v[i];
+        }
+      }
+      XReduce<R, 32>::run(v, lane);
+      constexpr int SH = 6 - ilog2(R);
+      if ((lane & ((1 << SH) - 1)) == 0) y[(size_t)p * d + o + (lane >> SH)] = v[0];
+    }
+  }
+}
+
 // --------------------------------------------------------- routed down (MXFP4)
 // Item (j, rg): rows o = rg*R .. rg*R+R-1 of the j-th active expert;
 // y[p][o] = sum_j Wd[e][o][j] h[p][j] for every sorted pair p of the expert.
@@ -700,8 +759,21 @@ hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& b
 
 hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st) {
-  if (s.T == 1) down_launch<4, 1>(s, bank, h, offsets, y, st);
-  else down_launch<4, 1>(s, bank, h, offsets, y, st);
+  if (s.T == 1 && s.d % kDownT1Chunk == 0 && (size_t)s.f * 4 <= 32768) {
+    const int chunks = s.d / kDownT1Chunk;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    const int64_t need = (int64_t)s.k * chunks, cap = (int64_t)cus * 8;
+    const unsigned g = (unsigned)(need < cap ? need : cap);
+    down_t1<<<g, 256, (size_t)s.f * 4, st>>>(static_cast<const uint8_t*>(bank.w2),
+                                              static_cast<const uint8_t*>(bank.w2_scale), h,
+                                              offsets, y, s.d, s.f, s.E);
+  } else {
+    down_launch<4, 1>(s, bank, h, offsets, y, st);
+  }
   return hipGetLastError();
 }
 

@@ -37,56 +37,60 @@ __global__ __launch_bounds__(256) void router_gemv_f64(const void* __restrict__ 
   const int nc = d / 8;
   const uint16_t* wrow = wr + (size_t)e * d;
   for (int t = 0; t < T; ++t) {
-    double acc = 0.0;
+    // Four independent fp64 partial sums per lane (chunk slot u mod 4), so
+    // the multiply-add chains overlap; any fixed order is covered by the bound.
+    double acc4[4] = {0.0, 0.0, 0.0, 0.0};
     float aabs = 0.0f;
     for (int c0 = 0; c0 < nc; c0 += kWave * U) {
       uint4 wv[U], xa[U], xb[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = c0 + lane + kWave * u;
-        if (c < nc) {
-          wv[u] = ldg16(wrow + (size_t)c * 8);
-          if (XF32) {
-            const float* xr = static_cast<const float*>(x) + (size_t)t * d + (size_t)c * 8;
-            xa[u] = ldg16(xr);
-            xb[u] = ldg16(xr + 4);
-          } else {
-            xa[u] = ldg16(static_cast<const uint16_t*>(x) + (size_t)t * d + (size_t)c * 8);
-          }
+        const int c = min(c0 + lane + kWave * u, nc - 1);
+        wv[u] = ldg16(wrow + (size_t)c * 8);
+        if (XF32) {
+          const float* xr = static_cast<const float*>(x) + (size_t)t * d + (size_t)c * 8;
+          xa[u] = ldg16(xr);
+          xb[u] = ldg16(xr + 4);
+        } else {
+          xa[u] = ldg16(static_cast<const uint16_t*>(x) + (size_t)t * d + (size_t)c * 8);
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = c0 + lane + kWave * u;
-        if (c < nc) {
-          const uint32_t ww[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
-          float xf[8];
-          if (XF32) {
-            xf[0] = __uint_as_float(xa[u].x); xf[1] = __uint_as_float(xa[u].y);
-            xf[2] = __uint_as_float(xa[u].z); xf[3] = __uint_as_float(xa[u].w);
-            xf[4] = __uint_as_float(xb[u].x); xf[5] = __uint_as_float(xb[u].y);
-            xf[6] = __uint_as_float(xb[u].z); xf[7] = __uint_as_float(xb[u].w);
-          } else {
-            const uint32_t xw[4] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w};
+        const bool ok = c0 + lane + kWave * u < nc;
+        const uint32_t ww[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+        float xf[8];
+        if (XF32) {
+          xf[0] = __uint_as_float(xa[u].x); xf[1] = __uint_as_float(xa[u].y);
+          xf[2] = __uint_as_float(xa[u].z); xf[3] = __uint_as_float(xa[u].w);
+          xf[4] = __uint_as_float(xb[u].x); xf[5] = __uint_as_float(xb[u].y);
+          xf[6] = __uint_as_float(xb[u].z); xf[7] = __uint_as_float(xb[u].w);
+        } else {
+          const uint32_t xw[4] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) { xf[2 * q] = bf16_lo(xw[q]); xf[2 * q + 1] = bf16_hi(xw[q]); }
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float w0 = bf16_lo(ww[q]), w1 = bf16_hi(ww[q]);
-            acc = __builtin_fma((double)xf[2 * q], (double)w0, acc);      // exact product
-            acc = __builtin_fma((double)xf[2 * q + 1], (double)w1, acc);
-            aabs = aabs + fabsf(xf[2 * q] * w0) + fabsf(xf[2 * q + 1] * w1);
-          }
+          for (int q = 0; q < 4; ++q) { xf[2 * q] = bf16_lo(xw[q]); xf[2 * q + 1] = bf16_hi(xw[q]); }
         }
+        double a = acc4[u & 3];
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float w0 = bf16_lo(ww[q]), w1 = bf16_hi(ww[q]);
+          a = __builtin_fma((double)xf[2 * q], (double)w0, a);      // exact product
+          a = __builtin_fma((double)xf[2 * q + 1], (double)w1, a);
+          s = s + fabsf(xf[2 * q] * w0) + fabsf(xf[2 * q + 1] * w1);
+        }
+        acc4[u & 3] = ok ? a : acc4[u & 3];
+        aabs = ok ? aabs + s : aabs;
       }
     }
+    double acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     acc = wave_sum(acc);
     aabs = wave_sum(aabs);
     if (lane == 0) {
-      // |acc - exact| <= (d/64 + 6) u S and |oracle - exact| <= d u S with
-      // u = 2^-53 and S = sum|p| <= 1.01 aabs (aabs is an fp32 sum of
-      // rounded |products|, d <= 16384).
+      // |acc - exact| <= (d/64 + 8) u S (per-lane chains, 2 adds, 6 butterfly
+      // levels) and |oracle - exact| <= d u S with u = 2^-53 and
+      // S = sum|p| <= 1.01 aabs (aabs is an fp32 sum of rounded |products|,
+      // d <= 16384).
       const double bnd = (2.0 * d + 64.0) * 0x1p-53 * (double)aabs * 1.02;
       logits[(size_t)t * E + e] = acc;
       lbound[(size_t)t * E + e] = (float)bnd;
@@ -156,19 +160,26 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
   uint64_t key[kMaxJ];
   float b[kMaxJ];
   int nonfin = 0;
+  // Every load is issued (clamped index) before any is used.
+  double lv[kMaxJ];
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j) {
+    const int e = min(lane + kWave * j, E - 1);
+    lv[j] = lrow[e];
+    b[j] = brow[e];
+  }
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) {
     const int e = lane + kWave * j;
-    key[j] = 0;
-    b[j] = 0.0f;
-    if (j < nj && e < E) {
-      const double lv = lrow[e];
-      if (!isfinite(lv)) ++nonfin;
-      if (logits_out) logits_out[(size_t)t * E + e] = (float)lv;
-      key[j] = order_key(isnan(lv) ? -INFINITY : lv);
-      b[j] = brow[e];
-    }
+    const bool ok = j < nj && e < E;
+    if (ok && !isfinite(lv[j])) ++nonfin;
+    key[j] = ok ? order_key(isnan(lv[j]) ? -INFINITY : lv[j]) : 0;
+    b[j] = ok ? b[j] : 0.0f;
   }
+  if (logits_out)
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j)
+      if (j < nj && lane + kWave * j < E) logits_out[(size_t)t * E + lane + kWave * j] = (float)lv[j];
   nonfin = wave_sum(nonfin);
   if (lane == 0 && nonfin && diag) atomicAdd(&diag[K3MOE_DIAG_NONFINITE_LOGITS], nonfin);
 
