@@ -138,8 +138,13 @@ size_t k3moe_workspace_bytes(const k3moe_shape* shape, int op);
  * weight of the pages' shard census).  Host-only helper. */
 uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols);
 
-/* Which path class a call with this shape takes (K3MOE_PATH_GEMV for
- * memory-bound decode batches, K3MOE_PATH_MFMA for large batches). */
+/* Which path class a call with this shape takes.  K3MOE_PATH_MFMA (grouped
+ * GEMMs on the bf16 matrix cores, weights decoded exactly in registers,
+ * h split into two bf16 terms) when T >= 32, x is bf16, d % 256 == 0 and
+ * f % 128 == 0; K3MOE_PATH_GEMV (one pass over each touched expert's weights
+ * per token, fp32 dot products) otherwise.  Results of the two classes agree
+ * within the stated tolerance, not bit for bit.  Returns K3MOE_PATH_GEMV for
+ * an invalid shape. */
 int k3moe_path_class(const k3moe_shape* shape);
 
 /* Router + top-k + softmax.

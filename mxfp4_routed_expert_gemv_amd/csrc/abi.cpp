@@ -207,8 +207,8 @@ uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols) {
 }
 
 int k3moe_path_class(const k3moe_shape* shape) {
-  (void)shape;
-  return K3MOE_PATH_GEMV;
+  if (check_shape(shape) != K3MOE_OK) return K3MOE_PATH_GEMV;
+  return use_mfma(*shape) ? K3MOE_PATH_MFMA : K3MOE_PATH_GEMV;
 }
 
 k3moe_status k3moe_route(const k3moe_shape* shape, const void* x, const void* w_router,

@@ -739,6 +739,7 @@ void down_launch(const k3moe_shape& s, const k3moe_expert_bank& bank, const floa
 hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& bank,
                                 const void* x, const int32_t* offsets,
                                 const int32_t* sorted_pair, float* h, hipStream_t st) {
+  if (use_mfma(s)) return launch_gateup_mfma(s, bank, x, offsets, sorted_pair, h, st);
   // One token: its row is staged in LDS (up to 32 KB).  Items loop over their
   // expert's tokens one at a time with the weight rows held in registers.
   const bool f32 = s.x_dtype == K3MOE_F32;
@@ -759,6 +760,7 @@ hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& b
 
 hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st) {
+  if (use_mfma(s)) return launch_down_mfma(s, bank, h, offsets, y, st);
   if (s.T == 1 && s.d % kDownT1Chunk == 0 && (size_t)s.f * 4 <= 32768) {
     const int chunks = s.d / kDownT1Chunk;
     int dev = 0, cus = 0;

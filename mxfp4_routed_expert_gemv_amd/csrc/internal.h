@@ -10,8 +10,11 @@
 
 namespace k3 {
 
-// Token count up to which a call takes the decode (GEMV) path class.
-constexpr int64_t kGemvMaxT = 64;
+// Smallest token count that takes the matrix-core (MFMA) path class; the
+// class also needs bf16 activations, d % 256 == 0 and f % 128 == 0.
+constexpr int64_t kMfmaMinT = 32;
+bool mfma_shape_ok(const k3moe_shape& s);
+inline bool use_mfma(const k3moe_shape& s) { return s.T >= kMfmaMinT && mfma_shape_ok(s); }
 // Tokens per chunk of the large-batch permute (one bit per token in LDS masks).
 int permute_chunk_tokens(int k);
 
@@ -75,6 +78,11 @@ hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& b
                                 const int32_t* sorted_pair, float* h, hipStream_t st);
 hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st);
+hipError_t launch_gateup_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
+                              const int32_t* offsets, const int32_t* sorted_pair, float* h,
+                              hipStream_t st);
+hipError_t launch_down_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
+                            const int32_t* offsets, float* y, hipStream_t st);
 hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                              const int32_t* offsets, const int32_t* sorted_pair, float* y,
                              const ExpertWs& ws, hipStream_t st);

@@ -102,6 +102,55 @@ def test_tiny_batch_composition_and_order():
     assert torch.equal(prefix, full[:9])
 
 
+# ------------------------------------------------- matrix-core (MFMA) class
+# A shrunken layer with bf16 activations and d % 256 == 0, f % 128 == 0, so
+# batches of 32 tokens or more take the grouped-GEMM path.  The token counts
+# below select every m-tile height (16 .. 80 rows) of the kernels; the skewed
+# variant gives experts several m-tiles and leaves others empty.
+MED = gen.configs.LayerConfig(name="medium", T=200, d=512, f=256, E=32, k=8, n_shared=1,
+                              f_shared=256, x_dtype="bf16", out_dtype="f32", scale_lo=-8,
+                              scale_hi=0)
+
+
+@pytest.mark.parametrize("T,zipf", [(32, None), (100, None), (160, None), (200, None),
+                                    (260, None), (600, 1.1), (1000, 1.1)])
+def test_mfma_class_parity(orc, T, zipf):
+    require_gpu()
+    from mxfp4_routed_expert_gemv_amd import PATH_MFMA
+    cfg = gen.configs.LayerConfig(**{**MED.__dict__, "T": T, "zipf_s": zipf,
+                                     "name": f"medium_T{T}" + ("_zipf" if zipf else "")})
+    log(f"case {cfg.name}")
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    assert L.path_class(T) == PATH_MFMA
+    r = L.staged(wl.x)
+    ref = _full_oracle(cfg, orc, gen.x(cfg))
+    counts = ref["counts"]
+    log(f"  pairs/expert max {counts.max()} min {counts.min()}")
+    _compare_full(r, ref, cfg, "f32")
+    out = L(wl.x)
+    torch.cuda.synchronize()
+    assert torch.equal(out, r["out"])
+
+
+def test_mfma_class_batch_composition():
+    """Within the matrix-core class a token's bits do not depend on the rest
+    of the batch, its position, or the m-tile height the batch size selects."""
+    require_gpu()
+    cfg = MED.with_tokens(200)
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    full = L(wl.x)
+    perm = torch.randperm(200, generator=torch.Generator().manual_seed(3)).to(wl.x.device)
+    shuffled = L(wl.x[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(shuffled, full[perm])
+    for n in (32, 64, 150):   # m-tiles of 16, 32 and 48 rows instead of 64
+        part = L(wl.x[:n].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[:n]), n
+
+
 def test_hand_worked_two_experts(orc):
     """The closed-form 1-token / 2-expert layer (hand-worked fixture), both
     nibble positions, through the C ABI."""
@@ -303,11 +352,12 @@ def test_decode_b1(big, orc):
 
 def test_decode_b64(big, orc):
     r, L, x = _run_big(big, gen.get("decode_b64"), orc, 6)
-    # batch composition: token 0 alone equals token 0 of the batch, bit for bit
-    alone = L(x[:1].contiguous())
+    # batch composition inside the matrix-core class: the first 32 tokens
+    # alone equal the same tokens of the batch of 64, bit for bit
+    part = L(x[:32].contiguous())
     full = L(x)
     torch.cuda.synchronize()
-    assert torch.equal(alone[0].view(torch.int16), full[0].view(torch.int16))
+    assert torch.equal(part.view(torch.int16), full[:32].view(torch.int16))
 
 
 def test_prefill_4096(big, orc):
