@@ -789,6 +789,7 @@ hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank
 
 hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                              float* y, const SharedWs& ws, hipStream_t st) {
+  if (shared_mfma_ok(s)) return launch_shared_mfma(s, bank, x, ws.h, y, st);
   constexpr int RG = 2, RD = 4;
   const int S = bank.n_experts, fs = bank.f, T = (int)s.T;
   const uint16_t* w13 = static_cast<const uint16_t*>(bank.w13);

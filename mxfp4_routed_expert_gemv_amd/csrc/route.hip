@@ -98,6 +98,121 @@ __global__ __launch_bounds__(256) void router_gemv_f64(const void* __restrict__ 
   }
 }
 
+// Large batches: the same fp64 logits on the fp64 matrix cores
+// (MFMA 16x16x4).  A workgroup computes 32 tokens x 32 experts; wave w
+// covers the contraction slice [w d/4, (w+1) d/4), and the four partial
+// sums are added in wave order.  Lane (i = lane % 16, c = lane / 16) holds
+// elements c*8 .. c*8+7 of each 32-element group of its token row (A) and
+// expert row (B); MFMA step q (0..7) takes element c*8 + q from every lane,
+// so each product pairs x and w of the same element.  The bound uses
+// sum|x_i w_i| <= |x| |w| (Cauchy-Schwarz), with the squared norms summed
+// in fp64 (bf16 squares are exact) along the same pass.
+typedef __attribute__((ext_vector_type(4))) double f64x4_t;
+
+__global__ __launch_bounds__(256) void router_mfma_f64(const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ wr,
+                                                       double* __restrict__ logits,
+                                                       float* __restrict__ lbound, int T, int d,
+                                                       int E) {
+  __shared__ double part[4][32][33];
+  __shared__ double nrm[4][2][32];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int li = lane & 15, lc = lane >> 4;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int kq = d / 4;                 // contraction slice per wave (multiple of 64)
+  const int kbeg = wv * kq;
+  const uint16_t* ar[2];
+  const uint16_t* br[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    ar[f] = x + (size_t)min(t0 + f * 16 + li, T - 1) * d + kbeg + lc * 8;
+    br[f] = wr + (size_t)min(e0 + f * 16 + li, E - 1) * d + kbeg + lc * 8;
+  }
+  f64x4_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  double sa[2] = {0.0, 0.0}, sb[2] = {0.0, 0.0};
+
+  uint4 av[2], bv[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) { av[f] = ldg16(ar[f]); bv[f] = ldg16(br[f]); }
+  const int ng = kq / 32;
+#pragma unroll 1
+  for (int gi = 0; gi < ng; ++gi) {
+    const int gn = min(gi + 1, ng - 1);
+    uint4 an[2], bn[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) { an[f] = ldg16(ar[f] + gn * 32); bn[f] = ldg16(br[f] + gn * 32); }
+    double xa[2][8], wb[2][8];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const uint32_t aw[4] = {av[f].x, av[f].y, av[f].z, av[f].w};
+      const uint32_t bw[4] = {bv[f].x, bv[f].y, bv[f].z, bv[f].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xa[f][2 * u] = (double)bf16_lo(aw[u]);
+        xa[f][2 * u + 1] = (double)bf16_hi(aw[u]);
+        wb[f][2 * u] = (double)bf16_lo(bw[u]);
+        wb[f][2 * u + 1] = (double)bf16_hi(bw[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        sa[f] = __builtin_fma(xa[f][u], xa[f][u], sa[f]);
+        sb[f] = __builtin_fma(wb[f][u], wb[f][u], sb[f]);
+      }
+    }
+#pragma unroll
+    for (int qs = 0; qs < 8; ++qs)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[a][qs], wb[b][qs], acc[a][b], 0, 0, 0);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) { av[f] = an[f]; bv[f] = bn[f]; }
+  }
+  // Output element r of fragment (a, b): token a*16 + lc + 4 r, expert b*16 + li.
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[wv][a * 16 + lc + 4 * r][b * 16 + li] = acc[a][b][r];
+  // squared norms: the four lanes c of a row, in lane order
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    double va = sa[f], vb = sb[f];
+    va += __shfl_xor(va, 16, kWave);
+    vb += __shfl_xor(vb, 16, kWave);
+    va += __shfl_xor(va, 32, kWave);
+    vb += __shfl_xor(vb, 32, kWave);
+    if (lc == 0) {
+      nrm[wv][0][f * 16 + li] = va;
+      nrm[wv][1][f * 16 + li] = vb;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int o = tid + 256 * u;
+    const int tt = o >> 5, ee = o & 31;
+    const int t = t0 + tt, e = e0 + ee;
+    if (t < T && e < E) {
+      const double l = ((part[0][tt][ee] + part[1][tt][ee]) + part[2][tt][ee]) + part[3][tt][ee];
+      const double nx = ((nrm[0][0][tt] + nrm[1][0][tt]) + nrm[2][0][tt]) + nrm[3][0][tt];
+      const double nw = ((nrm[0][1][ee] + nrm[1][1][ee]) + nrm[2][1][ee]) + nrm[3][1][ee];
+      // |l - exact| <= (d + 8) 2^-52 S for any internal order of the matrix
+      // core (each step rounds once to fp64), |oracle - exact| <= d 2^-53 S,
+      // S <= sqrt(nx nw) (1 + 2^-40) with the fp64 squared norms.
+      const double bnd = (3.0 * d + 128.0) * 0x1p-53 * sqrt(nx * nw) * 1.02;
+      logits[(size_t)t * E + e] = l;
+      lbound[(size_t)t * E + e] = (float)bnd;
+    }
+  }
+}
+
 constexpr int kMaxJ = 16;  // E <= 1024 = 16 per lane
 
 __device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
@@ -298,7 +413,10 @@ hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr,
   const int T = (int)s.T;
   const bool xf32 = s.x_dtype == K3MOE_F32;
   const dim3 g1((s.E + 3) / 4);
-  if (xf32)
+  if (use_mfma(s))
+    router_mfma_f64<<<dim3((T + 31) / 32, (s.E + 31) / 32), 256, 0, st>>>(
+        static_cast<const uint16_t*>(x), wr, ws.logits, ws.lbound, T, s.d, s.E);
+  else if (xf32)
     router_gemv_f64<true><<<g1, 256, 0, st>>>(x, wr, ws.logits, ws.lbound, T, s.d, s.E);
   else
     router_gemv_f64<false><<<g1, 256, 0, st>>>(x, wr, ws.logits, ws.lbound, T, s.d, s.E);

@@ -107,7 +107,7 @@ def test_tiny_batch_composition_and_order():
 # batches of 32 tokens or more take the grouped-GEMM path.  The token counts
 # below select every m-tile height (16 .. 80 rows) of the kernels; the skewed
 # variant gives experts several m-tiles and leaves others empty.
-MED = gen.configs.LayerConfig(name="medium", T=200, d=512, f=256, E=32, k=8, n_shared=1,
+MED = gen.configs.LayerConfig(name="medium", T=200, d=512, f=256, E=32, k=8, n_shared=2,
                               f_shared=256, x_dtype="bf16", out_dtype="f32", scale_lo=-8,
                               scale_hi=0)
 
