@@ -1,8 +1,8 @@
 // Routed expert FFN for large batches: grouped GEMMs on bf16 MFMA.
 //
-// The pages' expert FFN (kimi-k3-in-c review, "MXFP4 expert matmul" section:
-// nibbles decoded against a shared block exponent, multiplied by unquantised
-// activations) becomes, once tokens are grouped by expert, two GEMMs per
+// The pages' expert FFN (kimi-k3-in-c review, "KDA/MLA/MoE" table;
+// explainer page, "reduction one": nibbles decoded against a shared block
+// exponent, multiplied by unquantised activations) becomes, once tokens are grouped by expert, two GEMMs per
 // expert: H = silu(X W_gate^T) * (X W_up^T) and Y = H W_down^T.  Activations
 // stay exact: x is bf16, and the fp32 h is split into two bf16 terms
 // (hi = RNE(h), lo = RNE(h - hi)) that both go through the matrix core.  The
