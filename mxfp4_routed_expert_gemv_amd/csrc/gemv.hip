@@ -739,7 +739,7 @@ void down_launch(const k3moe_shape& s, const k3moe_expert_bank& bank, const floa
 hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& bank,
                                 const void* x, const int32_t* offsets,
                                 const int32_t* sorted_pair, float* h, hipStream_t st) {
-  if (use_mfma(s)) return launch_gateup_mfma(s, bank, x, offsets, sorted_pair, h, st);
+  if (use_mfma(s)) return launch_gateup_pc(s, bank, x, offsets, sorted_pair, h, st);
   // One token: its row is staged in LDS (up to 32 KB).  Items loop over their
   // expert's tokens one at a time with the weight rows held in registers.
   const bool f32 = s.x_dtype == K3MOE_F32;

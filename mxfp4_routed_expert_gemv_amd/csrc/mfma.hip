@@ -114,6 +114,14 @@ __device__ __forceinline__ ItemRange item_range(long n_items) {
   return ItemRange{lo + (blockIdx.x >> 3), hi, (long)(gridDim.x >> 3)};
 }
 
+// E8M0 byte -> fp32 scale 2^(s-127), branch-free (s = 0: 2^-127, s = 255: NaN).
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+  uint32_t bits = s << 23;
+  bits = s == 0u ? 0x00400000u : bits;
+  bits = s == 255u ? 0x7FC00000u : bits;
+  return __uint_as_float(bits);
+}
+
 // ------------------------------------------------------------------ gate/up
 // Item = (m-tile, n-tile of 128 features); wave w owns features
 // nt*128 + w*32 + [0, 32): B fragments nf = 0,1 are gate rows, 2,3 the up rows
@@ -239,6 +247,223 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           hr[16] = silu_mul(acc[i][1][r], acc[i][3][r]);
         }
       }
+  }
+}
+
+// ------------------------------------------------- gate/up, producer/consumer
+// The same product with the loads taken off the critical path: a workgroup
+// of 8 waves, where waves 4..7 (producers) copy each stage's activations,
+// weight codes and scales from HBM straight into LDS (LDS-DMA, no
+// registers) two stages ahead through a ring of three slots, and waves 0..3
+// (consumers) only read LDS, decode and issue MFMAs.  One s_barrier per
+// stage; before it the producers wait for the next stage's copies and the
+// consumers for their LDS reads, so a slot is refilled only after it was
+// read and read only after it was filled.  Both roles run the same loops and
+// barriers.
+//
+// LDS slot: A [BM rows][16 chunks of 8 bf16], chunk c of row r stored at
+// position c ^ (r & 15); B [256 rows][4 MX blocks of 16 bytes], block b of
+// row r at position b ^ ((r >> 2) & 3); S [256 rows] dword of 4 scales.  The
+// XOR placements spread the 16 rows a consumer fragment reads over all LDS
+// banks.  Local weight row r (0..255) belongs to consumer r / 64, fragment
+// (r / 16) % 4, lane r % 16: fragments 0,1 are gate rows, 2,3 the up rows of
+// the same 32 features.
+constexpr int kPcThreads = 512;
+constexpr int kRing = 3;
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// LDS-DMA copies: lane i's 16 (or 4) bytes from g land at lds_base + 16 i
+// (or 4 i); lds_base must be the same for every lane of the wave.
+__device__ __forceinline__ void dma16_to_lds(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 4, 0, 0);
+}
+
+// m-tile schedule for an NTH-thread workgroup (threads 0..255 own 4 experts each).
+template <int NTH>
+__device__ void build_mtiles_n(const int32_t* __restrict__ offsets, int E, int BM, int* s_mt,
+                               int* s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int c[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * 4 + j;
+    c[j] = 0;
+    if (tid < 256 && e < E) {
+      const int n = offsets[e + 1] - offsets[e];
+      c[j] = n > 0 ? (n + BM - 1) / BM : 0;
+    }
+    sum += c[j];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s_wave[wv] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wv; ++w) base += s_wave[w];
+  int ex = base + incl - sum;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * 4 + j;
+    if (tid < 256 && e < E) s_mt[e] = ex;
+    ex += c[j];
+  }
+  if (tid == NTH - 1) s_mt[E] = ex;
+  __syncthreads();
+}
+
+template <int MF>
+__global__ __launch_bounds__(kPcThreads) void gateup_pc(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
+    const uint8_t* __restrict__ w13s, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pair, float* __restrict__ h, int d, int f, int E, int k) {
+  constexpr int BM = 16 * MF;
+  constexpr int A_BYTES = BM * 256;
+  constexpr int B_BYTES = 256 * 64;
+  constexpr int S_BYTES = 256 * 4;
+  constexpr int SLOT = A_BYTES + B_BYTES + S_BYTES;
+  constexpr int NCOPY = MF + 5;        // copies per producer wave per stage
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * SLOT];
+  __shared__ int s_mt[kMaxE + 1];
+  __shared__ int s_wave[kPcThreads / 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const bool producer = wv >= 4;
+  const int pw = wv - 4;
+  build_mtiles_n<kPcThreads>(offsets, E, BM, s_mt, s_wave);
+  const int NT = f / 128;
+  const ItemRange ir = item_range((long)s_mt[E] * NT);
+  const int nst = d / kBK;
+  const size_t w_row = (size_t)d / 2, s_row = (size_t)d / 32;
+
+  for (long it = ir.first; it < ir.end; it += ir.step) {
+    const int mt = (int)(it / NT), nt = (int)(it - (long)mt * NT);
+    const int e = mtile_expert(s_mt, E, mt);
+    const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
+    const int rows = min(BM, offsets[e + 1] - row0);
+
+    // producer copy sources (element / byte pointers at stage 0)
+    const uint16_t* ap[MF];
+    const uint8_t* bp[4];
+    const uint8_t* spp = nullptr;
+    if (producer) {
+      const uint8_t* wbase = w13 + (size_t)e * 2 * f * w_row;
+      const uint8_t* sbase = w13s + (size_t)e * 2 * f * s_row;
+      auto grow = [&](int r) {
+        const int cw = r >> 6, nf = (r >> 4) & 3;
+        return (nf >= 2 ? f : 0) + nt * 128 + cw * 32 + (nf & 1) * 16 + (r & 15);
+      };
+#pragma unroll
+      for (int q = 0; q < MF; ++q) {
+        const int r = pw * (BM / 4) + q * 4 + (lane >> 4);
+        const int tok = sorted_pair[row0 + min(r, rows - 1)] / k;
+        const int c = (lane & 15) ^ (r & 15);
+        ap[q] = x + (size_t)tok * d + c * 8;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = (pw * 256 + q * 64 + lane) >> 2;
+        const int b = (lane & 3) ^ ((r >> 2) & 3);
+        bp[q] = wbase + (size_t)grow(r) * w_row + b * 16;
+      }
+      spp = sbase + (size_t)grow(pw * 64 + lane) * s_row;
+    }
+    auto issue = [&](int st, int slot) {
+      uint8_t* base = ring + slot * SLOT;
+#pragma unroll
+      for (int q = 0; q < MF; ++q)
+        dma16_to_lds(ap[q] + st * kBK, base + (pw * BM * 4 + q * 64) * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dma16_to_lds(bp[q] + st * (kBK / 2), base + A_BYTES + (pw * 256 + q * 64) * 16);
+      dma4_to_lds(spp + st * 4, base + A_BYTES + B_BYTES + pw * 256);
+    };
+
+    f32x4_t acc[MF][4];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) acc[i][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (producer) {
+      issue(0, 0);
+      if (nst > 1) {
+        issue(1, 1);
+        wait_vmem<NCOPY>();
+      } else {
+        wait_vmem<0>();
+      }
+    }
+    wg_barrier();
+#pragma unroll 1
+    for (int s = 0; s < nst; ++s) {
+      const int slot = s % kRing;
+      if (producer) {
+        if (s + 2 < nst) {
+          issue(s + 2, (s + 2) % kRing);
+          wait_vmem<NCOPY>();
+        } else {
+          wait_vmem<0>();
+        }
+      } else {
+        const uint8_t* base = ring + slot * SLOT;
+        float sc[4];
+        uint4 bq[4];
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          const int r = wv * 64 + nf * 16 + ln;
+          const uint32_t sw = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + r * 4);
+          sc[nf] = e8m0_scale((sw >> (8 * lg)) & 0xFFu);
+          bq[nf] = *reinterpret_cast<const uint4*>(base + A_BYTES + r * 64 + ((lg ^ ((r >> 2) & 3)) * 16));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8_t b[4];
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf) {
+            const uint4& q = bq[nf];
+            const uint32_t wj = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+            b[nf] = decode8(wj, sc[nf]);
+          }
+#pragma unroll
+          for (int i = 0; i < MF; ++i) {
+            const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(
+                base + (i * 16 + ln) * 256 + (((lg * 4 + j) ^ ln) * 16)));
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf)
+              acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nf], acc[i][nf], 0, 0, 0);
+          }
+        }
+        wait_lds();
+      }
+      wg_barrier();
+    }
+
+    if (!producer) {
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = i * 16 + lg * 4 + r;
+          if (m < rows) {
+            float* hr = h + (size_t)(row0 + m) * f + nt * 128 + wv * 32 + ln;
+            hr[0] = silu_mul(acc[i][0][r], acc[i][2][r]);
+            hr[16] = silu_mul(acc[i][1][r], acc[i][3][r]);
+          }
+        }
+    }
   }
 }
 
@@ -683,6 +908,24 @@ hipError_t launch_gateup_mfma(const k3moe_shape& s, const k3moe_expert_bank& b, 
     default: K3_GU(5); break;
   }
 #undef K3_GU
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_pc(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
+                            const int32_t* offsets, const int32_t* sorted_pair, float* h,
+                            hipStream_t st) {
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint8_t* w = static_cast<const uint8_t*>(b.w13);
+  const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
+  const dim3 g(mfma_grid() / 2), blk(kPcThreads);   // one 8-wave workgroup per CU
+#define K3_PC(MF) gateup_pc<MF><<<g, blk, 0, st>>>(xb, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k)
+  const int mf = pick_mf(s, 8);
+  if (mf <= 1) K3_PC(1);
+  else if (mf <= 2) K3_PC(2);
+  else if (mf <= 4) K3_PC(4);
+  else if (mf <= 6) K3_PC(6);
+  else K3_PC(8);
+#undef K3_PC
   return hipGetLastError();
 }
 
