@@ -184,9 +184,14 @@ k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank*
 
 /* The two halves of k3moe_expert_ffn, one kernel each (same kernels, same
  * bits):
- * gate/up + SiLU-GLU:  h [T*k][f] fp32, row q = silu(Wg x) * (Wu x) of
- *   expert e on token sorted_pair[q] / k (e as for k3moe_expert_ffn);
+ * gate/up + SiLU-GLU:  h, row q = silu(Wg x) * (Wu x) of expert e on token
+ *   sorted_pair[q] / k (e as for k3moe_expert_ffn);
  * down:  y [T*k][d] fp32, row q = Wd_e h[q].
+ * h is [T*k][f] 32-bit words.  GEMV path class: fp32 values.  MFMA path
+ * class: each group of 8 features is 8 bf16 values hi, then 8 bf16 values
+ * lo, with hi = RNE_bf16(h) and lo = RNE_bf16(h - hi), so h ~ hi + lo (the
+ * form the matrix cores consume).  A buffer written by k3moe_expert_gateup
+ * is meant for k3moe_expert_down with the same shape.
  * No workspace. */
 k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_bank* bank,
                                  const void* x, const int32_t* offsets,

@@ -760,7 +760,7 @@ hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& b
 
 hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st) {
-  if (use_mfma(s)) return launch_down_mfma(s, bank, h, offsets, y, st);
+  if (use_mfma(s)) return launch_down_pc(s, bank, h, offsets, y, st);
   if (s.T == 1 && s.d % kDownT1Chunk == 0 && (size_t)s.f * 4 <= 32768) {
     const int chunks = s.d / kDownT1Chunk;
     int dev = 0, cus = 0;

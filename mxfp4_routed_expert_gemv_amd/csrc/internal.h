@@ -84,6 +84,8 @@ hipError_t launch_gateup_mfma(const k3moe_shape& s, const k3moe_expert_bank& ban
 hipError_t launch_gateup_pc(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                             const int32_t* offsets, const int32_t* sorted_pair, float* h,
                             hipStream_t st);
+hipError_t launch_down_pc(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
+                          const int32_t* offsets, float* y, hipStream_t st);
 hipError_t launch_down_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                             const int32_t* offsets, float* y, hipStream_t st);
 bool shared_mfma_ok(const k3moe_shape& s);

@@ -452,15 +452,177 @@ __global__ __launch_bounds__(kPcThreads) void gateup_pc(
     }
 
     if (!producer) {
+      // h leaves as split pairs (hi = RNE(h), lo = RNE(h - hi), both bf16)
+      // in blocks of 8 features: 8 hi values, then 8 lo values.
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = i * 16 + lg * 4 + r;
           if (m < rows) {
-            float* hr = h + (size_t)(row0 + m) * f + nt * 128 + wv * 32 + ln;
-            hr[0] = silu_mul(acc[i][0][r], acc[i][2][r]);
-            hr[16] = silu_mul(acc[i][1][r], acc[i][3][r]);
+            uint16_t* hr = reinterpret_cast<uint16_t*>(h + (size_t)(row0 + m) * f);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const float v = silu_mul(acc[i][half][r], acc[i][half + 2][r]);
+              const uint16_t hi = f32_to_bf16(v);
+              const uint16_t lo = f32_to_bf16(v - __uint_as_float((uint32_t)hi << 16));
+              const int col = nt * 128 + wv * 32 + half * 16 + ln;
+              hr[(col >> 3) * 16 + (col & 7)] = hi;
+              hr[(col >> 3) * 16 + 8 + (col & 7)] = lo;
+            }
+          }
+        }
+    }
+  }
+}
+
+// --------------------------------------------------- down, producer/consumer
+// y = H W_down^T with H given as split bf16 pairs (blocks of 8 features:
+// 8 hi, then 8 lo), the layout the producer/consumer gate/up writes.  Same
+// roles, ring and barriers as gateup_pc; the A operand of a stage is BM rows
+// x 128 features x (hi, lo) = 32 sixteen-byte units per row, unit u of row r
+// stored at position u ^ (r & 15).  Local weight row r (0..255) is output
+// nt*256 + r, fragment (r / 16) % 4 of consumer r / 64.  Every step issues
+// the hi product, then the lo product.
+template <int MF>
+__global__ __launch_bounds__(kPcThreads) void down_pc(
+    const float* __restrict__ h, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
+    const int32_t* __restrict__ offsets, float* __restrict__ y, int d, int f, int E) {
+  constexpr int BM = 16 * MF;
+  constexpr int A_BYTES = BM * 512;
+  constexpr int B_BYTES = 256 * 64;
+  constexpr int S_BYTES = 256 * 4;
+  constexpr int SLOT = A_BYTES + B_BYTES + S_BYTES;
+  constexpr int NA = BM * 32 / 4 / 64;   // A copies per producer wave per stage
+  constexpr int NCOPY = NA + 5;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * SLOT];
+  __shared__ int s_mt[kMaxE + 1];
+  __shared__ int s_wave[kPcThreads / 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const bool producer = wv >= 4;
+  const int pw = wv - 4;
+  build_mtiles_n<kPcThreads>(offsets, E, BM, s_mt, s_wave);
+  const int NT = d / 256;
+  const ItemRange ir = item_range((long)s_mt[E] * NT);
+  const int nst = f / kBK;
+  const size_t w_row = (size_t)f / 2, s_row = (size_t)f / 32;
+  const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
+  const size_t h_row = (size_t)f * 4;    // bytes per split row
+
+  for (long it = ir.first; it < ir.end; it += ir.step) {
+    const int mt = (int)(it / NT), nt = (int)(it - (long)mt * NT);
+    const int e = mtile_expert(s_mt, E, mt);
+    const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
+    const int rows = min(BM, offsets[e + 1] - row0);
+
+    const uint8_t* ap[NA];
+    const uint8_t* bp[4];
+    const uint8_t* spp = nullptr;
+    if (producer) {
+      const uint8_t* wbase = w2 + (size_t)e * d * w_row;
+      const uint8_t* sbase = w2s + (size_t)e * d * s_row;
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        const int unit = pw * (BM * 8) + q * 64 + lane;   // BM*32 units over 4 waves
+        const int r = unit >> 5;
+        const int u = (unit & 31) ^ (r & 15);
+        ap[q] = hb + (size_t)(row0 + min(r, rows - 1)) * h_row + u * 16;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = (pw * 256 + q * 64 + lane) >> 2;
+        const int b = (lane & 3) ^ ((r >> 2) & 3);
+        bp[q] = wbase + (size_t)(nt * 256 + r) * w_row + b * 16;
+      }
+      spp = sbase + (size_t)(nt * 256 + pw * 64 + lane) * s_row;
+    }
+    auto issue = [&](int st, int slot) {
+      uint8_t* base = ring + slot * SLOT;
+#pragma unroll
+      for (int q = 0; q < NA; ++q)
+        dma16_to_lds(ap[q] + (size_t)st * 512, base + (pw * BM * 8 + q * 64) * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dma16_to_lds(bp[q] + st * (kBK / 2), base + A_BYTES + (pw * 256 + q * 64) * 16);
+      dma4_to_lds(spp + st * 4, base + A_BYTES + B_BYTES + pw * 256);
+    };
+
+    f32x4_t acc[MF][4];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) acc[i][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (producer) {
+      issue(0, 0);
+      if (nst > 1) {
+        issue(1, 1);
+        wait_vmem<NCOPY>();
+      } else {
+        wait_vmem<0>();
+      }
+    }
+    wg_barrier();
+#pragma unroll 1
+    for (int s = 0; s < nst; ++s) {
+      const int slot = s % kRing;
+      if (producer) {
+        if (s + 2 < nst) {
+          issue(s + 2, (s + 2) % kRing);
+          wait_vmem<NCOPY>();
+        } else {
+          wait_vmem<0>();
+        }
+      } else {
+        const uint8_t* base = ring + slot * SLOT;
+        float sc[4];
+        uint4 bq[4];
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          const int r = wv * 64 + nf * 16 + ln;
+          const uint32_t sw = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + r * 4);
+          sc[nf] = e8m0_scale((sw >> (8 * lg)) & 0xFFu);
+          bq[nf] = *reinterpret_cast<const uint4*>(base + A_BYTES + r * 64 + ((lg ^ ((r >> 2) & 3)) * 16));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8_t b[4];
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf) {
+            const uint4& q = bq[nf];
+            const uint32_t wj = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+            b[nf] = decode8(wj, sc[nf]);
+          }
+          const int c = lg * 4 + j;   // 8-feature block of this step
+#pragma unroll
+          for (int i = 0; i < MF; ++i) {
+            const uint8_t* arow = base + (i * 16 + ln) * 512;
+            const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * c) ^ ln) * 16)));
+            const bf16x8_t al = as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * c + 1) ^ ln) * 16)));
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) {
+              acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[nf], acc[i][nf], 0, 0, 0);
+              acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[nf], acc[i][nf], 0, 0, 0);
+            }
+          }
+        }
+        wait_lds();
+      }
+      wg_barrier();
+    }
+
+    if (!producer) {
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = i * 16 + lg * 4 + r;
+          if (m < rows) {
+            float* yr = y + (size_t)(row0 + m) * d + nt * 256 + wv * 64 + ln;
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) yr[nf * 16] = acc[i][nf][r];
           }
         }
     }
@@ -926,6 +1088,20 @@ hipError_t launch_gateup_pc(const k3moe_shape& s, const k3moe_expert_bank& b, co
   else if (mf <= 6) K3_PC(6);
   else K3_PC(8);
 #undef K3_PC
+  return hipGetLastError();
+}
+
+hipError_t launch_down_pc(const k3moe_shape& s, const k3moe_expert_bank& b, const float* h,
+                          const int32_t* offsets, float* y, hipStream_t st) {
+  const uint8_t* w = static_cast<const uint8_t*>(b.w2);
+  const uint8_t* ws = static_cast<const uint8_t*>(b.w2_scale);
+  const dim3 g(mfma_grid() / 2), blk(kPcThreads);
+#define K3_DPC(MF) down_pc<MF><<<g, blk, 0, st>>>(h, w, ws, offsets, y, s.d, s.f, s.E)
+  const int mf = pick_mf(s, 4);
+  if (mf <= 1) K3_DPC(1);
+  else if (mf <= 2) K3_DPC(2);
+  else K3_DPC(4);
+#undef K3_DPC
   return hipGetLastError();
 }
 
