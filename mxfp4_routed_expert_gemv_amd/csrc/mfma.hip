@@ -250,26 +250,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-// ------------------------------------------------- gate/up, producer/consumer
-// The same product with the loads taken off the critical path: a workgroup
-// of 8 waves, where waves 4..7 (producers) copy each stage's activations,
-// weight codes and scales from HBM straight into LDS (LDS-DMA, no
-// registers) two stages ahead through a ring of three slots, and waves 0..3
-// (consumers) only read LDS, decode and issue MFMAs.  One s_barrier per
-// stage; before it the producers wait for the next stage's copies and the
-// consumers for their LDS reads, so a slot is refilled only after it was
-// read and read only after it was filled.  Both roles run the same loops and
-// barriers.
+// ------------------------------------------- grouped GEMMs, producer/consumer
+// The routed gate/up and down products with the loads taken off the critical
+// path.  A workgroup has 8 waves:
+//   * waves 0..3 (consumers) only read LDS, decode weights and issue MFMAs;
+//   * waves 4,5 copy the activations of each stage (A: x rows gathered by
+//     the expert-sorted pairs, or h rows) into an RA-slot LDS ring;
+//   * waves 6,7 copy the weight codes and scales of each stage (B, streamed
+//     from HBM) into an RB-slot LDS ring.
+// Copies are LDS-DMA (global -> LDS without registers), issued R - 1 stages
+// ahead; each copier wave has its own memory counter, so the HBM stream never
+// waits behind the L2 stream.  One s_barrier per stage: before it every
+// copier waits until the next stage's copies have landed (a constant count
+// of newer copies may stay in flight; copies past the last stage repeat the
+// last stage into a slot nobody reads), and every consumer waits for its LDS
+// reads, so a slot is refilled only after it was read and read only after it
+// was filled.  All roles run the same loops and barriers.
 //
-// LDS slot: A [BM rows][16 chunks of 8 bf16], chunk c of row r stored at
-// position c ^ (r & 15); B [256 rows][4 MX blocks of 16 bytes], block b of
-// row r at position b ^ ((r >> 2) & 3); S [256 rows] dword of 4 scales.  The
-// XOR placements spread the 16 rows a consumer fragment reads over all LDS
-// banks.  Local weight row r (0..255) belongs to consumer r / 64, fragment
-// (r / 16) % 4, lane r % 16: fragments 0,1 are gate rows, 2,3 the up rows of
-// the same 32 features.
+// LDS layouts (XOR placements spread the 16 rows a consumer fragment reads
+// over all banks):
+//   A slot: [BM rows][AU units of 16 bytes], unit u of row r at position
+//     u ^ (r & 15).  Gate/up: AU = 16 units of 8 bf16.  Down: AU = 32, unit
+//     2c = the 8 hi values of feature block c, 2c + 1 the 8 lo values.
+//   B slot: codes [256 rows][4 MX blocks of 16 bytes], block b of row r at
+//     position b ^ ((r >> 2) & 3); then scales [256 rows] one dword (the 4
+//     block scales of the stage).  Local weight row r belongs to consumer
+//     r / 64, fragment (r / 16) % 4, lane r % 16.
 constexpr int kPcThreads = 512;
-constexpr int kRing = 3;
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 template <int N>
@@ -323,268 +330,148 @@ __device__ void build_mtiles_n(const int32_t* __restrict__ offsets, int E, int B
   __syncthreads();
 }
 
-template <int MF>
-__global__ __launch_bounds__(kPcThreads) void gateup_pc(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
-    const uint8_t* __restrict__ w13s, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pair, float* __restrict__ h, int d, int f, int E, int k) {
+// Gate/up (DOWN = false): item = (m-tile, 128 features); B fragments 0,1 are
+// the gate rows and 2,3 the up rows of consumer w's features nt*128 + w*32 +
+// [0, 32); output h as split pairs (8 hi, then 8 lo bf16 per 8 features).
+// Down (DOWN = true): item = (m-tile, 256 outputs); consumer w owns outputs
+// nt*256 + w*64 + [0, 64); A = split h; each step issues the hi product, then
+// the lo product; output y fp32.
+template <int MF, int RA, int RB, bool DOWN>
+__global__ __launch_bounds__(kPcThreads) void mx_gemm_pc(
+    const uint8_t* __restrict__ a_src, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pair, float* __restrict__ out, int d, int f, int E,
+    int k) {
   constexpr int BM = 16 * MF;
-  constexpr int A_BYTES = BM * 256;
-  constexpr int B_BYTES = 256 * 64;
-  constexpr int S_BYTES = 256 * 4;
-  constexpr int SLOT = A_BYTES + B_BYTES + S_BYTES;
-  constexpr int NCOPY = MF + 5;        // copies per producer wave per stage
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * SLOT];
+  constexpr int AU = DOWN ? 32 : 16;
+  constexpr int A_SLOT = BM * AU * 16;
+  constexpr int B_CODES = 256 * 64;
+  constexpr int B_SLOT = B_CODES + 256 * 4;
+  constexpr int NA = BM * AU / 2 / 64;   // A copies per A wave per stage
+  constexpr int NB = 8 + 2;              // B copies per B wave per stage
+  static_assert(RA >= 2 && RB >= 2, "rings need two slots");
+  // at most R - 1 stages of copies are in flight per copier wave; the memory
+  // counter tracks 63
+  static_assert((RA - 1) * NA <= 63 && (RB - 1) * NB <= 63, "memory counter range");
+  __shared__ __attribute__((aligned(16))) uint8_t sA[RA * A_SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[RB * B_SLOT];
   __shared__ int s_mt[kMaxE + 1];
   __shared__ int s_wave[kPcThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const bool producer = wv >= 4;
-  const int pw = wv - 4;
+  const bool a_copier = wv == 4 || wv == 5, b_copier = wv >= 6;
+  const int pa = wv - 4, pb = wv - 6;
   build_mtiles_n<kPcThreads>(offsets, E, BM, s_mt, s_wave);
-  const int NT = f / 128;
+  const int NT = DOWN ? d / 256 : f / 128;
+  const int nst = (DOWN ? f : d) / kBK;
   const ItemRange ir = item_range((long)s_mt[E] * NT);
-  const int nst = d / kBK;
-  const size_t w_row = (size_t)d / 2, s_row = (size_t)d / 32;
+  const size_t w_row = (size_t)(DOWN ? f : d) / 2, s_row = (size_t)(DOWN ? f : d) / 32;
+  const size_t e_rows = DOWN ? (size_t)d : (size_t)2 * f;
+  const size_t a_row = DOWN ? (size_t)f * 4 : (size_t)d * 2;   // bytes per A source row
 
-  for (long it = ir.first; it < ir.end; it += ir.step) {
-    const int mt = (int)(it / NT), nt = (int)(it - (long)mt * NT);
-    const int e = mtile_expert(s_mt, E, mt);
-    const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
-    const int rows = min(BM, offsets[e + 1] - row0);
-
-    // producer copy sources (element / byte pointers at stage 0)
-    const uint16_t* ap[MF];
-    const uint8_t* bp[4];
-    const uint8_t* spp = nullptr;
-    if (producer) {
-      const uint8_t* wbase = w13 + (size_t)e * 2 * f * w_row;
-      const uint8_t* sbase = w13s + (size_t)e * 2 * f * s_row;
-      auto grow = [&](int r) {
-        const int cw = r >> 6, nf = (r >> 4) & 3;
-        return (nf >= 2 ? f : 0) + nt * 128 + cw * 32 + (nf & 1) * 16 + (r & 15);
-      };
-#pragma unroll
-      for (int q = 0; q < MF; ++q) {
-        const int r = pw * (BM / 4) + q * 4 + (lane >> 4);
-        const int tok = sorted_pair[row0 + min(r, rows - 1)] / k;
-        const int c = (lane & 15) ^ (r & 15);
-        ap[q] = x + (size_t)tok * d + c * 8;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = (pw * 256 + q * 64 + lane) >> 2;
-        const int b = (lane & 3) ^ ((r >> 2) & 3);
-        bp[q] = wbase + (size_t)grow(r) * w_row + b * 16;
-      }
-      spp = sbase + (size_t)grow(pw * 64 + lane) * s_row;
-    }
-    auto issue = [&](int st, int slot) {
-      uint8_t* base = ring + slot * SLOT;
-#pragma unroll
-      for (int q = 0; q < MF; ++q)
-        dma16_to_lds(ap[q] + st * kBK, base + (pw * BM * 4 + q * 64) * 16);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dma16_to_lds(bp[q] + st * (kBK / 2), base + A_BYTES + (pw * 256 + q * 64) * 16);
-      dma4_to_lds(spp + st * 4, base + A_BYTES + B_BYTES + pw * 256);
-    };
-
-    f32x4_t acc[MF][4];
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf) acc[i][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    if (producer) {
-      issue(0, 0);
-      if (nst > 1) {
-        issue(1, 1);
-        wait_vmem<NCOPY>();
-      } else {
-        wait_vmem<0>();
-      }
-    }
-    wg_barrier();
-#pragma unroll 1
-    for (int s = 0; s < nst; ++s) {
-      const int slot = s % kRing;
-      if (producer) {
-        if (s + 2 < nst) {
-          issue(s + 2, (s + 2) % kRing);
-          wait_vmem<NCOPY>();
-        } else {
-          wait_vmem<0>();
-        }
-      } else {
-        const uint8_t* base = ring + slot * SLOT;
-        float sc[4];
-        uint4 bq[4];
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-          const int r = wv * 64 + nf * 16 + ln;
-          const uint32_t sw = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + r * 4);
-          sc[nf] = e8m0_scale((sw >> (8 * lg)) & 0xFFu);
-          bq[nf] = *reinterpret_cast<const uint4*>(base + A_BYTES + r * 64 + ((lg ^ ((r >> 2) & 3)) * 16));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x8_t b[4];
-#pragma unroll
-          for (int nf = 0; nf < 4; ++nf) {
-            const uint4& q = bq[nf];
-            const uint32_t wj = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-            b[nf] = decode8(wj, sc[nf]);
-          }
-#pragma unroll
-          for (int i = 0; i < MF; ++i) {
-            const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(
-                base + (i * 16 + ln) * 256 + (((lg * 4 + j) ^ ln) * 16)));
-#pragma unroll
-            for (int nf = 0; nf < 4; ++nf)
-              acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nf], acc[i][nf], 0, 0, 0);
-          }
-        }
-        wait_lds();
-      }
-      wg_barrier();
-    }
-
-    if (!producer) {
-      // h leaves as split pairs (hi = RNE(h), lo = RNE(h - hi), both bf16)
-      // in blocks of 8 features: 8 hi values, then 8 lo values.
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = i * 16 + lg * 4 + r;
-          if (m < rows) {
-            uint16_t* hr = reinterpret_cast<uint16_t*>(h + (size_t)(row0 + m) * f);
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const float v = silu_mul(acc[i][half][r], acc[i][half + 2][r]);
-              const uint16_t hi = f32_to_bf16(v);
-              const uint16_t lo = f32_to_bf16(v - __uint_as_float((uint32_t)hi << 16));
-              const int col = nt * 128 + wv * 32 + half * 16 + ln;
-              hr[(col >> 3) * 16 + (col & 7)] = hi;
-              hr[(col >> 3) * 16 + 8 + (col & 7)] = lo;
-            }
-          }
-        }
-    }
-  }
-}
-
-// --------------------------------------------------- down, producer/consumer
-// y = H W_down^T with H given as split bf16 pairs (blocks of 8 features:
-// 8 hi, then 8 lo), the layout the producer/consumer gate/up writes.  Same
-// roles, ring and barriers as gateup_pc; the A operand of a stage is BM rows
-// x 128 features x (hi, lo) = 32 sixteen-byte units per row, unit u of row r
-// stored at position u ^ (r & 15).  Local weight row r (0..255) is output
-// nt*256 + r, fragment (r / 16) % 4 of consumer r / 64.  Every step issues
-// the hi product, then the lo product.
-template <int MF>
-__global__ __launch_bounds__(kPcThreads) void down_pc(
-    const float* __restrict__ h, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
-    const int32_t* __restrict__ offsets, float* __restrict__ y, int d, int f, int E) {
-  constexpr int BM = 16 * MF;
-  constexpr int A_BYTES = BM * 512;
-  constexpr int B_BYTES = 256 * 64;
-  constexpr int S_BYTES = 256 * 4;
-  constexpr int SLOT = A_BYTES + B_BYTES + S_BYTES;
-  constexpr int NA = BM * 32 / 4 / 64;   // A copies per producer wave per stage
-  constexpr int NCOPY = NA + 5;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * SLOT];
-  __shared__ int s_mt[kMaxE + 1];
-  __shared__ int s_wave[kPcThreads / 64];
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int ln = lane & 15, lg = lane >> 4;
-  const bool producer = wv >= 4;
-  const int pw = wv - 4;
-  build_mtiles_n<kPcThreads>(offsets, E, BM, s_mt, s_wave);
-  const int NT = d / 256;
-  const ItemRange ir = item_range((long)s_mt[E] * NT);
-  const int nst = f / kBK;
-  const size_t w_row = (size_t)f / 2, s_row = (size_t)f / 32;
-  const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
-  const size_t h_row = (size_t)f * 4;    // bytes per split row
-
-  for (long it = ir.first; it < ir.end; it += ir.step) {
-    const int mt = (int)(it / NT), nt = (int)(it - (long)mt * NT);
-    const int e = mtile_expert(s_mt, E, mt);
-    const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
-    const int rows = min(BM, offsets[e + 1] - row0);
-
-    const uint8_t* ap[NA];
-    const uint8_t* bp[4];
-    const uint8_t* spp = nullptr;
-    if (producer) {
-      const uint8_t* wbase = w2 + (size_t)e * d * w_row;
-      const uint8_t* sbase = w2s + (size_t)e * d * s_row;
+  // Every role walks the same items and executes 1 + nst barriers per item
+  // (one after the prologue, one per stage).
+  if (a_copier) {
+    for (long it = ir.first; it < ir.end; it += ir.step) {
+      const int mt = (int)(it / NT);
+      const int e = mtile_expert(s_mt, E, mt);
+      const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
+      const int rows = min(BM, offsets[e + 1] - row0);
+      const uint8_t* ap[NA];
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
-        const int unit = pw * (BM * 8) + q * 64 + lane;   // BM*32 units over 4 waves
-        const int r = unit >> 5;
-        const int u = (unit & 31) ^ (r & 15);
-        ap[q] = hb + (size_t)(row0 + min(r, rows - 1)) * h_row + u * 16;
+        const int unit = pa * (BM * AU / 2) + q * 64 + lane;
+        const int r = unit / AU;
+        const int u = (unit % AU) ^ (r & 15);
+        const int rr = min(r, rows - 1);
+        const size_t src_row = DOWN ? (size_t)(row0 + rr) : (size_t)(sorted_pair[row0 + rr] / k);
+        ap[q] = a_src + src_row * a_row + u * 16;
       }
+      auto issue_a = [&](int st, int slot) {
+        uint8_t* base = sA + slot * A_SLOT + pa * (BM * AU / 2) * 16;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = (pw * 256 + q * 64 + lane) >> 2;
-        const int b = (lane & 3) ^ ((r >> 2) & 3);
-        bp[q] = wbase + (size_t)(nt * 256 + r) * w_row + b * 16;
-      }
-      spp = sbase + (size_t)(nt * 256 + pw * 64 + lane) * s_row;
-    }
-    auto issue = [&](int st, int slot) {
-      uint8_t* base = ring + slot * SLOT;
+        for (int q = 0; q < NA; ++q) dma16_to_lds(ap[q] + (size_t)st * (AU * 16), base + q * 1024);
+      };
 #pragma unroll
-      for (int q = 0; q < NA; ++q)
-        dma16_to_lds(ap[q] + (size_t)st * 512, base + (pw * BM * 8 + q * 64) * 16);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dma16_to_lds(bp[q] + st * (kBK / 2), base + A_BYTES + (pw * 256 + q * 64) * 16);
-      dma4_to_lds(spp + st * 4, base + A_BYTES + B_BYTES + pw * 256);
-    };
-
-    f32x4_t acc[MF][4];
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf) acc[i][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    if (producer) {
-      issue(0, 0);
-      if (nst > 1) {
-        issue(1, 1);
-        wait_vmem<NCOPY>();
-      } else {
-        wait_vmem<0>();
-      }
-    }
-    wg_barrier();
+      for (int q = 0; q < RA - 1; ++q) issue_a(min(q, nst - 1), q);
+      wait_vmem<(RA - 2) * NA>();
+      wg_barrier();
 #pragma unroll 1
-    for (int s = 0; s < nst; ++s) {
-      const int slot = s % kRing;
-      if (producer) {
-        if (s + 2 < nst) {
-          issue(s + 2, (s + 2) % kRing);
-          wait_vmem<NCOPY>();
-        } else {
-          wait_vmem<0>();
-        }
-      } else {
-        const uint8_t* base = ring + slot * SLOT;
+      for (int s = 0; s < nst; ++s) {
+        issue_a(min(s + RA - 1, nst - 1), (s + RA - 1) % RA);
+        wait_vmem<(RA - 2) * NA>();
+        wg_barrier();
+      }
+      // copies past the last stage land before the next item refills the ring
+      wait_vmem<0>();
+    }
+  } else if (b_copier) {
+    for (long it = ir.first; it < ir.end; it += ir.step) {
+      const int mt = (int)(it / NT), nt = (int)(it - (long)mt * NT);
+      const int e = mtile_expert(s_mt, E, mt);
+      auto grow = [&](int r) -> size_t {
+        if (DOWN) return (size_t)nt * 256 + r;
+        const int cw = r >> 6, nf = (r >> 4) & 3;
+        return (size_t)((nf >= 2 ? f : 0) + nt * 128 + cw * 32 + (nf & 1) * 16 + (r & 15));
+      };
+      const uint8_t* wbase = wq + (size_t)e * e_rows * w_row;
+      const uint8_t* sbase = wsc + (size_t)e * e_rows * s_row;
+      const uint8_t* bp[8];
+      const uint8_t* sp[2];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = (pb * 512 + q * 64 + lane) >> 2;
+        const int b = (lane & 3) ^ ((r >> 2) & 3);
+        bp[q] = wbase + grow(r) * w_row + b * 16;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) sp[q] = sbase + grow(pb * 128 + q * 64 + lane) * s_row;
+      auto issue_b = [&](int st, int slot) {
+        uint8_t* base = sB + slot * B_SLOT;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          dma16_to_lds(bp[q] + st * (kBK / 2), base + (pb * 512 + q * 64) * 16);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          dma4_to_lds(sp[q] + st * 4, base + B_CODES + (pb * 128 + q * 64) * 4);
+      };
+#pragma unroll
+      for (int q = 0; q < RB - 1; ++q) issue_b(min(q, nst - 1), q);
+      wait_vmem<(RB - 2) * NB>();
+      wg_barrier();
+#pragma unroll 1
+      for (int s = 0; s < nst; ++s) {
+        issue_b(min(s + RB - 1, nst - 1), (s + RB - 1) % RB);
+        wait_vmem<(RB - 2) * NB>();
+        wg_barrier();
+      }
+      wait_vmem<0>();
+    }
+  } else {
+    for (long it = ir.first; it < ir.end; it += ir.step) {
+      const int mt = (int)(it / NT), nt = (int)(it - (long)mt * NT);
+      const int e = mtile_expert(s_mt, E, mt);
+      const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
+      const int rows = min(BM, offsets[e + 1] - row0);
+      f32x4_t acc[MF][4];
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) acc[i][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      wg_barrier();
+#pragma unroll 1
+      for (int s = 0; s < nst; ++s) {
+        const uint8_t* abase = sA + (s % RA) * A_SLOT;
+        const uint8_t* bbase = sB + (s % RB) * B_SLOT;
         float sc[4];
         uint4 bq[4];
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) {
           const int r = wv * 64 + nf * 16 + ln;
-          const uint32_t sw = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + r * 4);
+          const uint32_t sw = *reinterpret_cast<const uint32_t*>(bbase + B_CODES + r * 4);
           sc[nf] = e8m0_scale((sw >> (8 * lg)) & 0xFFu);
-          bq[nf] = *reinterpret_cast<const uint4*>(base + A_BYTES + r * 64 + ((lg ^ ((r >> 2) & 3)) * 16));
+          bq[nf] = *reinterpret_cast<const uint4*>(bbase + r * 64 + ((lg ^ ((r >> 2) & 3)) * 16));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -595,34 +482,51 @@ __global__ __launch_bounds__(kPcThreads) void down_pc(
             const uint32_t wj = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
             b[nf] = decode8(wj, sc[nf]);
           }
-          const int c = lg * 4 + j;   // 8-feature block of this step
+          const int c = lg * 4 + j;   // 8-element block of the stage this step reads
 #pragma unroll
           for (int i = 0; i < MF; ++i) {
-            const uint8_t* arow = base + (i * 16 + ln) * 512;
-            const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * c) ^ ln) * 16)));
-            const bf16x8_t al = as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * c + 1) ^ ln) * 16)));
+            const uint8_t* arow = abase + (i * 16 + ln) * (AU * 16);
+            if (DOWN) {
+              const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * c) ^ ln) * 16)));
+              const bf16x8_t al = as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * c + 1) ^ ln) * 16)));
 #pragma unroll
-            for (int nf = 0; nf < 4; ++nf) {
-              acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[nf], acc[i][nf], 0, 0, 0);
-              acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[nf], acc[i][nf], 0, 0, 0);
+              for (int nf = 0; nf < 4; ++nf) {
+                acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[nf], acc[i][nf], 0, 0, 0);
+                acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[nf], acc[i][nf], 0, 0, 0);
+              }
+            } else {
+              const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(arow + ((c ^ ln) * 16)));
+#pragma unroll
+              for (int nf = 0; nf < 4; ++nf)
+                acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nf], acc[i][nf], 0, 0, 0);
             }
           }
         }
         wait_lds();
+        wg_barrier();
       }
-      wg_barrier();
-    }
-
-    if (!producer) {
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = i * 16 + lg * 4 + r;
           if (m < rows) {
-            float* yr = y + (size_t)(row0 + m) * d + nt * 256 + wv * 64 + ln;
+            if (DOWN) {
+              float* yr = out + (size_t)(row0 + m) * d + nt * 256 + wv * 64 + ln;
 #pragma unroll
-            for (int nf = 0; nf < 4; ++nf) yr[nf * 16] = acc[i][nf][r];
+              for (int nf = 0; nf < 4; ++nf) yr[nf * 16] = acc[i][nf][r];
+            } else {
+              uint16_t* hr = reinterpret_cast<uint16_t*>(out + (size_t)(row0 + m) * f);
+#pragma unroll
+              for (int half = 0; half < 2; ++half) {
+                const float v = silu_mul(acc[i][half][r], acc[i][half + 2][r]);
+                const uint16_t hi = f32_to_bf16(v);
+                const uint16_t lo = f32_to_bf16(v - __uint_as_float((uint32_t)hi << 16));
+                const int col = nt * 128 + wv * 32 + half * 16 + ln;
+                hr[(col >> 3) * 16 + (col & 7)] = hi;
+                hr[(col >> 3) * 16 + 8 + (col & 7)] = lo;
+              }
+            }
           }
         }
     }
@@ -1076,31 +980,34 @@ hipError_t launch_gateup_mfma(const k3moe_shape& s, const k3moe_expert_bank& b, 
 hipError_t launch_gateup_pc(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
                             const int32_t* offsets, const int32_t* sorted_pair, float* h,
                             hipStream_t st) {
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
   const uint8_t* w = static_cast<const uint8_t*>(b.w13);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
   const dim3 g(mfma_grid() / 2), blk(kPcThreads);   // one 8-wave workgroup per CU
-#define K3_PC(MF) gateup_pc<MF><<<g, blk, 0, st>>>(xb, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k)
+#define K3_PC(MF, RA, RB) \
+  mx_gemm_pc<MF, RA, RB, false><<<g, blk, 0, st>>>(xb, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k)
   const int mf = pick_mf(s, 8);
-  if (mf <= 1) K3_PC(1);
-  else if (mf <= 2) K3_PC(2);
-  else if (mf <= 4) K3_PC(4);
-  else if (mf <= 6) K3_PC(6);
-  else K3_PC(8);
+  if (mf <= 1) K3_PC(1, 3, 7);
+  else if (mf <= 2) K3_PC(2, 3, 7);
+  else if (mf <= 4) K3_PC(4, 3, 6);
+  else if (mf <= 6) K3_PC(6, 3, 4);
+  else K3_PC(8, 2, 5);
 #undef K3_PC
   return hipGetLastError();
 }
 
 hipError_t launch_down_pc(const k3moe_shape& s, const k3moe_expert_bank& b, const float* h,
                           const int32_t* offsets, float* y, hipStream_t st) {
+  const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
   const uint8_t* w = static_cast<const uint8_t*>(b.w2);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w2_scale);
   const dim3 g(mfma_grid() / 2), blk(kPcThreads);
-#define K3_DPC(MF) down_pc<MF><<<g, blk, 0, st>>>(h, w, ws, offsets, y, s.d, s.f, s.E)
+#define K3_DPC(MF, RA, RB) \
+  mx_gemm_pc<MF, RA, RB, true><<<g, blk, 0, st>>>(hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k)
   const int mf = pick_mf(s, 4);
-  if (mf <= 1) K3_DPC(1);
-  else if (mf <= 2) K3_DPC(2);
-  else K3_DPC(4);
+  if (mf <= 1) K3_DPC(1, 3, 7);
+  else if (mf <= 2) K3_DPC(2, 3, 6);
+  else K3_DPC(4, 2, 5);
 #undef K3_DPC
   return hipGetLastError();
 }
