@@ -353,21 +353,40 @@ k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* we
   K3_CHECK(check_ws(workspace, workspace_bytes, need));
   const LayerWs L = carve_layer(s, workspace, nullptr);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // One token: the top-k kernel also writes the (trivial) permutation.
+  PermOut perm;
+  if (s.T == 1) {
+    perm.counts = L.counts;
+    perm.offsets = L.offsets;
+    perm.sorted_pair = L.sorted_pair;
+    perm.pair_pos = L.pair_pos;
+  }
   hipError_t e = launch_route(s, x, static_cast<const uint16_t*>(weights->w_router), L.topk_idx,
-                              L.topk_w, nullptr, diag, carve_route(s, L.scratch, nullptr), st);
+                              L.topk_w, nullptr, diag, carve_route(s, L.scratch, nullptr), st,
+                              perm);
   if (e != hipSuccess) return hip_status(e, "k3moe_layer route");
-  e = launch_permute(s, L.topk_idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, diag,
-                     carve_permute(s, L.scratch, nullptr), st);
-  if (e != hipSuccess) return hip_status(e, "k3moe_layer permute");
+  if (s.T != 1) {
+    e = launch_permute(s, L.topk_idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, diag,
+                       carve_permute(s, L.scratch, nullptr), st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer permute");
+  }
   e = launch_expert_ffn(s, weights->routed, x, L.offsets, L.sorted_pair, L.y_perm,
                         carve_expert(s, L.scratch, nullptr), st);
   if (e != hipSuccess) return hip_status(e, "k3moe_layer routed experts");
   if (s.n_shared > 0) {
+    // the shared experts' down kernel finishes each output with the combine
+    CombineArgs comb;
+    comb.y_perm = L.y_perm;
+    comb.pair_pos = L.pair_pos;
+    comb.topk_w = L.topk_w;
+    comb.out = out;
+    comb.k = s.k;
+    comb.out_bf16 = s.out_dtype == K3MOE_BF16;
     e = launch_shared_ffn(s, weights->shared, x, L.shared_y, carve_shared(s, L.scratch, nullptr),
-                          st);
-    if (e != hipSuccess) return hip_status(e, "k3moe_layer shared experts");
+                          st, comb);
+    return hip_status(e, "k3moe_layer shared experts + combine");
   }
-  e = launch_combine(s, L.y_perm, L.pair_pos, L.topk_w, L.shared_y, out, st);
+  e = launch_combine(s, L.y_perm, L.pair_pos, L.topk_w, nullptr, out, st);
   return hip_status(e, "k3moe_layer combine");
 }
 

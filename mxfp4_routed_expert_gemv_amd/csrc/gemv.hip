@@ -636,12 +636,82 @@ __global__ __launch_bounds__(256) void gemv_gateup_bf16(const uint16_t* __restri
   }
 }
 
+// One token, shared experts' down: each wave owns 2 output rows and, per lane,
+// the 16-byte chunks c = lane + 64 u (u < 4) of every shared expert's rows,
+// all loaded before any arithmetic.  Per (row, expert): fp32 fused
+// multiply-adds over the lane's chunks in order, the fixed transposed
+// butterfly over the wave, then the experts added in order.  Requires
+// f_shared == 2048 (4 chunks of 8 per lane) and at most 2 shared experts.
+constexpr int kSdRows = 2, kSdU = 4, kSdMaxS = 2;
+__global__ __launch_bounds__(256) void shared_down_t1(const uint16_t* __restrict__ w2,
+                                                      const float* __restrict__ hs,
+                                                      float* __restrict__ y, int d, int fs, int S,
+                                                      CombineArgs comb) {
+  constexpr int R = kSdRows, U = kSdU, MS = kSdMaxS;
+  const int lane = threadIdx.x & 63;
+  const int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  if (o0 >= d) return;
+  uint4 wv[MS][R][U];
+  uint4 ha[MS][U], hb[MS][U];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const int sc = min(s, S - 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = lane + kWave * u;
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        wv[s][i][u] = ldg16(w2 + ((size_t)sc * d + o0 + i) * fs + (size_t)c * 8);
+      ha[s][u] = ldg16(hs + (size_t)sc * fs + (size_t)c * 8);
+      hb[s][u] = ldg16(hs + (size_t)sc * fs + (size_t)c * 8 + 4);
+    }
+  }
+  float v[MS * R];
+#pragma unroll
+  for (int s = 0; s < MS; ++s)
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float a = 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t ww[4] = {wv[s][i][u].x, wv[s][i][u].y, wv[s][i][u].z, wv[s][i][u].w};
+        const float hh[8] = {__uint_as_float(ha[s][u].x), __uint_as_float(ha[s][u].y),
+                             __uint_as_float(ha[s][u].z), __uint_as_float(ha[s][u].w),
+                             __uint_as_float(hb[s][u].x), __uint_as_float(hb[s][u].y),
+                             __uint_as_float(hb[s][u].z), __uint_as_float(hb[s][u].w)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a = __builtin_fmaf(bf16_lo(ww[q]), hh[2 * q], a);
+          a = __builtin_fmaf(bf16_hi(ww[q]), hh[2 * q + 1], a);
+        }
+      }
+      v[s * R + i] = a;
+    }
+  XReduce<MS * R, 32>::run(v, lane);
+  // lane group g = lane >> 4 holds total (s = g / R, row i = g % R)
+  const int g = lane >> 4;
+  float tot = v[0];
+  // experts added in order: row i's total = t(s=0, i) + t(s=1, i)
+  const float other = __shfl(tot, (lane + 16 * R) & 63, kWave);
+  if ((lane & 15) == 0 && g < R) {
+    const float total = S > 1 ? tot + other : tot;
+    const int o = o0 + g;
+    if (comb.y_perm) {
+      const float r = combine_one(total, comb.y_perm, comb.pair_pos, comb.topk_w, 0, comb.k, d, o);
+      if (comb.out_bf16) static_cast<uint16_t*>(comb.out)[o] = f32_to_bf16(r);
+      else static_cast<float*>(comb.out)[o] = r;
+    } else {
+      y[o] = total;
+    }
+  }
+}
+
 // y[t][o] = sum over shared experts s in order of (sum_j W2[s][o][j] hs[t][s][j]).
 template <int R, int MT, int NU>
 __global__ __launch_bounds__(256) void gemv_down_bf16(const uint16_t* __restrict__ w2,
                                                       const float* __restrict__ hs,
                                                       float* __restrict__ y, int T, int d, int fs,
-                                                      int S, int rgroups) {
+                                                      int S, int rgroups, CombineArgs comb) {
   constexpr int NV = R * MT;
   const int lane = threadIdx.x & 63;
   const int rg = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -685,7 +755,17 @@ __global__ __launch_bounds__(256) void gemv_down_bf16(const uint16_t* __restrict
     }
     if ((lane & ((1 << SH) - 1)) == 0) {
       const int i = idx / MT, mt = idx - i * MT;
-      if (t0 + mt < T) y[(size_t)(t0 + mt) * d + o0 + i] = tot;
+      if (t0 + mt < T) {
+        const size_t oi = (size_t)(t0 + mt) * d + o0 + i;
+        if (comb.y_perm) {
+          const float v = combine_one(tot, comb.y_perm, comb.pair_pos, comb.topk_w, t0 + mt,
+                                      comb.k, d, o0 + i);
+          if (comb.out_bf16) static_cast<uint16_t*>(comb.out)[oi] = f32_to_bf16(v);
+          else static_cast<float*>(comb.out)[oi] = v;
+        } else {
+          y[oi] = tot;
+        }
+      }
     }
   }
 }
@@ -788,8 +868,9 @@ hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank
 }
 
 hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
-                             float* y, const SharedWs& ws, hipStream_t st) {
-  if (shared_mfma_ok(s)) return launch_shared_mfma(s, bank, x, ws.h, y, st);
+                             float* y, const SharedWs& ws, hipStream_t st,
+                             const CombineArgs& comb) {
+  if (shared_mfma_ok(s)) return launch_shared_mfma(s, bank, x, ws.h, y, st, comb);
   constexpr int RG = 2, RD = 4;
   const int S = bank.n_experts, fs = bank.f, T = (int)s.T;
   const uint16_t* w13 = static_cast<const uint16_t*>(bank.w13);
@@ -810,11 +891,15 @@ hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (T == 1 && fs == kSdU * 8 * kWave && S <= kSdMaxS && s.d % (4 * kSdRows) == 0) {
+    shared_down_t1<<<s.d / (4 * kSdRows), 256, 0, st>>>(w2, ws.h, y, s.d, fs, S, comb);
+    return hipGetLastError();
+  }
   const unsigned g2 = blocks_for_waves(rg_dn);
   if (T == 1)
-    gemv_down_bf16<RD, 1, 2><<<g2, 256, 0, st>>>(w2, ws.h, y, T, s.d, fs, S, rg_dn);
+    gemv_down_bf16<RD, 1, 2><<<g2, 256, 0, st>>>(w2, ws.h, y, T, s.d, fs, S, rg_dn, comb);
   else
-    gemv_down_bf16<RD, 2, 2><<<g2, 256, 0, st>>>(w2, ws.h, y, T, s.d, fs, S, rg_dn);
+    gemv_down_bf16<RD, 2, 2><<<g2, 256, 0, st>>>(w2, ws.h, y, T, s.d, fs, S, rg_dn, comb);
   return hipGetLastError();
 }
 

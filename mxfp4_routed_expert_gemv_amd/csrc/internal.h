@@ -66,10 +66,32 @@ ExpertWs carve_expert(const k3moe_shape& s, void* ws, size_t* bytes);
 SharedWs carve_shared(const k3moe_shape& s, void* ws, size_t* bytes);
 LayerWs carve_layer(const k3moe_shape& s, void* ws, size_t* bytes);
 
+// Outputs of k3moe_permute, written by the top-k kernel itself when the
+// batch is one token (its ids, already in ascending order, are the sorted
+// order); counts == nullptr means "not requested".
+struct PermOut {
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* sorted_pair = nullptr;
+  int32_t* pair_pos = nullptr;
+};
+// The combine folded into the shared experts' down kernel: its fp32 result
+// for (t, o) takes the place of shared_y[t][o] and the routed terms follow in
+// the same order as in the combine kernel (same bits).  y_perm == nullptr
+// means "not requested".
+struct CombineArgs {
+  const float* y_perm = nullptr;
+  const int32_t* pair_pos = nullptr;
+  const float* topk_w = nullptr;
+  void* out = nullptr;
+  int k = 0;
+  bool out_bf16 = false;
+};
+
 // Launchers: enqueue on `st`, return hipSuccess or the launch error.
 hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, int32_t* idx,
                         float* w, float* logits_out, int32_t* diag, const RouteWs& ws,
-                        hipStream_t st);
+                        hipStream_t st, const PermOut& perm = PermOut());
 hipError_t launch_permute(const k3moe_shape& s, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                           int32_t* diag, const PermuteWs& ws, hipStream_t st);
@@ -90,12 +112,13 @@ hipError_t launch_down_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank,
                             const int32_t* offsets, float* y, hipStream_t st);
 bool shared_mfma_ok(const k3moe_shape& s);
 hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
-                              float* h, float* y, hipStream_t st);
+                              float* h, float* y, hipStream_t st, const CombineArgs& comb);
 hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                              const int32_t* offsets, const int32_t* sorted_pair, float* y,
                              const ExpertWs& ws, hipStream_t st);
 hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
-                             float* y, const SharedWs& ws, hipStream_t st);
+                             float* y, const SharedWs& ws, hipStream_t st,
+                             const CombineArgs& comb = CombineArgs());
 hipError_t launch_combine(const k3moe_shape& s, const float* y_perm, const int32_t* pair_pos,
                           const float* topk_w, const float* shared_y, void* out, hipStream_t st);
 

@@ -155,6 +155,35 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return (g / (1.0f + expf(-g))) * u;
 }
 
+// One output of the fixed-order combine: starting from the shared experts'
+// fp32 value, the routed slots of token t in slot order (ascending expert
+// id), skipping zero weights and dropped pairs.  The combine kernel and the
+// fused shared-expert epilogues both call this, so they agree bit for bit.
+__device__ __forceinline__ float combine_one(float acc, const float* __restrict__ y_perm,
+                                             const int32_t* __restrict__ pair_pos,
+                                             const float* __restrict__ topk_w, int64_t t, int k,
+                                             int d, int o) {
+  // groups of 8 slots: every load of a group is issued before its first
+  // multiply-add (dropped pairs read row 0 and are skipped)
+  constexpr int G = 8;
+  for (int s0 = 0; s0 < k; s0 += G) {
+    float w[G], v[G];
+    int pp[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int s = min(s0 + u, k - 1);
+      w[u] = topk_w[t * k + s];
+      pp[u] = pair_pos[t * k + s];
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) v[u] = y_perm[(size_t)(pp[u] >= 0 ? pp[u] : 0) * d + o];
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (s0 + u < k && w[u] != 0.0f && pp[u] >= 0) acc = __builtin_fmaf(w[u], v[u], acc);
+  }
+  return acc;
+}
+
 __device__ __forceinline__ uint4 ldg16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

@@ -791,7 +791,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 template <int MF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void down_shared_mfma(
     const float* __restrict__ h, const uint16_t* __restrict__ w2, float* __restrict__ y, int T,
-    int d, int fs, int S) {
+    int d, int fs, int S, CombineArgs comb) {
   constexpr int BM = 16 * MF;
   constexpr int PER = BM / 16;    // 16-byte h chunks per thread per stage (16 per row)
   __shared__ __attribute__((aligned(16))) uint8_t sH[2][BM * kLdsRowS];
@@ -900,9 +900,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int r = 0; r < 4; ++r) {
         const int m = i * 16 + lg * 4 + r;
         if (m < rows) {
-          float* yr = y + (size_t)(row0 + m) * d + nt * 256 + wv * 64 + ln;
+          const int t = row0 + m;
+          const int o = nt * 256 + wv * 64 + ln;
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf) yr[nf * 16] = acc[i][nf][r];
+          for (int nf = 0; nf < 4; ++nf) {
+            const size_t oi = (size_t)t * d + o + nf * 16;
+            if (comb.y_perm) {
+              const float v = combine_one(acc[i][nf][r], comb.y_perm, comb.pair_pos, comb.topk_w,
+                                          t, comb.k, d, o + nf * 16);
+              if (comb.out_bf16) static_cast<uint16_t*>(comb.out)[oi] = f32_to_bf16(v);
+              else static_cast<float*>(comb.out)[oi] = v;
+            } else {
+              y[oi] = acc[i][nf][r];
+            }
+          }
         }
       }
   }
@@ -938,7 +949,7 @@ bool shared_mfma_ok(const k3moe_shape& s) {
 }
 
 hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
-                              float* h, float* y, hipStream_t st) {
+                              float* h, float* y, hipStream_t st, const CombineArgs& comb) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* w13 = static_cast<const uint16_t*>(b.w13);
   const uint16_t* w2 = static_cast<const uint16_t*>(b.w2);
@@ -949,8 +960,8 @@ hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& b, 
   else gateup_shared_mfma<2><<<g, blk, 0, st>>>(xb, w13, h, T, s.d, fs, S);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (T >= 128) down_shared_mfma<4><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S);
-  else down_shared_mfma<2><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S);
+  if (T >= 128) down_shared_mfma<4><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
+  else down_shared_mfma<2><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
   return hipGetLastError();
 }
 

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
                                                    float* __restrict__ w_out,
                                                    float* __restrict__ logits_out,
                                                    int32_t* __restrict__ diag, int T, int d, int E,
-                                                   int k) {
+                                                   int k, PermOut perm) {
   __shared__ double candL[1024];
   __shared__ int candId[1024];
   __shared__ int candTaken[1024];
@@ -289,7 +289,8 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
     const bool ok = j < nj && e < E;
     if (ok && !isfinite(lv[j])) ++nonfin;
     key[j] = ok ? order_key(isnan(lv[j]) ? -INFINITY : lv[j]) : 0;
-    b[j] = ok ? b[j] : 0.0f;
+    // masked with bit operations so the loads above stay unconditional
+    b[j] = __uint_as_float(__float_as_uint(b[j]) & (0u - (uint32_t)ok));
   }
   if (logits_out)
 #pragma unroll
@@ -380,28 +381,48 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
     if (lane == 0 && diag) atomicAdd(&diag[K3MOE_DIAG_RECHECKED_TOKENS], 1);
   }
 
-  // Softmax over the chosen logits; outputs in ascending expert id.
+  // Softmax over the chosen logits; outputs in ascending expert id.  The
+  // chosen (id, logit) pairs are first compacted in ascending id into
+  // chosen[] / candL[] (slot p = rank among the chosen), so each slot's
+  // exponential is evaluated once, by lane p.
   uint64_t kmax = 0;
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j)
     if (((taken >> j) & 1u) && key[j] > kmax) kmax = key[j];
   const double m = key_value(wave_max_u64(kmax));
-  double zl = 0.0;
-#pragma unroll
-  for (int j = 0; j < kMaxJ; ++j)
-    if ((taken >> j) & 1u) zl += exp(key_value(key[j]) - m);
-  const double z = wave_sum(zl);
   int base = 0;
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) {
     const bool mine = (taken >> j) & 1u;   // never set for j >= nj
     const unsigned long long bal = __ballot(mine);
+    const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
     if (mine) {
-      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-      idx_out[(size_t)t * k + pos] = lane + kWave * j;
-      w_out[(size_t)t * k + pos] = (float)(exp(key_value(key[j]) - m) / z);
+      chosen[pos] = lane + kWave * j;
+      candL[pos] = key_value(key[j]);
+    }
+    // one token: expert e = lane + 64 j has count 0/1 and offset = the
+    // number of chosen experts below it (ids run j-major, then lane)
+    const int e = lane + kWave * j;
+    if (perm.counts && j < nj && e < E) {
+      perm.counts[e] = mine ? 1 : 0;
+      perm.offsets[e] = pos;
     }
     base += __popcll(bal);
+  }
+  if (perm.counts) {
+    if (lane == 0) perm.offsets[E] = base;
+    if (lane < k) {
+      perm.sorted_pair[lane] = lane;
+      perm.pair_pos[lane] = lane;
+    }
+  }
+  __syncthreads();
+  // k <= 64: one slot per lane; z summed by the fixed butterfly
+  const double ep = lane < k ? exp(candL[lane] - m) : 0.0;
+  const double z = wave_sum(ep);
+  if (lane < k) {
+    idx_out[(size_t)t * k + lane] = chosen[lane];
+    w_out[(size_t)t * k + lane] = (float)(ep / z);
   }
 }
 
@@ -409,7 +430,8 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
 
 hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, int32_t* idx,
                         float* w, float* logits_out, int32_t* diag, const RouteWs& ws,
-                        hipStream_t st) {
+                        hipStream_t st, const PermOut& perm) {
+  if (perm.counts && s.T != 1) return hipErrorInvalidValue;
   const int T = (int)s.T;
   const bool xf32 = s.x_dtype == K3MOE_F32;
   const dim3 g1((s.E + 3) / 4);
@@ -424,10 +446,10 @@ hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr,
   if (err != hipSuccess) return err;
   if (xf32)
     topk_softmax<true><<<T, 64, 0, st>>>(ws.logits, ws.lbound, x, wr, idx, w, logits_out, diag,
-                                         T, s.d, s.E, s.k);
+                                         T, s.d, s.E, s.k, perm);
   else
     topk_softmax<false><<<T, 64, 0, st>>>(ws.logits, ws.lbound, x, wr, idx, w, logits_out, diag,
-                                          T, s.d, s.E, s.k);
+                                          T, s.d, s.E, s.k, perm);
   return hipGetLastError();
 }
 
