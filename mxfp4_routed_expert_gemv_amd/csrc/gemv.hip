@@ -636,6 +636,52 @@ __global__ __launch_bounds__(256) void gemv_gateup_bf16(const uint16_t* __restri
   }
 }
 
+// One token, shared experts' gate/up: each wave owns one feature j of one
+// shared expert (its gate row and up row) and, per lane, the chunks
+// c = lane + 64 u (u < 14, 8 bf16 each) of both rows, all loaded before any
+// arithmetic; x is staged in LDS once per workgroup.  Per row: dot2 steps
+// over the lane's chunks in order, then the fixed transposed butterfly.
+// Requires d == 7168 (14 chunks per lane) and bf16 x.
+constexpr int kSgU = 14;
+__global__ __launch_bounds__(256) void shared_gateup_t1(const uint16_t* __restrict__ w13,
+                                                        const uint16_t* __restrict__ x,
+                                                        float* __restrict__ hs, int d, int fs,
+                                                        int S) {
+  __shared__ uint4 xs[kSgU * kWave];
+  stage_row(reinterpret_cast<const uint4*>(x), d / 8, xs);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);   // (expert, feature)
+  if (item >= S * fs) return;
+  const int se = item / fs, j = item - se * fs;
+  const uint16_t* gr = w13 + ((size_t)se * 2 * fs + j) * d;
+  const uint16_t* ur = gr + (size_t)fs * d;
+  uint4 g[kSgU], u[kSgU];
+#pragma unroll
+  for (int q = 0; q < kSgU; ++q) {
+    const int c = lane + kWave * q;
+    g[q] = ldg16(gr + (size_t)c * 8);
+    u[q] = ldg16(ur + (size_t)c * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load above is issued before any arithmetic
+  float v[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < kSgU; ++q) {
+    const uint4 xa = xs[lane + kWave * q];
+    v[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(g[q].x), as_bf16x2(xa.x), v[0], false);
+    v[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(g[q].y), as_bf16x2(xa.y), v[0], false);
+    v[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(g[q].z), as_bf16x2(xa.z), v[0], false);
+    v[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(g[q].w), as_bf16x2(xa.w), v[0], false);
+    v[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(u[q].x), as_bf16x2(xa.x), v[1], false);
+    v[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(u[q].y), as_bf16x2(xa.y), v[1], false);
+    v[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(u[q].z), as_bf16x2(xa.z), v[1], false);
+    v[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(u[q].w), as_bf16x2(xa.w), v[1], false);
+  }
+  XReduce<2, 32>::run(v, lane);
+  const float uval = __shfl_xor(v[0], 32, kWave);
+  if (lane == 0) hs[(size_t)se * fs + j] = silu_mul(v[0], uval);
+}
+
 // One token, shared experts' down: each wave owns 2 output rows and, per lane,
 // the 16-byte chunks c = lane + 64 u (u < 4) of every shared expert's rows,
 // all loaded before any arithmetic.  Per (row, expert): fp32 fused
@@ -878,7 +924,10 @@ hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank
   const int rg_gu = fs / RG, rg_dn = s.d / RD;
   const unsigned g1 = blocks_for_waves((int64_t)S * rg_gu);
   const bool xf32 = s.x_dtype == K3MOE_F32;
-  if (T == 1) {
+  if (T == 1 && !xf32 && s.d == kSgU * 8 * kWave) {
+    shared_gateup_t1<<<(S * fs + 3) / 4, 256, 0, st>>>(w13, static_cast<const uint16_t*>(x), ws.h,
+                                                      s.d, fs, S);
+  } else if (T == 1) {
     if (xf32)
       gemv_gateup_bf16<RG, 1, 4, true><<<g1, 256, 0, st>>>(w13, x, ws.h, T, s.d, fs, S, rg_gu);
     else
