@@ -164,15 +164,20 @@ LayerWs carve_layer(const k3moe_shape& s, void* ws, size_t* bytes) {
   r.pair_pos = c.take<int32_t>(P);
   r.y_perm = c.take<float>(P * s.d);
   r.shared_y = s.n_shared > 0 ? c.take<float>((size_t)s.T * s.d) : nullptr;
-  size_t a = 0, b = 0, e = 0, sh = 0;
+  r.shared_h = s.n_shared > 0 ? carve_shared(s, c.base ? c.base + c.off : nullptr, nullptr).h
+                              : nullptr;
+  if (s.n_shared > 0) {
+    size_t sh = 0;
+    carve_shared(s, nullptr, &sh);
+    c.off += sh;
+  }
+  size_t a = 0, b = 0, e = 0;
   carve_route(s, nullptr, &a);
   carve_permute(s, nullptr, &b);
   carve_expert(s, nullptr, &e);
-  carve_shared(s, nullptr, &sh);
   size_t m = a;
   if (b > m) m = b;
   if (e > m) m = e;
-  if (sh > m) m = sh;
   r.scratch_bytes = m;
   r.scratch = c.take<char>(m);
   if (bytes) *bytes = c.off;
@@ -353,6 +358,37 @@ k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* we
   K3_CHECK(check_ws(workspace, workspace_bytes, need));
   const LayerWs L = carve_layer(s, workspace, nullptr);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (topk_shared_t1_ok(s) && shared_down_t1_ok(s)) {
+    // One token: router logits; then the selection (which also writes the
+    // permutation) beside the shared experts' gate/up; the routed experts;
+    // the shared experts' down finishing each output with the combine.
+    const RouteWs rws = carve_route(s, L.scratch, nullptr);
+    PermOut perm;
+    perm.counts = L.counts;
+    perm.offsets = L.offsets;
+    perm.sorted_pair = L.sorted_pair;
+    perm.pair_pos = L.pair_pos;
+    SharedWs sws;
+    sws.h = L.shared_h;
+    hipError_t e = launch_router_logits(s, x, static_cast<const uint16_t*>(weights->w_router),
+                                        rws, st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer router");
+    e = launch_topk_shared_t1(s, x, static_cast<const uint16_t*>(weights->w_router), L.topk_idx,
+                              L.topk_w, diag, rws, perm, weights->shared, sws.h, st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer top-k + shared gate/up");
+    e = launch_expert_ffn(s, weights->routed, x, L.offsets, L.sorted_pair, L.y_perm,
+                          carve_expert(s, L.scratch, nullptr), st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer routed experts");
+    CombineArgs comb;
+    comb.y_perm = L.y_perm;
+    comb.pair_pos = L.pair_pos;
+    comb.topk_w = L.topk_w;
+    comb.out = out;
+    comb.k = s.k;
+    comb.out_bf16 = s.out_dtype == K3MOE_BF16;
+    e = launch_shared_down_t1(s, weights->shared, sws, L.shared_y, st, comb);
+    return hip_status(e, "k3moe_layer shared down + combine");
+  }
   // One token: the top-k kernel also writes the (trivial) permutation.
   PermOut perm;
   if (s.T == 1) {
@@ -382,8 +418,9 @@ k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* we
     comb.out = out;
     comb.k = s.k;
     comb.out_bf16 = s.out_dtype == K3MOE_BF16;
-    e = launch_shared_ffn(s, weights->shared, x, L.shared_y, carve_shared(s, L.scratch, nullptr),
-                          st, comb);
+    SharedWs sws;
+    sws.h = L.shared_h;
+    e = launch_shared_ffn(s, weights->shared, x, L.shared_y, sws, st, comb);
     return hip_status(e, "k3moe_layer shared experts + combine");
   }
   e = launch_combine(s, L.y_perm, L.pair_pos, L.topk_w, nullptr, out, st);

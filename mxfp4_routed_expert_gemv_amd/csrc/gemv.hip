@@ -19,6 +19,7 @@
 // in registers.
 #include "internal.h"
 #include "kern_common.h"
+#include "decode_t1.h"
 
 namespace k3 {
 namespace {
@@ -117,16 +118,6 @@ __device__ __forceinline__ void stage_meta(const int32_t* __restrict__ offsets,
 }
 
 // Copy n16 16-byte words of one activation row into LDS (256 threads).
-__device__ __forceinline__ void stage_row(const uint4* __restrict__ src, int n16, uint4* dst) {
-  constexpr int U = 8;  // up to 2048 words (32 KB)
-  uint4 t[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) t[u] = src[min((int)threadIdx.x + 256 * u, n16 - 1)];
-  // Out-of-range threads rewrite the last word with its own value: stores
-  // stay unconditional, so the loads above are all issued before any wait.
-#pragma unroll
-  for (int u = 0; u < U; ++u) dst[min((int)threadIdx.x + 256 * u, n16 - 1)] = t[u];
-}
 
 // Persistent walk over work items: item it goes to wave it mod (#waves).
 // Overlap of one wave's loads with another's decode comes from occupancy
@@ -636,13 +627,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_bf16(const uint16_t* __restri
   }
 }
 
-// One token, shared experts' gate/up: each wave owns one feature j of one
-// shared expert (its gate row and up row) and, per lane, the chunks
-// c = lane + 64 u (u < 14, 8 bf16 each) of both rows, all loaded before any
-// arithmetic; x is staged in LDS once per workgroup.  Per row: dot2 steps
-// over the lane's chunks in order, then the fixed transposed butterfly.
-// Requires d == 7168 (14 chunks per lane) and bf16 x.
-constexpr int kSgU = 14;
+// One token, shared experts' gate/up: one (expert, feature) item per wave.
 __global__ __launch_bounds__(256) void shared_gateup_t1(const uint16_t* __restrict__ w13,
                                                         const uint16_t* __restrict__ x,
                                                         float* __restrict__ hs, int d, int fs,
@@ -650,36 +635,8 @@ __global__ __launch_bounds__(256) void shared_gateup_t1(const uint16_t* __restri
   __shared__ uint4 xs[kSgU * kWave];
   stage_row(reinterpret_cast<const uint4*>(x), d / 8, xs);
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);   // (expert, feature)
-  if (item >= S * fs) return;
-  const int se = item / fs, j = item - se * fs;
-  const uint16_t* gr = w13 + ((size_t)se * 2 * fs + j) * d;
-  const uint16_t* ur = gr + (size_t)fs * d;
-  uint4 g[kSgU], u[kSgU];
-#pragma unroll
-  for (int q = 0; q < kSgU; ++q) {
-    const int c = lane + kWave * q;
-    g[q] = ldg16(gr + (size_t)c * 8);
-    u[q] = ldg16(ur + (size_t)c * 8);
-  }
-  __builtin_amdgcn_sched_barrier(0);   // every load above is issued before any arithmetic
-  float v[2] = {0.0f, 0.0f};
-#pragma unroll
-  for (int q = 0; q < kSgU; ++q) {
-    const uint4 xa = xs[lane + kWave * q];
-    v[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(g[q].x), as_bf16x2(xa.x), v[0], false);
-    v[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(g[q].y), as_bf16x2(xa.y), v[0], false);
-    v[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(g[q].z), as_bf16x2(xa.z), v[0], false);
-    v[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(g[q].w), as_bf16x2(xa.w), v[0], false);
-    v[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(u[q].x), as_bf16x2(xa.x), v[1], false);
-    v[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(u[q].y), as_bf16x2(xa.y), v[1], false);
-    v[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(u[q].z), as_bf16x2(xa.z), v[1], false);
-    v[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(u[q].w), as_bf16x2(xa.w), v[1], false);
-  }
-  XReduce<2, 32>::run(v, lane);
-  const float uval = __shfl_xor(v[0], 32, kWave);
-  if (lane == 0) hs[(size_t)se * fs + j] = silu_mul(v[0], uval);
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item < S * fs) shared_gateup_item(item, w13, xs, hs, d, fs, threadIdx.x & 63);
 }
 
 // One token, shared experts' down: each wave owns 2 output rows and, per lane,
@@ -911,6 +868,22 @@ hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank
   hipError_t err = launch_expert_gateup(s, bank, x, offsets, sorted_pair, ws.h, st);
   if (err != hipSuccess) return err;
   return launch_expert_down(s, bank, ws.h, offsets, y, st);
+}
+
+hipError_t launch_shared_down_t1(const k3moe_shape& s, const k3moe_expert_bank& bank,
+                                 const SharedWs& ws, float* y, hipStream_t st,
+                                 const CombineArgs& comb) {
+  const int S = bank.n_experts, fs = bank.f;
+  if (s.T != 1 || fs != kSdU * 8 * kWave || S > kSdMaxS || s.d % (4 * kSdRows) != 0)
+    return hipErrorInvalidValue;
+  shared_down_t1<<<s.d / (4 * kSdRows), 256, 0, st>>>(static_cast<const uint16_t*>(bank.w2), ws.h,
+                                                      y, s.d, fs, S, comb);
+  return hipGetLastError();
+}
+
+bool shared_down_t1_ok(const k3moe_shape& s) {
+  return s.T == 1 && s.f_shared == kSdU * 8 * kWave && s.n_shared <= kSdMaxS &&
+         s.d % (4 * kSdRows) == 0;
 }
 
 hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,

@@ -56,7 +56,8 @@ struct LayerWs {
   int32_t* pair_pos;
   float* y_perm;
   float* shared_y;
-  void* scratch;      // shared by the stage workspaces (stages run in order)
+  float* shared_h;    // [T][n_shared][f_shared], live from the shared gate/up to its down
+  void* scratch;      // route, permute and routed-expert workspaces (stages run in order)
   size_t scratch_bytes;
 };
 
@@ -92,6 +93,19 @@ struct CombineArgs {
 hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, int32_t* idx,
                         float* w, float* logits_out, int32_t* diag, const RouteWs& ws,
                         hipStream_t st, const PermOut& perm = PermOut());
+// The two halves of launch_route, and the one-token selection fused with the
+// shared experts' gate/up (which writes SharedWs::h).
+hipError_t launch_router_logits(const k3moe_shape& s, const void* x, const uint16_t* wr,
+                                const RouteWs& ws, hipStream_t st);
+bool topk_shared_t1_ok(const k3moe_shape& s);
+hipError_t launch_topk_shared_t1(const k3moe_shape& s, const void* x, const uint16_t* wr,
+                                 int32_t* idx, float* w, int32_t* diag, const RouteWs& ws,
+                                 const PermOut& perm, const k3moe_expert_bank& shared, float* hs,
+                                 hipStream_t st);
+bool shared_down_t1_ok(const k3moe_shape& s);
+hipError_t launch_shared_down_t1(const k3moe_shape& s, const k3moe_expert_bank& bank,
+                                 const SharedWs& ws, float* y, hipStream_t st,
+                                 const CombineArgs& comb);
 hipError_t launch_permute(const k3moe_shape& s, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                           int32_t* diag, const PermuteWs& ws, hipStream_t st);

@@ -188,4 +188,19 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Copies n16 16-byte words (at most 2048) into LDS with a 256-thread
+// workgroup; out-of-range threads rewrite the last word with its own value,
+// so every load is issued before any wait.
+__device__ __forceinline__ void stage_row(const uint4* __restrict__ src, int n16, uint4* dst) {
+  constexpr int U = 8;  // up to 2048 words (32 KB)
+  uint4 t[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) t[u] = src[min((int)threadIdx.x + 256 * u, n16 - 1)];
+  // Out-of-range threads rewrite the last word with its own value: stores
+  // stay unconditional, so the loads above are all issued before any wait.
+#pragma unroll
+  for (int u = 0; u < U; ++u) dst[min((int)threadIdx.x + 256 * u, n16 - 1)] = t[u];
+}
+
+
 }  // namespace k3

@@ -14,6 +14,7 @@
 //      same bits — and selects among them.
 #include "internal.h"
 #include "kern_common.h"
+#include "decode_t1.h"
 
 #include <limits.h>
 
@@ -248,26 +249,35 @@ __device__ __forceinline__ void lane_best(const uint64_t (&key)[kMaxJ], uint32_t
     if (!((taken >> j) & 1u) && key[j] > kb) { kb = key[j]; jb = j; }
 }
 
-// One wave (= one workgroup) per token.  Lane l holds experts l + 64 j as
+// LDS of one token's selection (one wave).
+struct TopkLds {
+  double candL[1024];
+  int candId[1024];
+  int candTaken[1024];
+  int chosen[1024];
+};
+
+// Orders the wave's LDS accesses (the selection runs in a single wave, so no
+// workgroup barrier is needed, nor allowed when it shares a workgroup).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Token t's selection by one wave.  Lane l holds experts l + 64 j as
 // order-preserving 64-bit keys; each of k rounds takes the wave maximum with
 // DPP, ties between lanes going to the lower expert id.
 template <bool XF32>
-__global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ logits,
-                                                   const float* __restrict__ lbound,
-                                                   const void* __restrict__ x,
-                                                   const uint16_t* __restrict__ wr,
-                                                   int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ w_out,
-                                                   float* __restrict__ logits_out,
-                                                   int32_t* __restrict__ diag, int T, int d, int E,
-                                                   int k, PermOut perm) {
-  __shared__ double candL[1024];
-  __shared__ int candId[1024];
-  __shared__ int candTaken[1024];
-  __shared__ int chosen[1024];
-  const int lane = threadIdx.x;
-  const int t = blockIdx.x;
-  if (t >= T) return;
+__device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restrict__ logits,
+                           const float* __restrict__ lbound, const void* __restrict__ x,
+                           const uint16_t* __restrict__ wr, int32_t* __restrict__ idx_out,
+                           float* __restrict__ w_out, float* __restrict__ logits_out,
+                           int32_t* __restrict__ diag, int d, int E, int k, const PermOut& perm) {
+  double* candL = sm.candL;
+  int* candId = sm.candId;
+  int* candTaken = sm.candTaken;
+  int* chosen = sm.chosen;
   const int nj = (E + kWave - 1) / kWave;
   const double* lrow = logits + (size_t)t * E;
   const float* brow = lbound + (size_t)t * E;
@@ -350,12 +360,12 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
       n += __popcll(bal);
     }
     for (int q = lane; q < 1024; q += kWave) chosen[q] = 0;
-    __syncthreads();
+    wave_sync();
     for (int q = lane; q < n; q += kWave) {
       candL[q] = exact_logit<XF32>(x, wr, t, candId[q], d);
       candTaken[q] = 0;
     }
-    __syncthreads();
+    wave_sync();
     for (int r = 0; r < k; ++r) {
       double bv = -INFINITY;
       int bi = INT_MAX, bq = -1;
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
         if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; owner = oq; }
       }
       if (lane == 0) { candTaken[owner] = 1; chosen[bi] = 1; }
-      __syncthreads();
+      wave_sync();
     }
     taken = 0;
 #pragma unroll
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
       perm.pair_pos[lane] = lane;
     }
   }
-  __syncthreads();
+  wave_sync();
   // k <= 64: one slot per lane; z summed by the fixed butterfly
   const double ep = lane < k ? exp(candL[lane] - m) : 0.0;
   const double z = wave_sum(ep);
@@ -426,7 +436,78 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
   }
 }
 
+template <bool XF32>
+__global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ logits,
+                                                   const float* __restrict__ lbound,
+                                                   const void* __restrict__ x,
+                                                   const uint16_t* __restrict__ wr,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ w_out,
+                                                   float* __restrict__ logits_out,
+                                                   int32_t* __restrict__ diag, int T, int d, int E,
+                                                   int k, PermOut perm) {
+  __shared__ TopkLds sm;
+  if ((int)blockIdx.x >= T) return;
+  topk_token<XF32>(blockIdx.x, threadIdx.x, sm, logits, lbound, x, wr, idx_out, w_out,
+                   logits_out, diag, d, E, k, perm);
+}
+
+// One token: the selection (wave 0 of workgroup 0) runs beside the shared
+// experts' gate/up (every other wave takes one (expert, feature) item), which
+// does not depend on the routing.  Workgroups of 4 waves; x is staged in LDS
+// by every workgroup before the roles split, and no barrier follows.
+__global__ __launch_bounds__(256) void topk_shared_t1(
+    const double* __restrict__ logits, const float* __restrict__ lbound,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ diag, int d,
+    int E, int k, PermOut perm, const uint16_t* __restrict__ w13s, float* __restrict__ hs, int fs,
+    int S) {
+  __shared__ TopkLds sm;
+  __shared__ uint4 xs[kSgU * kWave];
+  stage_row(reinterpret_cast<const uint4*>(x), d / 8, xs);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw == 0) {
+    topk_token<false>(0, lane, sm, logits, lbound, x, wr, idx_out, w_out, nullptr, diag, d, E, k,
+                      perm);
+  } else if (gw - 1 < S * fs) {
+    shared_gateup_item(gw - 1, w13s, xs, hs, d, fs, lane);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_router_logits(const k3moe_shape& s, const void* x, const uint16_t* wr,
+                                const RouteWs& ws, hipStream_t st) {
+  const int T = (int)s.T;
+  if (use_mfma(s))
+    router_mfma_f64<<<dim3((T + 31) / 32, (s.E + 31) / 32), 256, 0, st>>>(
+        static_cast<const uint16_t*>(x), wr, ws.logits, ws.lbound, T, s.d, s.E);
+  else if (s.x_dtype == K3MOE_F32)
+    router_gemv_f64<true><<<dim3((s.E + 3) / 4), 256, 0, st>>>(x, wr, ws.logits, ws.lbound, T, s.d,
+                                                               s.E);
+  else
+    router_gemv_f64<false><<<dim3((s.E + 3) / 4), 256, 0, st>>>(x, wr, ws.logits, ws.lbound, T,
+                                                                s.d, s.E);
+  return hipGetLastError();
+}
+
+bool topk_shared_t1_ok(const k3moe_shape& s) {
+  return s.T == 1 && s.x_dtype == K3MOE_BF16 && s.d == kSgU * 8 * kWave && s.n_shared > 0;
+}
+
+hipError_t launch_topk_shared_t1(const k3moe_shape& s, const void* x, const uint16_t* wr,
+                                 int32_t* idx, float* w, int32_t* diag, const RouteWs& ws,
+                                 const PermOut& perm, const k3moe_expert_bank& shared, float* hs,
+                                 hipStream_t st) {
+  if (!topk_shared_t1_ok(s)) return hipErrorInvalidValue;
+  const int items = shared.n_experts * shared.f;
+  topk_shared_t1<<<(items + 1 + 3) / 4, 256, 0, st>>>(
+      ws.logits, ws.lbound, static_cast<const uint16_t*>(x), wr, idx, w, diag, s.d, s.E, s.k, perm,
+      static_cast<const uint16_t*>(shared.w13), hs, shared.f, shared.n_experts);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, int32_t* idx,
                         float* w, float* logits_out, int32_t* diag, const RouteWs& ws,
