@@ -409,8 +409,8 @@ k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* we
   e = launch_expert_ffn(s, weights->routed, x, L.offsets, L.sorted_pair, L.y_perm,
                         carve_expert(s, L.scratch, nullptr), st);
   if (e != hipSuccess) return hip_status(e, "k3moe_layer routed experts");
-  if (s.n_shared > 0) {
-    // the shared experts' down kernel finishes each output with the combine
+  if (s.n_shared > 0 && !shared_mfma_ok(s)) {
+    // the shared experts' down GEMV finishes each output with the combine
     CombineArgs comb;
     comb.y_perm = L.y_perm;
     comb.pair_pos = L.pair_pos;
@@ -423,7 +423,14 @@ k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* we
     e = launch_shared_ffn(s, weights->shared, x, L.shared_y, sws, st, comb);
     return hip_status(e, "k3moe_layer shared experts + combine");
   }
-  e = launch_combine(s, L.y_perm, L.pair_pos, L.topk_w, nullptr, out, st);
+  if (s.n_shared > 0) {
+    SharedWs sws;
+    sws.h = L.shared_h;
+    e = launch_shared_ffn(s, weights->shared, x, L.shared_y, sws, st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer shared experts");
+  }
+  e = launch_combine(s, L.y_perm, L.pair_pos, L.topk_w, s.n_shared > 0 ? L.shared_y : nullptr,
+                     out, st);
   return hip_status(e, "k3moe_layer combine");
 }
 

@@ -11,7 +11,7 @@
 namespace k3 {
 
 // Smallest token count that takes the matrix-core (MFMA) path class; the
-// class also needs bf16 activations, d % 256 == 0 and f % 128 == 0.
+// class also needs bf16 activations, d % 512 == 0 and f % 256 == 0.
 constexpr int64_t kMfmaMinT = 32;
 bool mfma_shape_ok(const k3moe_shape& s);
 inline bool use_mfma(const k3moe_shape& s) { return s.T >= kMfmaMinT && mfma_shape_ok(s); }

@@ -336,8 +336,8 @@ __device__ void build_mtiles_n(const int32_t* __restrict__ offsets, int E, int B
 // Down (DOWN = true): item = (m-tile, 256 outputs); consumer w owns outputs
 // nt*256 + w*64 + [0, 64); A = split h; each step issues the hi product, then
 // the lo product; output y fp32.
-template <int MF, int RA, int RB, bool DOWN>
-__global__ __launch_bounds__(kPcThreads) void mx_gemm_pc(
+template <int MF, int RA, int RB, bool DOWN, int NC>
+__global__ __launch_bounds__((NC + 4) * 64) void mx_gemm_pc(
     const uint8_t* __restrict__ a_src, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pair, float* __restrict__ out, int d, int f, int E,
@@ -345,10 +345,14 @@ __global__ __launch_bounds__(kPcThreads) void mx_gemm_pc(
   constexpr int BM = 16 * MF;
   constexpr int AU = DOWN ? 32 : 16;
   constexpr int A_SLOT = BM * AU * 16;
-  constexpr int B_CODES = 256 * 64;
-  constexpr int B_SLOT = B_CODES + 256 * 4;
-  constexpr int NA = BM * AU / 2 / 64;   // A copies per A wave per stage
-  constexpr int NB = 8 + 2;              // B copies per B wave per stage
+  constexpr int NTH = (NC + 4) * 64;
+  constexpr int BROWS = NC * 64;                // weight rows per stage
+  constexpr int B_CODES = BROWS * 64;
+  constexpr int B_SLOT = B_CODES + BROWS * 4;
+  constexpr int NA = BM * AU / 2 / 64;          // A copies per A wave per stage
+  constexpr int NBC = BROWS * 4 / 2 / 64;       // B code copies per B wave per stage
+  constexpr int NBS = BROWS / 2 / 64;           // B scale copies per B wave per stage
+  constexpr int NB = NBC + NBS;
   static_assert(RA >= 2 && RB >= 2, "rings need two slots");
   // at most R - 1 stages of copies are in flight per copier wave; the memory
   // counter tracks 63
@@ -356,14 +360,14 @@ __global__ __launch_bounds__(kPcThreads) void mx_gemm_pc(
   __shared__ __attribute__((aligned(16))) uint8_t sA[RA * A_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sB[RB * B_SLOT];
   __shared__ int s_mt[kMaxE + 1];
-  __shared__ int s_wave[kPcThreads / 64];
+  __shared__ int s_wave[NTH / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const bool a_copier = wv == 4 || wv == 5, b_copier = wv >= 6;
-  const int pa = wv - 4, pb = wv - 6;
-  build_mtiles_n<kPcThreads>(offsets, E, BM, s_mt, s_wave);
-  const int NT = DOWN ? d / 256 : f / 128;
+  const bool a_copier = wv == NC || wv == NC + 1, b_copier = wv >= NC + 2;
+  const int pa = wv - NC, pb = wv - NC - 2;
+  build_mtiles_n<NTH>(offsets, E, BM, s_mt, s_wave);
+  const int NT = DOWN ? d / (NC * 64) : f / (NC * 32);
   const int nst = (DOWN ? f : d) / kBK;
   const ItemRange ir = item_range((long)s_mt[E] * NT);
   const size_t w_row = (size_t)(DOWN ? f : d) / 2, s_row = (size_t)(DOWN ? f : d) / 32;
@@ -411,30 +415,30 @@ __global__ __launch_bounds__(kPcThreads) void mx_gemm_pc(
       const int mt = (int)(it / NT), nt = (int)(it - (long)mt * NT);
       const int e = mtile_expert(s_mt, E, mt);
       auto grow = [&](int r) -> size_t {
-        if (DOWN) return (size_t)nt * 256 + r;
+        if (DOWN) return (size_t)nt * (NC * 64) + r;
         const int cw = r >> 6, nf = (r >> 4) & 3;
-        return (size_t)((nf >= 2 ? f : 0) + nt * 128 + cw * 32 + (nf & 1) * 16 + (r & 15));
+        return (size_t)((nf >= 2 ? f : 0) + nt * (NC * 32) + cw * 32 + (nf & 1) * 16 + (r & 15));
       };
       const uint8_t* wbase = wq + (size_t)e * e_rows * w_row;
       const uint8_t* sbase = wsc + (size_t)e * e_rows * s_row;
-      const uint8_t* bp[8];
-      const uint8_t* sp[2];
+      const uint8_t* bp[NBC];
+      const uint8_t* sp[NBS];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int r = (pb * 512 + q * 64 + lane) >> 2;
+      for (int q = 0; q < NBC; ++q) {
+        const int r = (pb * (NBC * 64) + q * 64 + lane) >> 2;
         const int b = (lane & 3) ^ ((r >> 2) & 3);
         bp[q] = wbase + grow(r) * w_row + b * 16;
       }
 #pragma unroll
-      for (int q = 0; q < 2; ++q) sp[q] = sbase + grow(pb * 128 + q * 64 + lane) * s_row;
+      for (int q = 0; q < NBS; ++q) sp[q] = sbase + grow(pb * (NBS * 64) + q * 64 + lane) * s_row;
       auto issue_b = [&](int st, int slot) {
         uint8_t* base = sB + slot * B_SLOT;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          dma16_to_lds(bp[q] + st * (kBK / 2), base + (pb * 512 + q * 64) * 16);
+        for (int q = 0; q < NBC; ++q)
+          dma16_to_lds(bp[q] + st * (kBK / 2), base + (pb * (NBC * 64) + q * 64) * 16);
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          dma4_to_lds(sp[q] + st * 4, base + B_CODES + (pb * 128 + q * 64) * 4);
+        for (int q = 0; q < NBS; ++q)
+          dma4_to_lds(sp[q] + st * 4, base + B_CODES + (pb * (NBS * 64) + q * 64) * 4);
       };
 #pragma unroll
       for (int q = 0; q < RB - 1; ++q) issue_b(min(q, nst - 1), q);
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(kPcThreads) void mx_gemm_pc(
           const int m = i * 16 + lg * 4 + r;
           if (m < rows) {
             if (DOWN) {
-              float* yr = out + (size_t)(row0 + m) * d + nt * 256 + wv * 64 + ln;
+              float* yr = out + (size_t)(row0 + m) * d + nt * (NC * 64) + wv * 64 + ln;
 #pragma unroll
               for (int nf = 0; nf < 4; ++nf) yr[nf * 16] = acc[i][nf][r];
             } else {
@@ -522,7 +526,7 @@ __global__ __launch_bounds__(kPcThreads) void mx_gemm_pc(
                 const float v = silu_mul(acc[i][half][r], acc[i][half + 2][r]);
                 const uint16_t hi = f32_to_bf16(v);
                 const uint16_t lo = f32_to_bf16(v - __uint_as_float((uint32_t)hi << 16));
-                const int col = nt * 128 + wv * 32 + half * 16 + ln;
+                const int col = nt * (NC * 32) + wv * 32 + half * 16 + ln;
                 hr[(col >> 3) * 16 + (col & 7)] = hi;
                 hr[(col >> 3) * 16 + 8 + (col & 7)] = lo;
               }
@@ -788,7 +792,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // Item = (m-tile, n-tile of 256 outputs); the contraction runs over the
 // shared experts in order, then over each one's fs elements, so
 // y = sum over s of h_s W2_s^T is one accumulation chain per output.
-template <int MF>
+template <int MF, bool COMBINE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void down_shared_mfma(
     const float* __restrict__ h, const uint16_t* __restrict__ w2, float* __restrict__ y, int T,
     int d, int fs, int S, CombineArgs comb) {
@@ -905,7 +909,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
           for (int nf = 0; nf < 4; ++nf) {
             const size_t oi = (size_t)t * d + o + nf * 16;
-            if (comb.y_perm) {
+            if (COMBINE) {
               const float v = combine_one(acc[i][nf][r], comb.y_perm, comb.pair_pos, comb.topk_w,
                                           t, comb.k, d, o + nf * 16);
               if (comb.out_bf16) static_cast<uint16_t*>(comb.out)[oi] = f32_to_bf16(v);
@@ -960,13 +964,16 @@ hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& b, 
   else gateup_shared_mfma<2><<<g, blk, 0, st>>>(xb, w13, h, T, s.d, fs, S);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (T >= 128) down_shared_mfma<4><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
-  else down_shared_mfma<2><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
+  // (the combine stays a kernel of its own in this class: folded into this
+  // epilogue its scattered reads cost more than they save)
+  if (comb.y_perm) return hipErrorInvalidValue;
+  if (T >= 128) down_shared_mfma<4, false><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
+  else down_shared_mfma<2, false><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
   return hipGetLastError();
 }
 
 bool mfma_shape_ok(const k3moe_shape& s) {
-  return s.x_dtype == K3MOE_BF16 && s.d % 256 == 0 && s.f % 128 == 0;
+  return s.x_dtype == K3MOE_BF16 && s.d % 512 == 0 && s.f % 256 == 0;
 }
 
 hipError_t launch_gateup_mfma(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
@@ -994,15 +1001,19 @@ hipError_t launch_gateup_pc(const k3moe_shape& s, const k3moe_expert_bank& b, co
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   const uint8_t* w = static_cast<const uint8_t*>(b.w13);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
-  const dim3 g(mfma_grid() / 2), blk(kPcThreads);   // one 8-wave workgroup per CU
-#define K3_PC(MF, RA, RB) \
-  mx_gemm_pc<MF, RA, RB, false><<<g, blk, 0, st>>>(xb, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k)
+  const dim3 g(mfma_grid() / 2);   // one workgroup per CU
+#define K3_PC(MF, RA, RB, NC)                                                               \
+  mx_gemm_pc<MF, RA, RB, false, NC><<<g, dim3((NC + 4) * 64), 0, st>>>(xb, w, ws, offsets, \
+                                                                      sorted_pair, h, s.d, s.f, s.E, s.k)
+  // Four consumer waves (128 features per item) up to 96-row m-tiles; for
+  // taller expected m-tiles, eight consumer waves (256 features per item,
+  // half the activation re-reads) with 80-row m-tiles.
   const int mf = pick_mf(s, 8);
-  if (mf <= 1) K3_PC(1, 3, 7);
-  else if (mf <= 2) K3_PC(2, 3, 7);
-  else if (mf <= 4) K3_PC(4, 3, 6);
-  else if (mf <= 6) K3_PC(6, 3, 4);
-  else K3_PC(8, 2, 5);
+  if (mf <= 1) K3_PC(1, 3, 7, 4);
+  else if (mf <= 2) K3_PC(2, 3, 7, 4);
+  else if (mf <= 4) K3_PC(4, 3, 6, 4);
+  else if (mf <= 6) K3_PC(6, 3, 4, 4);
+  else K3_PC(5, 2, 3, 8);
 #undef K3_PC
   return hipGetLastError();
 }
@@ -1012,13 +1023,14 @@ hipError_t launch_down_pc(const k3moe_shape& s, const k3moe_expert_bank& b, cons
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
   const uint8_t* w = static_cast<const uint8_t*>(b.w2);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w2_scale);
-  const dim3 g(mfma_grid() / 2), blk(kPcThreads);
-#define K3_DPC(MF, RA, RB) \
-  mx_gemm_pc<MF, RA, RB, true><<<g, blk, 0, st>>>(hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k)
-  const int mf = pick_mf(s, 4);
-  if (mf <= 1) K3_DPC(1, 3, 7);
-  else if (mf <= 2) K3_DPC(2, 3, 6);
-  else K3_DPC(4, 2, 5);
+  const dim3 g(mfma_grid() / 2);
+#define K3_DPC(MF, RA, RB, NC)                                                               \
+  mx_gemm_pc<MF, RA, RB, true, NC><<<g, dim3((NC + 4) * 64), 0, st>>>(hb, w, ws, offsets, nullptr, \
+                                                                     y, s.d, s.f, s.E, s.k)
+  const int mf = pick_mf(s, 3);
+  if (mf <= 1) K3_DPC(1, 3, 3, 8);
+  else if (mf <= 2) K3_DPC(2, 3, 3, 8);
+  else K3_DPC(3, 2, 3, 8);
 #undef K3_DPC
   return hipGetLastError();
 }
