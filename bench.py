@@ -10,9 +10,10 @@ routed weights come from HBM rather than from a cache warmed by the previous
 step.
 
 Printed: one JSON line with throughput (tokens/s), the roofline of the
-dominant kernel (the routed gate/up MXFP4 GEMV, timed live with HIP events on
-the stream it runs on) and the CPU oracle timed on a bounded sample of the same
-workload on this host.
+dominant kernel (the routed gate/up kernel, timed live with HIP events on the
+stream it runs on: HBM-bound for decode batches, bf16-MFMA-bound for large
+batches), per-step percentiles, and the CPU oracle timed on a bounded sample
+of the same workload on this host.
 """
 import argparse
 import hashlib
@@ -26,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0     # dense bf16 matrix peak (the format the large-batch path issues)
+MXFP4_MFMA_PEAK_TFLOPS = 10100.0   # dense MXFP4 matrix peak, for reference
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (MXFP4 bytes) at batch 1/64/4096"
 PMC_FILE = os.path.join(ROOT, "profiles", "gateup_t1_decode_b1_counters.md")
 GEMV_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "gemv.hip")
@@ -54,37 +57,44 @@ def stored_traffic():
 
 
 def cpu_baseline(cfg, budget_s: float):
-    """The oracle, as it stands, on consecutive tokens of the workload until
-    about budget_s seconds of oracle time are spent (input generation excluded)."""
+    """The oracle, as it stands, on consecutive tokens of the workload (chunks of
+    up to 8 tokens, the workload's own router and experts) until about budget_s
+    seconds of oracle time are spent (input generation excluded)."""
     import gen
     import oracle
     orc = oracle.default()
     wr = gen.router(cfg)
     shared = gen.shared_bank(cfg)
-    spent, n = 0.0, 0
-    T = cfg.T
-    while spent < budget_s and n < 64:
-        x = gen.x(cfg.with_tokens((n + 1) * T), n * T, (n + 1) * T)
+    spent, done = 0.0, 0
+    chunk = min(cfg.T, 8)
+    limit = cfg.T * 64
+    experts = {}
+    while spent < budget_s and done < limit:
+        x = gen.x(cfg, done, done + chunk) if done + chunk <= cfg.T else \
+            gen.x(cfg.with_tokens(done + chunk), done, done + chunk)
         x64 = oracle.to_f64(x)
         t0 = time.perf_counter()
         _, idx, w = orc.route(x64, wr, cfg.k)
         spent += time.perf_counter() - t0
-        experts = {int(e): gen.routed_expert(cfg, int(e)) for e in set(idx.ravel().tolist())}
+        need = set(idx.ravel().tolist())
+        experts = {e: experts[e] if e in experts else gen.routed_expert(cfg, int(e)) for e in need}
         t0 = time.perf_counter()
         orc.token_outputs(x, idx, w, lambda e: experts[e], shared)
         spent += time.perf_counter() - t0
-        n += 1
-    return dict(value=n * T / spent, unit="tokens/s", cores=orc.threads(), kind="oracle",
-                sample=f"{n} batch(es) of {T} token(s) of {cfg.name}, full layer per token "
-                       f"(fp64 router, top-k, {cfg.k} MXFP4 experts, {cfg.n_shared} shared, "
-                       f"combine), {spent:.1f} s of oracle time")
+        done += chunk
+    return dict(value=done / spent, unit="tokens/s", cores=orc.threads(), kind="oracle",
+                sample=f"first {done} token(s) of {cfg.name} in chunks of {chunk}, full layer "
+                       f"per token (fp64 router, top-k, {cfg.k} MXFP4 experts, {cfg.n_shared} "
+                       f"shared, combine), {spent:.1f} s of oracle time")
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50 for decode workloads, 10 for prefill)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="warm-up steps (default 5 for decode workloads, 3 for prefill)")
     ap.add_argument("--workload", default="decode_b1",
                     help="decode_b1 (default), decode_b64, prefill_4096, prefill_16384_zipf")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -105,13 +115,15 @@ def main():
 
     import gen
     import gen.device
-    from mxfp4_routed_expert_gemv_amd import DIAG_COUNT, OP_LAYER, lib
+    from mxfp4_routed_expert_gemv_amd import DIAG_COUNT, OP_EXPERT_FFN, OP_LAYER, k3moe_expert_ffn, lib
     from mxfp4_routed_expert_gemv_amd.layer import MoELayer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     cfg = gen.get(args.workload)
-    K, W = args.steps, args.warmup
+    big = cfg.T >= 1024
+    K = args.steps if args.steps is not None else (10 if big else 50)
+    W = args.warmup if args.warmup is not None else (3 if big else 5)
     log(f"workload {cfg.name}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
 
     wl = gen.device.build(cfg.with_tokens(1), routed_on_device=True)
@@ -135,17 +147,22 @@ def main():
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------- timed region
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
+    ev[0].record(stream)
     for i in range(K):
         layer(batches[W + i], out=out, diag=diag, workspace=ws)
-    ev1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = ev0.elapsed_time(ev1) / K
-    log(f"layer: {ms_per_step * 1e3:.1f} us/step (wall {wall / K * 1e6:.1f} us/step)")
+    ms_per_step = ev[0].elapsed_time(ev[K]) / K
+    steps_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(K))
+
+    def pct(q):
+        return steps_ms[min(K - 1, int(round(q * (K - 1))))]
+    log(f"layer: {ms_per_step * 1e3:.1f} us/step (wall {wall / K * 1e6:.1f} us/step; "
+        f"p10 {pct(0.1) * 1e3:.1f} p50 {pct(0.5) * 1e3:.1f} p90 {pct(0.9) * 1e3:.1f} us)")
 
     # ------------------------------------------- dominant kernel, HIP events
     # The routed gate/up GEMV alone: route + permute of K fresh tokens are
@@ -172,9 +189,27 @@ def main():
     per_expert_gu = lib.k3moe_mxfp4_bytes(2 * cfg.f, cfg.d)
     gu_bytes = sum(touched) / len(touched) * per_expert_gu
     gu_avg_s = sum(gu_ms) / len(gu_ms) / 1e3
-    achieved = gu_bytes / gu_avg_s / 1e9
-    log(f"gate/up GEMV: {gu_avg_s * 1e6:.1f} us avg, {gu_bytes / 1e6:.1f} MB/launch, "
-        f"{achieved:.0f} GB/s")
+    gu_gbs = gu_bytes / gu_avg_s / 1e9
+    gu_flops = 2.0 * T * cfg.k * 2 * cfg.f * cfg.d      # useful gate/up FLOPs per launch
+    gu_tflops = gu_flops / gu_avg_s / 1e12
+    mfma_class = layer.path_class(T) == 1
+    log(f"gate/up: {gu_avg_s * 1e6:.1f} us avg, {gu_bytes / 1e6:.1f} MB/launch, "
+        f"{gu_gbs:.0f} GB/s, {gu_tflops:.1f} TFLOP/s useful")
+
+    # routed expert FFN (gate/up + down) of the same prepared batches
+    ffn_ms = None
+    if mfma_class:
+        y = torch.empty((T * cfg.k, cfg.d), dtype=torch.float32, device="cuda")
+        fws = layer.workspace(shape, OP_EXPERT_FFN)
+        a.record(stream)
+        for x, offsets, sp in prepared:
+            k3moe_expert_ffn(shape, layer.routed_bank, x, offsets, sp, y, fws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ffn_ms = a.elapsed_time(b) / K
+        ffn_flops = 2.0 * T * cfg.k * 3 * cfg.f * cfg.d
+        log(f"routed FFN: {ffn_ms * 1e3:.1f} us avg, {ffn_flops / (ffn_ms / 1e3) / 1e12:.1f} "
+            f"TFLOP/s useful")
 
     # whole-layer algorithmic bytes (MXFP4 experts touched + shared + router + x, out)
     per_expert = lib.k3moe_mxfp4_bytes(2 * cfg.f, cfg.d) + lib.k3moe_mxfp4_bytes(cfg.d, cfg.f)
@@ -208,14 +243,27 @@ def main():
                    "experts": cfg.E, "top_k": cfg.k, "shared_experts": cfg.n_shared,
                    "weights": "routed MXFP4 (E2M1 + E8M0/32), shared and router bf16",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gateup_t1" if T == 1 else "gateup_persistent", "bytes_per_launch": gu_bytes,
-                     "avg_launch_us": gu_avg_s * 1e6},
+        "roofline": ({"bound": "mfma", "achieved": gu_tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": gu_tflops / BF16_MFMA_PEAK_TFLOPS,
+                      "traffic": None, "kernel": "mx_gemm_pc (gate/up)",
+                      "flops_per_launch": gu_flops, "avg_launch_us": gu_avg_s * 1e6,
+                      "frac_of_mxfp4_peak": gu_tflops / MXFP4_MFMA_PEAK_TFLOPS,
+                      "mxfp4_gbs": gu_gbs}
+                     if mfma_class else
+                     {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                      "kernel": "gateup_t1" if T == 1 else "gateup_persistent",
+                      "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6}),
+        "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "layer_hbm_gbs": layer_bytes / (ms_per_step / 1e3) / 1e9,
         "layer_bytes_per_step": layer_bytes,
         "rechecked_tokens": int(diag[0].item()),
     }
+    if ffn_ms is not None:
+        ffn_tflops = 2.0 * T * cfg.k * 3 * cfg.f * cfg.d / (ffn_ms / 1e3) / 1e12
+        result["routed_ffn"] = {"avg_us": ffn_ms * 1e3, "useful_tflops": ffn_tflops,
+                                "frac_of_bf16_peak": ffn_tflops / BF16_MFMA_PEAK_TFLOPS,
+                                "frac_of_mxfp4_peak": ffn_tflops / MXFP4_MFMA_PEAK_TFLOPS}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

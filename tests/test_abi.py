@@ -143,7 +143,7 @@ def test_status_strings_and_path_class():
     assert k3.k3moe_path_class(big_shape(T=31)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=32)) == k3.PATH_MFMA
     assert k3.k3moe_path_class(big_shape(T=4096)) == k3.PATH_MFMA
-    # the matrix-core class needs bf16 activations and d % 256, f % 128
+    # the matrix-core class needs bf16 activations and d % 512, f % 256
     assert k3.k3moe_path_class(big_shape(T=4096, x_dtype=k3.F32)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, d=7168 + 128)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, f=2048 + 64)) == k3.PATH_GEMV
