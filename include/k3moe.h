@@ -68,7 +68,8 @@ enum {
   K3MOE_OP_EXPERT_FFN = 2,
   K3MOE_OP_SHARED_FFN = 3,
   K3MOE_OP_COMBINE = 4,
-  K3MOE_OP_LAYER = 5
+  K3MOE_OP_LAYER = 5,
+  K3MOE_OP_EXPERT_GATEUP = 6
 };
 /* Path classes (k3moe_path_class). */
 enum { K3MOE_PATH_GEMV = 0, K3MOE_PATH_MFMA = 1 };
@@ -139,9 +140,10 @@ size_t k3moe_workspace_bytes(const k3moe_shape* shape, int op);
 uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols);
 
 /* Which path class a call with this shape takes.  K3MOE_PATH_MFMA (grouped
- * GEMMs on the bf16 matrix cores, weights decoded exactly in registers,
- * h split into two bf16 terms) when T >= 32, x is bf16, d % 256 == 0 and
- * f % 128 == 0; K3MOE_PATH_GEMV (one pass over each touched expert's weights
+ * GEMMs on the scaled MXFP4 matrix-core instruction: the stored weight bytes
+ * as one operand, the activations split into E4M3 passes with E8M0 block
+ * scales as the other) when T >= 32, x is bf16, d % 512 == 0 and
+ * f % 512 == 0; K3MOE_PATH_GEMV (one pass over each touched expert's weights
  * per token, fp32 dot products) otherwise.  Results of the two classes agree
  * within the stated tolerance, not bit for bit.  Returns K3MOE_PATH_GEMV for
  * an invalid shape. */
@@ -182,20 +184,24 @@ k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank*
                               const void* x, const int32_t* offsets, const int32_t* sorted_pair,
                               float* y, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The two halves of k3moe_expert_ffn, one kernel each (same kernels, same
- * bits):
+/* The two halves of k3moe_expert_ffn (same kernels, same bits):
  * gate/up + SiLU-GLU:  h, row q = silu(Wg x) * (Wu x) of expert e on token
  *   sorted_pair[q] / k (e as for k3moe_expert_ffn);
  * down:  y [T*k][d] fp32, row q = Wd_e h[q].
- * h is [T*k][f] 32-bit words.  GEMV path class: fp32 values.  MFMA path
- * class: each group of 8 features is 8 bf16 values hi, then 8 bf16 values
- * lo, with hi = RNE_bf16(h) and lo = RNE_bf16(h - hi), so h ~ hi + lo (the
- * form the matrix cores consume).  A buffer written by k3moe_expert_gateup
- * is meant for k3moe_expert_down with the same shape.
- * No workspace. */
+ * h is a buffer of [T*k][f] 32-bit words.  GEMV path class: fp32 values.
+ * MFMA path class: each row is f/128 stages of 400 bytes, the value split
+ * into 3 E4M3 passes with one E8M0 scale per pass and 32-feature block
+ * (h ~ sum_p code_p * 2^(scale_p - 127)): 3 x 128 code bytes in feature
+ * order, then byte 4p + b = scale of pass p, block b, then 4 unused bytes;
+ * this is the operand form of the scaled matrix-core instruction.  A buffer
+ * written by k3moe_expert_gateup is meant for k3moe_expert_down with the same
+ * shape.
+ * Workspace (gate/up only): k3moe_workspace_bytes(shape, K3MOE_OP_EXPERT_GATEUP)
+ * (0 in the GEMV class, where NULL is accepted): x in E4M3 passes. */
 k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_bank* bank,
                                  const void* x, const int32_t* offsets,
-                                 const int32_t* sorted_pair, float* h, void* stream);
+                                 const int32_t* sorted_pair, float* h, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 k3moe_status k3moe_expert_down(const k3moe_shape* shape, const k3moe_expert_bank* bank,
                                const float* h, const int32_t* offsets, float* y, void* stream);
 

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libk3moe.so")
 
 F32, BF16 = 0, 1
 FMT_MXFP4, FMT_BF16 = 0, 1
-OP_ROUTE, OP_PERMUTE, OP_EXPERT_FFN, OP_SHARED_FFN, OP_COMBINE, OP_LAYER = range(6)
+(OP_ROUTE, OP_PERMUTE, OP_EXPERT_FFN, OP_SHARED_FFN, OP_COMBINE, OP_LAYER,
+ OP_EXPERT_GATEUP) = range(7)
 PATH_GEMV, PATH_MFMA = 0, 1
 DIAG_RECHECKED_TOKENS, DIAG_NONFINITE_LOGITS, DIAG_BAD_EXPERT_IDS = 0, 1, 2
 DIAG_COUNT = 4
@@ -80,7 +81,7 @@ def _load():
     lib.k3moe_expert_ffn.restype = ctypes.c_int
     lib.k3moe_expert_ffn.argtypes = [SP, ctypes.POINTER(ExpertBank), P, P, P, P, P, S, P]
     lib.k3moe_expert_gateup.restype = ctypes.c_int
-    lib.k3moe_expert_gateup.argtypes = [SP, ctypes.POINTER(ExpertBank), P, P, P, P, P]
+    lib.k3moe_expert_gateup.argtypes = [SP, ctypes.POINTER(ExpertBank), P, P, P, P, P, S, P]
     lib.k3moe_expert_down.restype = ctypes.c_int
     lib.k3moe_expert_down.argtypes = [SP, ctypes.POINTER(ExpertBank), P, P, P, P]
     lib.k3moe_shared_ffn.restype = ctypes.c_int
@@ -166,9 +167,11 @@ def k3moe_expert_ffn(shape, bank: ExpertBank, x, offsets, sorted_pair, y, worksp
                                 _stream(stream)))
 
 
-def k3moe_expert_gateup(shape, bank: ExpertBank, x, offsets, sorted_pair, h, stream=None):
+def k3moe_expert_gateup(shape, bank: ExpertBank, x, offsets, sorted_pair, h, workspace=None,
+                        stream=None):
+    wp, wb = _ws(workspace)
     _check(lib.k3moe_expert_gateup(ctypes.byref(shape), ctypes.byref(bank), _addr(x),
-                                   _addr(offsets), _addr(sorted_pair), _addr(h),
+                                   _addr(offsets), _addr(sorted_pair), _addr(h), wp, wb,
                                    _stream(stream)))
 
 

@@ -136,10 +136,20 @@ PermuteWs carve_permute(const k3moe_shape& s, void* ws, size_t* bytes) {
   return r;
 }
 
+ExpertWs carve_gateup(const k3moe_shape& s, void* ws, size_t* bytes) {
+  Carver c(ws);
+  ExpertWs r;
+  r.h = nullptr;
+  r.xq = use_mfma(s) ? c.take<uint8_t>(xq_bytes(s)) : nullptr;
+  if (bytes) *bytes = c.off;
+  return r;
+}
+
 ExpertWs carve_expert(const k3moe_shape& s, void* ws, size_t* bytes) {
   Carver c(ws);
   ExpertWs r;
   r.h = c.take<float>((size_t)s.T * s.k * s.f);
+  r.xq = use_mfma(s) ? c.take<uint8_t>(xq_bytes(s)) : nullptr;
   if (bytes) *bytes = c.off;
   return r;
 }
@@ -198,6 +208,7 @@ size_t k3moe_workspace_bytes(const k3moe_shape* shape, int op) {
     case K3MOE_OP_ROUTE: carve_route(*shape, nullptr, &n); break;
     case K3MOE_OP_PERMUTE: carve_permute(*shape, nullptr, &n); break;
     case K3MOE_OP_EXPERT_FFN: carve_expert(*shape, nullptr, &n); break;
+    case K3MOE_OP_EXPERT_GATEUP: carve_gateup(*shape, nullptr, &n); break;
     case K3MOE_OP_SHARED_FFN: carve_shared(*shape, nullptr, &n); break;
     case K3MOE_OP_COMBINE: n = 0; break;
     case K3MOE_OP_LAYER: carve_layer(*shape, nullptr, &n); break;
@@ -280,7 +291,8 @@ k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank*
 
 k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_bank* bank,
                                  const void* x, const int32_t* offsets,
-                                 const int32_t* sorted_pair, float* h, void* stream) {
+                                 const int32_t* sorted_pair, float* h, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   K3_CHECK(check_shape(shape));
   const k3moe_shape& s = *shape;
   K3_CHECK(check_routed_bank(s, bank));
@@ -289,7 +301,11 @@ k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_ba
   K3_CHECK(need_ptr(offsets, "offsets"));
   K3_CHECK(need_ptr(sorted_pair, "sorted_pair"));
   K3_CHECK(need_ptr(h, "h"));
-  return hip_status(launch_expert_gateup(s, *bank, x, offsets, sorted_pair, h,
+  size_t need = 0;
+  carve_gateup(s, nullptr, &need);
+  K3_CHECK(check_ws(workspace, workspace_bytes, need));
+  const ExpertWs ws = carve_gateup(s, workspace, nullptr);
+  return hip_status(launch_expert_gateup(s, *bank, x, offsets, sorted_pair, h, ws.xq,
                                          static_cast<hipStream_t>(stream)),
                     "k3moe_expert_gateup launch");
 }

@@ -162,7 +162,6 @@ template <bool XF32>
 struct XBlock;  // one 32-element activation block
 template <>
 struct XBlock<false> {
-  static constexpr int W = 4;   // 16-byte words per block
   uint4 v[4];
   __device__ __forceinline__ void load(const void* x, size_t elem) {
     const uint16_t* p = static_cast<const uint16_t*>(x) + elem;
@@ -177,7 +176,6 @@ struct XBlock<false> {
 };
 template <>
 struct XBlock<true> {
-  static constexpr int W = 8;
   uint4 v[8];
   __device__ __forceinline__ void load(const void* x, size_t elem) {
     const float* p = static_cast<const float*>(x) + elem;
@@ -821,8 +819,9 @@ void down_launch(const k3moe_shape& s, const k3moe_expert_bank& bank, const floa
 
 hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& bank,
                                 const void* x, const int32_t* offsets,
-                                const int32_t* sorted_pair, float* h, hipStream_t st) {
-  if (use_mfma(s)) return launch_gateup_pc(s, bank, x, offsets, sorted_pair, h, st);
+                                const int32_t* sorted_pair, float* h, uint8_t* xq,
+                                hipStream_t st) {
+  if (use_mfma(s)) return launch_gateup_scaled(s, bank, x, offsets, sorted_pair, h, xq, st);
   // One token: its row is staged in LDS (up to 32 KB).  Items loop over their
   // expert's tokens one at a time with the weight rows held in registers.
   const bool f32 = s.x_dtype == K3MOE_F32;
@@ -843,7 +842,7 @@ hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& b
 
 hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st) {
-  if (use_mfma(s)) return launch_down_pc(s, bank, h, offsets, y, st);
+  if (use_mfma(s)) return launch_down_scaled(s, bank, h, offsets, y, st);
   if (s.T == 1 && s.d % kDownT1Chunk == 0 && (size_t)s.f * 4 <= 32768) {
     const int chunks = s.d / kDownT1Chunk;
     int dev = 0, cus = 0;
@@ -865,7 +864,7 @@ hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& ban
 hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                              const int32_t* offsets, const int32_t* sorted_pair, float* y,
                              const ExpertWs& ws, hipStream_t st) {
-  hipError_t err = launch_expert_gateup(s, bank, x, offsets, sorted_pair, ws.h, st);
+  hipError_t err = launch_expert_gateup(s, bank, x, offsets, sorted_pair, ws.h, ws.xq, st);
   if (err != hipSuccess) return err;
   return launch_expert_down(s, bank, ws.h, offsets, y, st);
 }

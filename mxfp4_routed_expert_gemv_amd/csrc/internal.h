@@ -11,7 +11,7 @@
 namespace k3 {
 
 // Smallest token count that takes the matrix-core (MFMA) path class; the
-// class also needs bf16 activations, d % 512 == 0 and f % 256 == 0.
+// class also needs bf16 activations, d % 512 == 0 and f % 512 == 0.
 constexpr int64_t kMfmaMinT = 32;
 bool mfma_shape_ok(const k3moe_shape& s);
 inline bool use_mfma(const k3moe_shape& s) { return s.T >= kMfmaMinT && mfma_shape_ok(s); }
@@ -42,8 +42,12 @@ struct PermuteWs {
   int32_t* chunk_base;  // [nchunks][E]
 };
 struct ExpertWs {
-  float* h;           // [P][f]
+  float* h;           // [P][f] 32-bit words (GEMV class: fp32 h; MFMA class: h in passes)
+  uint8_t* xq;        // MFMA class: x in E4M3 passes, xq_bytes(s); else nullptr
 };
+// Bytes of the quantised activations of the MFMA class (0 in the GEMV class).
+size_t xq_bytes(const k3moe_shape& s);
+ExpertWs carve_gateup(const k3moe_shape& s, void* ws, size_t* bytes);
 struct SharedWs {
   float* h;           // [T][n_shared][f_shared]
 };
@@ -111,19 +115,20 @@ hipError_t launch_permute(const k3moe_shape& s, const int32_t* idx, int32_t* cou
                           int32_t* diag, const PermuteWs& ws, hipStream_t st);
 hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& bank,
                                 const void* x, const int32_t* offsets,
-                                const int32_t* sorted_pair, float* h, hipStream_t st);
+                                const int32_t* sorted_pair, float* h, uint8_t* xq,
+                                hipStream_t st);
 hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st);
-hipError_t launch_gateup_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
-                              const int32_t* offsets, const int32_t* sorted_pair, float* h,
-                              hipStream_t st);
-hipError_t launch_gateup_pc(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
-                            const int32_t* offsets, const int32_t* sorted_pair, float* h,
-                            hipStream_t st);
-hipError_t launch_down_pc(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
-                          const int32_t* offsets, float* y, hipStream_t st);
-hipError_t launch_down_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
-                            const int32_t* offsets, float* y, hipStream_t st);
+// Scaled-MXFP4 matrix-core path (MFMA class): x quantisation + gate/up, down.
+hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
+                                const int32_t* offsets, const int32_t* sorted_pair, float* h,
+                                uint8_t* xq, hipStream_t st);
+hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
+                              const int32_t* offsets, float* y, hipStream_t st);
+// Persistent grid of the grouped GEMMs (two workgroups per CU, a multiple of
+// 8) and the m-tile height (in 16-row blocks) for a batch.
+int mfma_grid();
+int pick_mf(const k3moe_shape& s, int max_mf);
 bool shared_mfma_ok(const k3moe_shape& s);
 hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                               float* h, float* y, hipStream_t st, const CombineArgs& comb);

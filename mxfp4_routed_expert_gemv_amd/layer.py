@@ -3,10 +3,10 @@ allocates outputs and workspaces with torch, and calls the library.  Every
 computation happens in libk3moe's kernels; this file only marshals."""
 import torch
 
-from . import (BF16, DIAG_COUNT, F32, FMT_BF16, FMT_MXFP4, OP_EXPERT_FFN, OP_LAYER, OP_PERMUTE,
-               OP_ROUTE, OP_SHARED_FFN, k3moe_combine, k3moe_expert_down, k3moe_expert_ffn,
-               k3moe_expert_gateup, k3moe_layer, k3moe_path_class, k3moe_permute, k3moe_route,
-               k3moe_shared_ffn, k3moe_workspace_bytes, make_bank, make_shape, make_weights)
+from . import (BF16, DIAG_COUNT, F32, FMT_BF16, FMT_MXFP4, OP_EXPERT_FFN, OP_EXPERT_GATEUP,
+               OP_LAYER, OP_PERMUTE, OP_ROUTE, OP_SHARED_FFN, k3moe_combine, k3moe_expert_down,
+               k3moe_expert_ffn, k3moe_expert_gateup, k3moe_layer, k3moe_path_class,
+               k3moe_permute, k3moe_route, k3moe_shared_ffn, k3moe_workspace_bytes, make_bank, make_shape, make_weights)
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -83,7 +83,8 @@ class MoELayer:
         s = self.shape(T, x.dtype)
         if h is None:
             h = torch.empty((max(T * self.k, 1), self.f), dtype=torch.float32, device=self._dev())
-        k3moe_expert_gateup(s, self.routed_bank, x, offsets, sorted_pair, h, stream)
+        k3moe_expert_gateup(s, self.routed_bank, x, offsets, sorted_pair, h,
+                            self.workspace(s, OP_EXPERT_GATEUP), stream)
         return h[:T * self.k]
 
     def expert_down(self, h, offsets, T, y=None, stream=None):

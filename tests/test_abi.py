@@ -56,7 +56,7 @@ def test_mxfp4_bytes_matches_pages_accounting():
 
 def test_workspace_sizes():
     s = big_shape(T=1)
-    for op in range(6):
+    for op in range(7):
         n = k3.k3moe_workspace_bytes(s, op)
         assert n % 256 == 0
     assert k3.k3moe_workspace_bytes(s, k3.OP_LAYER) >= 16 * 7168 * 4
@@ -64,6 +64,26 @@ def test_workspace_sizes():
     assert k3.k3moe_workspace_bytes(big_shape(T=0), k3.OP_LAYER) == 0
     assert k3.k3moe_workspace_bytes(big_shape(d=100), k3.OP_LAYER) == 0
     assert k3.k3moe_workspace_bytes(s, 99) == 0
+    # gate/up alone: nothing in the GEMV class; in the matrix-core class the
+    # activations in two E4M3 passes, 272 bytes per token and 128-element stage
+    assert k3.k3moe_workspace_bytes(s, k3.OP_EXPERT_GATEUP) == 0
+    big = big_shape(T=4096)
+    xq = 4096 * (7168 // 128) * 272
+    assert k3.k3moe_workspace_bytes(big, k3.OP_EXPERT_GATEUP) == (xq + 255) // 256 * 256
+    assert k3.k3moe_workspace_bytes(big, k3.OP_EXPERT_FFN) >= 4096 * 16 * 2048 * 4 + xq
+
+
+def test_gateup_workspace_validation():
+    bank = k3.make_bank(k3.FMT_MXFP4, 896, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
+
+    def gateup(shape, ws, nbytes):
+        return k3.lib.k3moe_expert_gateup(ctypes.byref(shape), ctypes.byref(bank), FAKE, FAKE,
+                                          FAKE, FAKE, ws, nbytes, None)
+    big = big_shape(T=64)
+    assert gateup(big, None, 0) == EWORKSPACE
+    need = k3.k3moe_workspace_bytes(big, k3.OP_EXPERT_GATEUP)
+    assert gateup(big, FAKE * 256, need - 256) == EWORKSPACE
+    assert gateup(big, FAKE * 256 + 16, need) == EALIGN
 
 
 def _route(shape, x=FAKE, wr=FAKE, idx=FAKE, w=FAKE, ws=(FAKE * 256, 1 << 40)):
@@ -143,8 +163,9 @@ def test_status_strings_and_path_class():
     assert k3.k3moe_path_class(big_shape(T=31)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=32)) == k3.PATH_MFMA
     assert k3.k3moe_path_class(big_shape(T=4096)) == k3.PATH_MFMA
-    # the matrix-core class needs bf16 activations and d % 512, f % 256
+    # the matrix-core class needs bf16 activations and d % 512, f % 512
     assert k3.k3moe_path_class(big_shape(T=4096, x_dtype=k3.F32)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, d=7168 + 128)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, f=2048 + 64)) == k3.PATH_GEMV
+    assert k3.k3moe_path_class(big_shape(T=4096, f=2048 + 256)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, d=0)) == k3.PATH_GEMV

@@ -103,11 +103,12 @@ def test_tiny_batch_composition_and_order():
 
 
 # ------------------------------------------------- matrix-core (MFMA) class
-# A shrunken layer with bf16 activations and d % 256 == 0, f % 128 == 0, so
+# A shrunken layer with bf16 activations and d % 512 == 0, f % 512 == 0, so
 # batches of 32 tokens or more take the grouped-GEMM path.  The token counts
-# below select every m-tile height (16 .. 80 rows) of the kernels; the skewed
-# variant gives experts several m-tiles and leaves others empty.
-MED = gen.configs.LayerConfig(name="medium", T=200, d=512, f=256, E=32, k=8, n_shared=2,
+# below select every m-tile height (16 .. 96 rows) of the kernels and every
+# count of live 16-row blocks; the skewed variant gives experts several
+# m-tiles and leaves others empty.
+MED = gen.configs.LayerConfig(name="medium", T=200, d=512, f=512, E=32, k=8, n_shared=2,
                               f_shared=256, x_dtype="bf16", out_dtype="f32", scale_lo=-8,
                               scale_hi=0)
 
