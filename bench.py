@@ -33,8 +33,8 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0      # dense fp8 matrix peak: the rate of the scal
 MXFP4_MFMA_PEAK_TFLOPS = 10100.0   # dense MXFP4 x MXFP4 matrix peak, for reference
 X_PASSES = 2                       # E4M3 passes that carry bf16 x exactly (one MFMA each)
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (MXFP4 bytes) at batch 1/64/4096"
-PMC_FILE = os.path.join(ROOT, "profiles", "gateup_t1_decode_b1_counters.md")
-GEMV_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "gemv.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "gateup_1tok_decode_b1_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "mxscale.hip")
 
 
 def log(msg):
@@ -42,7 +42,7 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    with open(GEMV_SRC, "rb") as fh:
+    with open(KERNEL_SRC, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
@@ -196,26 +196,29 @@ def main():
     gu_flops = 2.0 * T * cfg.k * 2 * cfg.f * cfg.d      # useful gate/up FLOPs per launch
     gu_tflops = gu_flops / gu_avg_s / 1e12
     mfma_class = layer.path_class(T) == 1
+    # the routed experts take the scaled matrix-core instruction at any batch
+    # size for bf16 activations and d, f multiples of 512
+    routed_scaled = cfg.x_dtype == "bf16" and cfg.d % 512 == 0 and cfg.f % 512 == 0
     # the bound of the gate/up kernel: useful FLOPs per weight byte against the
     # ridge of the instruction it issues (fp8 matrix peak / HBM peak)
-    mfma_bound = mfma_class and gu_flops / gu_bytes >= FP8_MFMA_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
+    mfma_bound = routed_scaled and gu_flops / gu_bytes >= FP8_MFMA_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
     log(f"gate/up: {gu_avg_s * 1e6:.1f} us avg, {gu_bytes / 1e6:.1f} MB/launch, "
         f"{gu_gbs:.0f} GB/s, {gu_tflops:.1f} TFLOP/s useful")
 
     # routed expert FFN (gate/up + down) of the same prepared batches
-    ffn_ms = None
-    if mfma_class:
-        y = torch.empty((T * cfg.k, cfg.d), dtype=torch.float32, device="cuda")
-        fws = layer.workspace(shape, OP_EXPERT_FFN)
-        a.record(stream)
-        for x, offsets, sp in prepared:
-            k3moe_expert_ffn(shape, layer.routed_bank, x, offsets, sp, y, fws)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ffn_ms = a.elapsed_time(b) / K
-        ffn_flops = 2.0 * T * cfg.k * 3 * cfg.f * cfg.d
-        log(f"routed FFN: {ffn_ms * 1e3:.1f} us avg, {ffn_flops / (ffn_ms / 1e3) / 1e12:.1f} "
-            f"TFLOP/s useful")
+    y = torch.empty((T * cfg.k, cfg.d), dtype=torch.float32, device="cuda")
+    fws = layer.workspace(shape, OP_EXPERT_FFN)
+    a.record(stream)
+    for x, offsets, sp in prepared:
+        k3moe_expert_ffn(shape, layer.routed_bank, x, offsets, sp, y, fws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ffn_ms = a.elapsed_time(b) / K
+    ffn_flops = 2.0 * T * cfg.k * 3 * cfg.f * cfg.d
+    per_expert_ffn = lib.k3moe_mxfp4_bytes(2 * cfg.f, cfg.d) + lib.k3moe_mxfp4_bytes(cfg.d, cfg.f)
+    ffn_bytes = sum(touched) / len(touched) * per_expert_ffn
+    log(f"routed FFN: {ffn_ms * 1e3:.1f} us avg, {ffn_bytes / (ffn_ms / 1e3) / 1e9:.0f} GB/s, "
+        f"{ffn_flops / (ffn_ms / 1e3) / 1e12:.1f} TFLOP/s useful")
 
     # whole-layer algorithmic bytes (MXFP4 experts touched + shared + router + x, out)
     per_expert = lib.k3moe_mxfp4_bytes(2 * cfg.f, cfg.d) + lib.k3moe_mxfp4_bytes(cfg.d, cfg.f)
@@ -259,7 +262,8 @@ def main():
                      if mfma_bound else
                      {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic if T == 1 else None,
-                      "kernel": ("gateup_t1" if T == 1 else "mx_gemm_scaled (gate/up)" if mfma_class
+                      "kernel": ("gateup_1tok" if T == 1 and routed_scaled
+                                 else "mx_gemm_scaled (gate/up)" if routed_scaled
                                  else "gateup_persistent"),
                       "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6,
                       "useful_tflops": gu_tflops}),
@@ -268,11 +272,13 @@ def main():
         "layer_bytes_per_step": layer_bytes,
         "rechecked_tokens": int(diag[0].item()),
     }
-    if ffn_ms is not None:
-        ffn_tflops = 2.0 * T * cfg.k * 3 * cfg.f * cfg.d / (ffn_ms / 1e3) / 1e12
-        result["routed_ffn"] = {"avg_us": ffn_ms * 1e3, "useful_tflops": ffn_tflops,
-                                "frac_of_fp8_peak": ffn_tflops / FP8_MFMA_PEAK_TFLOPS,
-                                "frac_of_mxfp4_peak": ffn_tflops / MXFP4_MFMA_PEAK_TFLOPS}
+    ffn_tflops = ffn_flops / (ffn_ms / 1e3) / 1e12
+    ffn_gbs = ffn_bytes / (ffn_ms / 1e3) / 1e9
+    result["routed_ffn"] = {"avg_us": ffn_ms * 1e3, "mxfp4_bytes": ffn_bytes,
+                            "mxfp4_gbs": ffn_gbs, "frac_of_hbm_peak": ffn_gbs / HBM_PEAK_GBS,
+                            "useful_tflops": ffn_tflops,
+                            "frac_of_fp8_peak": ffn_tflops / FP8_MFMA_PEAK_TFLOPS,
+                            "frac_of_mxfp4_peak": ffn_tflops / MXFP4_MFMA_PEAK_TFLOPS}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -139,14 +139,18 @@ size_t k3moe_workspace_bytes(const k3moe_shape* shape, int op);
  * weight of the pages' shard census).  Host-only helper. */
 uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols);
 
-/* Which path class a call with this shape takes.  K3MOE_PATH_MFMA (grouped
- * GEMMs on the scaled MXFP4 matrix-core instruction: the stored weight bytes
- * as one operand, the activations split into E4M3 passes with E8M0 block
- * scales as the other) when T >= 32, x is bf16, d % 512 == 0 and
- * f % 512 == 0; K3MOE_PATH_GEMV (one pass over each touched expert's weights
- * per token, fp32 dot products) otherwise.  Results of the two classes agree
- * within the stated tolerance, not bit for bit.  Returns K3MOE_PATH_GEMV for
- * an invalid shape. */
+/* Which path class a call with this shape takes.  K3MOE_PATH_MFMA (router,
+ * shared and routed experts as matrix-core GEMMs, the routed ones on the
+ * scaled MXFP4 instruction: the stored weight bytes as one operand, the
+ * activations split into E4M3 passes with E8M0 block scales as the other)
+ * when T >= 32, x is bf16, d % 512 == 0 and f % 512 == 0; K3MOE_PATH_GEMV (router and shared experts as GEMVs, one
+ * pass over the weights per token, fp32 dot products) otherwise.  The routed
+ * experts take the scaled matrix-core instruction in both classes whenever x
+ * is bf16, d % 512 == 0 and f % 512 == 0 (one token: one workgroup per
+ * active expert and output slice; more: the grouped GEMMs), so their outputs
+ * for a token are the same bits at every batch size; otherwise they are fp32
+ * GEMVs.  Results of the two classes agree within the stated tolerance, not
+ * bit for bit.  Returns K3MOE_PATH_GEMV for an invalid shape. */
 int k3moe_path_class(const k3moe_shape* shape);
 
 /* Router + top-k + softmax.
@@ -188,16 +192,19 @@ k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank*
  * gate/up + SiLU-GLU:  h, row q = silu(Wg x) * (Wu x) of expert e on token
  *   sorted_pair[q] / k (e as for k3moe_expert_ffn);
  * down:  y [T*k][d] fp32, row q = Wd_e h[q].
- * h is a buffer of [T*k][f] 32-bit words.  GEMV path class: fp32 values.
- * MFMA path class: each row is f/128 stages of 400 bytes, the value split
- * into 3 E4M3 passes with one E8M0 scale per pass and 32-feature block
- * (h ~ sum_p code_p * 2^(scale_p - 127)): 3 x 128 code bytes in feature
- * order, then byte 4p + b = scale of pass p, block b, then 4 unused bytes;
- * this is the operand form of the scaled matrix-core instruction.  A buffer
+ * h is a buffer of [T*k][f] 32-bit words.  Its form follows the routed
+ * experts' kernels, which take the scaled matrix-core instruction whenever x
+ * is bf16, d % 512 == 0 and f % 512 == 0 (at every T, in both path classes):
+ * then row q starts at byte q * (f/128) * 400 and is f/128 stages of 400
+ * bytes, the value split into 3 E4M3 passes with one E8M0 scale per pass and
+ * 32-feature block (h ~ sum_p code_p * 2^(scale_p - 127)): 3 x 128 code bytes
+ * in feature order, then byte 4p + b = scale of pass p, block b, then 4
+ * unused bytes; this is the operand form of the instruction.  Otherwise (fp32
+ * x, or other d, f) h holds fp32 values, row q at word q * f.  A buffer
  * written by k3moe_expert_gateup is meant for k3moe_expert_down with the same
  * shape.
  * Workspace (gate/up only): k3moe_workspace_bytes(shape, K3MOE_OP_EXPERT_GATEUP)
- * (0 in the GEMV class, where NULL is accepted): x in E4M3 passes. */
+ * (0 for the fp32 form, where NULL is accepted): x in E4M3 passes. */
 k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_bank* bank,
                                  const void* x, const int32_t* offsets,
                                  const int32_t* sorted_pair, float* h, void* workspace,

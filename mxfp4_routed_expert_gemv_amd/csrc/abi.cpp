@@ -140,7 +140,7 @@ ExpertWs carve_gateup(const k3moe_shape& s, void* ws, size_t* bytes) {
   Carver c(ws);
   ExpertWs r;
   r.h = nullptr;
-  r.xq = use_mfma(s) ? c.take<uint8_t>(xq_bytes(s)) : nullptr;
+  r.xq = routed_scaled(s) ? c.take<uint8_t>(xq_bytes(s)) : nullptr;
   if (bytes) *bytes = c.off;
   return r;
 }
@@ -149,7 +149,7 @@ ExpertWs carve_expert(const k3moe_shape& s, void* ws, size_t* bytes) {
   Carver c(ws);
   ExpertWs r;
   r.h = c.take<float>((size_t)s.T * s.k * s.f);
-  r.xq = use_mfma(s) ? c.take<uint8_t>(xq_bytes(s)) : nullptr;
+  r.xq = routed_scaled(s) ? c.take<uint8_t>(xq_bytes(s)) : nullptr;
   if (bytes) *bytes = c.off;
   return r;
 }

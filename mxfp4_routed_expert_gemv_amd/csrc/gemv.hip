@@ -82,19 +82,23 @@ __device__ __forceinline__ void stage_meta(const int32_t* __restrict__ offsets,
     f[u] = (tid * 4 + u < E && o[u + 1] > o[u]) ? 1 : 0;
     c += f[u];
   }
-  sums[tid] = c;
-  __syncthreads();
-  for (int dd = 1; dd < 256; dd <<= 1) {
-    const int add = tid >= dd ? sums[tid - dd] : 0;
-    __syncthreads();
-    sums[tid] += add;
-    __syncthreads();
+  // exclusive position of this thread's first active expert: a scan within
+  // each wave, then the totals of the lower waves
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
   }
-  int pos = sums[tid] - c;
+  if (lane == kWave - 1) sums[wv] = incl;
+  __syncthreads();
+  int pos = incl - c;
+  for (int w = 0; w < wv; ++w) pos += sums[w];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     if (f[u]) m.act[pos++] = tid * 4 + u;
-  if (tid == 255) m.n_act = sums[255];
+  if (tid == 255) m.n_act = pos;
   __syncthreads();
   if constexpr (NTOK > 0) {
     const int n = m.n_act;
@@ -821,7 +825,7 @@ hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& b
                                 const void* x, const int32_t* offsets,
                                 const int32_t* sorted_pair, float* h, uint8_t* xq,
                                 hipStream_t st) {
-  if (use_mfma(s)) return launch_gateup_scaled(s, bank, x, offsets, sorted_pair, h, xq, st);
+  if (routed_scaled(s)) return launch_gateup_scaled(s, bank, x, offsets, sorted_pair, h, xq, st);
   // One token: its row is staged in LDS (up to 32 KB).  Items loop over their
   // expert's tokens one at a time with the weight rows held in registers.
   const bool f32 = s.x_dtype == K3MOE_F32;
@@ -842,7 +846,7 @@ hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& b
 
 hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st) {
-  if (use_mfma(s)) return launch_down_scaled(s, bank, h, offsets, y, st);
+  if (routed_scaled(s)) return launch_down_scaled(s, bank, h, offsets, y, st);
   if (s.T == 1 && s.d % kDownT1Chunk == 0 && (size_t)s.f * 4 <= 32768) {
     const int chunks = s.d / kDownT1Chunk;
     int dev = 0, cus = 0;

@@ -75,6 +75,11 @@ __device__ __forceinline__ void dma16_raw(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
+// One byte per lane: lane i's byte lands in LDS dword i (zero-extended).
+__device__ __forceinline__ void dma1_raw(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // m-tile schedule for an NTH-thread workgroup: s_mt[e] = index of expert e's

@@ -15,6 +15,11 @@ namespace k3 {
 constexpr int64_t kMfmaMinT = 32;
 bool mfma_shape_ok(const k3moe_shape& s);
 inline bool use_mfma(const k3moe_shape& s) { return s.T >= kMfmaMinT && mfma_shape_ok(s); }
+// The routed experts run on the scaled-MXFP4 matrix-core instruction at any
+// token count when the shape allows it (one token included: the instruction
+// takes the stored E2M1 bytes as they are, which leaves the vector ALU free),
+// so a token's routed outputs do not depend on the batch size at all there.
+inline bool routed_scaled(const k3moe_shape& s) { return mfma_shape_ok(s); }
 // Tokens per chunk of the large-batch permute (one bit per token in LDS masks).
 int permute_chunk_tokens(int k);
 

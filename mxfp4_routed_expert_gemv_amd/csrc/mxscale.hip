@@ -98,20 +98,15 @@ constexpr uint32_t kNaNCode = 0x7Fu;
 constexpr uint32_t kAbsInf = 0x7F800000u;
 
 // ------------------------------------------------------------ x quantisation
-// x [T][d] bf16 -> xq [T][d/128][17 units of 16 bytes]: per stage, the codes
-// of pass 0 (128 bytes, element order), of pass 1, then one unit whose byte
-// 4p + b is the scale of pass p, block b (bytes 8..15 zero).  One thread per
-// 32-element block; the 4 threads of a stage are adjacent lanes.
-__global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
-                                               uint8_t* __restrict__ xq, int64_t nblk, int d) {
+// One 32-element block of bf16 x (64 bytes at src) -> its 2 pass code words
+// (pass p, elements 4i .. 4i+3 in word i, element order within the word)
+// and its first-pass scale byte.
+__device__ __forceinline__ uint32_t quant_xblock(const uint16_t* src, uint32_t (&packed)[2][8]) {
   constexpr int NP = 2;
-  const int64_t gb = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t b = gb < nblk ? gb : nblk - 1;   // lanes past the end redo the last block
-  const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
   uint32_t w[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint4 v = src[q];
+    const uint4 v = reinterpret_cast<const uint4*>(src)[q];
     w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
   }
   uint32_t mb = 0;
@@ -122,7 +117,6 @@ __global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
   }
   const bool bad = mb >= kAbsInf;
   const uint32_t sb0 = bad ? 127u + kPassStep * (NP - 1) : first_scale<NP>(mb);
-  uint32_t packed[NP][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -136,12 +130,15 @@ __global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
       for (int p = 0; p < NP; ++p) packed[p][i] |= (bad ? kNaNCode : c[p]) << (8 * e);
     }
   }
-  const int nst = d / kBK;
-  const int64_t nb_row = d / 32;
-  const int64_t t = b / nb_row;
-  const int j = (int)(b - t * nb_row), st = j >> 2, blk = j & 3;
-  uint8_t* row = xq + ((size_t)t * nst + st) * (NP * 128 + 16);
-  // scale unit: lane blk == 0 of the stage gathers its neighbours' bytes
+  return sb0;
+}
+
+// Writes one quantised block into a stage record (272 bytes: pass 0 codes,
+// pass 1 codes, scale unit) at `row`; lanes 4m .. 4m+3 hold the 4 blocks of
+// one stage (blk = lane % 4) and are all active.
+__device__ __forceinline__ void store_xblock(uint8_t* row, int blk, const uint32_t (&packed)[2][8],
+                                             uint32_t sb0, bool write) {
+  constexpr int NP = 2;
   uint32_t sc[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -152,7 +149,7 @@ __global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
     for (int q = 0; q < 4; ++q) v |= (__shfl(mine, (l0 + q) & 63, 64) & 0xFFu) << (8 * q);
     sc[p] = v;
   }
-  if (gb < nblk) {
+  if (write) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       uint4* dst = reinterpret_cast<uint4*>(row + p * 128 + blk * 32);
@@ -161,6 +158,23 @@ __global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
     }
     if (blk == 0) *reinterpret_cast<uint4*>(row + NP * 128) = uint4{sc[0], sc[1], 0u, 0u};
   }
+}
+
+// x [T][d] bf16 -> xq [T][d/128][17 units of 16 bytes]: per stage, the codes
+// of pass 0 (128 bytes, element order), of pass 1, then one unit whose byte
+// 4p + b is the scale of pass p, block b (bytes 8..15 zero).  One thread per
+// 32-element block; the 4 threads of a stage are adjacent lanes.
+__global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
+                                               uint8_t* __restrict__ xq, int64_t nblk, int d) {
+  const int64_t gb = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = gb < nblk ? gb : nblk - 1;   // lanes past the end redo the last block
+  uint32_t packed[2][8];
+  const uint32_t sb0 = quant_xblock(x + b * 32, packed);
+  const int nst = d / kBK;
+  const int64_t nb_row = d / 32;
+  const int64_t t = b / nb_row;
+  const int j = (int)(b - t * nb_row), st = j >> 2, blk = j & 3;
+  store_xblock(xq + ((size_t)t * nst + st) * (2 * 128 + 16), blk, packed, sb0, gb < nblk);
 }
 
 // ---------------------------------------------------------- grouped GEMMs
@@ -500,15 +514,394 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   wait_vmem<0>();
 }
 
+// -------------------------------------------------------------- one token
+// The decode batch of one token: each touched expert's weights are read once,
+// so the product is bound by how fast they stream, and decoding E2M1 on the
+// vector ALU (a quarter-rate conversion per two weights) costs about half the
+// streaming time.  Here the weights go to the matrix core as stored, as in
+// the grouped GEMM, and every wave streams only its own weight rows:
+//   * the wave's rows are NF fragments of 16 rows; their codes stream through
+//     a private LDS ring of D stages by LDS-DMA (issued D - 1 stages ahead,
+//     the wave's own wait counts, no barrier inside the stream); their scales
+//     for all stages sit in LDS (copied once, contiguous rows);
+//   * the activation row (x in 2 passes, quantised in the workgroup by the
+//     same code as quant_x; or the pair's h row in 3 passes) sits in LDS and
+//     every lane reads its A operand from it, so all 16 rows of the product
+//     are the token's (row 0 is stored); the raw row arrives by LDS-DMA
+//     while the workgroup scans the offsets, and x is quantised while the
+//     first weight stages fly;
+//   * per output, stages then passes then the instruction's own order, as in
+//     the grouped GEMM: the token's bits equal its row's bits there.
+// One workgroup (4 waves) per (active expert, 128 features) for gate/up and
+// per (active expert, 64 NF output rows) for down.  For one token an active
+// expert has exactly one pair, at sorted position j = its rank.
+
+// The expert whose range of sorted positions holds j, or -1.  Each thread
+// checks 4 consecutive experts per round with all its loads issued at once,
+// so the scan costs one memory latency for up to 1024 experts.
+__device__ int expert_at(const int32_t* __restrict__ offsets, int E, int j, int* s_e) {
+  const int t4 = threadIdx.x * 4;
+  int o[5];
+#pragma unroll
+  for (int u = 0; u < 5; ++u) o[u] = offsets[min(t4 + u, E)];
+  if (threadIdx.x == 0) *s_e = -1;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (t4 + u < E && o[u] <= j && o[u + 1] > j) *s_e = t4 + u;
+  for (int b = t4 + 4 * (int)blockDim.x; b < E; b += 4 * (int)blockDim.x) {
+#pragma unroll
+    for (int u = 0; u < 5; ++u) o[u] = offsets[min(b + u, E)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (b + u < E && o[u] <= j && o[u + 1] > j) *s_e = b + u;
+  }
+  __syncthreads();
+  return *s_e;
+}
+
+// A step of the one-token stream moves 128 bytes (two 128-element stages) of
+// each of the wave's rows; one copy instruction covers 8 rows (lane L: row
+// L / 8 of the 8, 16-byte unit (L % 8) ^ swz(row)).  A row's 128 bytes sit
+// at row * 128 in the slot, unit u at position u ^ swz(row): the 16 lanes
+// that read one block of 16 consecutive rows then hit 16 distinct 4-bank
+// groups of LDS.
+__device__ __forceinline__ int step_swz(int row) { return (row >> 1) & 7; }
+
+// LDS offset (within a step slot) of the block the lane feeds to the
+// instruction for stage q (0, 1) of the step: row rw, block 4q + lg.
+__device__ __forceinline__ int step_block_off(int rw, int q, int lg) {
+  return rw * 128 + (((4 * q + lg) ^ step_swz(rw)) << 4);
+}
+
+constexpr int kDn1Ring = 2, kGu1ScaleRing = 3;
+
+// Quantises one step of the token's row (stages 2t, 2t+1: 8 blocks of 32)
+// into two stage records at rec (the layout quant_x writes) with one wave:
+// lane l takes elements 4l .. 4l+3 of the step (8 bytes at src), the 8 lanes
+// of a block reduce its largest magnitude, and every element goes through
+// the same split as in quant_xblock, so the records equal quant_x's bit for
+// bit.
+__device__ __forceinline__ void quant_x_step(const uint8_t* src, uint8_t* rec, int lane) {
+  constexpr int NP = 2, REC = (NP * 8 + 1) * 16;
+  const uint2 raw = *reinterpret_cast<const uint2*>(src);
+  const uint32_t w[2] = {raw.x, raw.y};
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    mb = max(mb, (w[i] << 16) & 0x7FFFFFFFu);
+    mb = max(mb, w[i] & 0x7FFF0000u);
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o, 64));
+  const bool bad = mb >= kAbsInf;
+  const uint32_t sb0 = bad ? 127u + kPassStep * (NP - 1) : first_scale<NP>(mb);
+  uint32_t pk[NP] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t bits = e & 1 ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+    uint32_t c[NP];
+    split_passes<NP>(__uint_as_float(bits), sb0, c);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) pk[p] |= (bad ? kNaNCode : c[p]) << (8 * e);
+  }
+  uint8_t* r = rec + (lane >> 5) * REC;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) *reinterpret_cast<uint32_t*>(r + p * 128 + (lane & 31) * 4) = pk[p];
+  if ((lane & 7) == 0) {
+    const int blk = (lane >> 3) & 3;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) r[NP * 128 + 4 * p + blk] = (uint8_t)(sb0 - kPassStep * p);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gateup_1tok(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
+    uint8_t* __restrict__ hq, int d, int f, int E) {
+  constexpr int NF = 4, NP = 2, NPH = 3, UA = NP * 8 + 1, REC = UA * 16;
+  constexpr int ROWS = NF * 16, SLOT = ROWS * 128, NCI = ROWS / 8, SG = kGu1ScaleRing;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int s_e;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ln = lane & 15, lg = lane >> 4;
+  const int ngr = f / 128;
+  const int j = blockIdx.x / ngr, nt = blockIdx.x - j * ngr;
+  const int nst = d / kBK, nb = d / 32, nsp = nst / 2;
+  const size_t w_row = (size_t)d / 2, s_row = (size_t)nb;
+  const int x_pad = (2 * d + 1023) / 1024 * 1024;
+  uint8_t* s_x = lds;                                        // the bf16 row
+  uint8_t* s_xq = lds + x_pad + wv * 2 * (2 * REC);          // the wave's 2 step records
+  uint8_t* s_sc = lds + x_pad + 8 * (2 * REC) + wv * SG * 1024;
+  uint8_t* s_ring = lds + x_pad + 8 * (2 * REC) + 4 * SG * 1024 + wv * D * SLOT;
+  // the token's row by LDS-DMA (1 KB per instruction, the waves in turn),
+  // beside the offsets scan
+  {
+    const int units = d / 8;
+    const uint8_t* xs = reinterpret_cast<const uint8_t*>(x);
+    for (int u = wv; u * 64 < units; u += 4)
+      dma16_raw(xs + min(u * 64 + lane, units - 1) * 16, lds_addr(s_x) + (uint32_t)(u * 1024));
+  }
+  const int e = expert_at(offsets, E, j, &s_e);
+  wait_vmem<0>();
+  if (e < 0) return;
+  __syncthreads();
+  // the wave's rows: 0 .. 31 gate rows F + r, 32 .. 63 the up rows; fragment
+  // nf holds rows nf * 16 + [0, 16)
+  const int F = nt * 128 + wv * 32;
+  const size_t gate0 = (size_t)e * 2 * f + F, up0 = gate0 + f;
+  auto wrow = [&](int r) { return r < 32 ? gate0 + r : up0 + (r - 32); };
+  const uint8_t* cp[NCI];
+#pragma unroll
+  for (int i = 0; i < NCI; ++i) {
+    const int r = i * 8 + (lane >> 3);
+    cp[i] = wq + wrow(r) * w_row + (((lane & 7) ^ step_swz(r)) << 4);
+  }
+  // scales: one 16-byte unit (4 stages) per row and pair of steps, lane = row
+  const uint8_t* sp = wsc + wrow(lane) * s_row;
+  const uint32_t ring_l = lds_addr(s_ring), sc_l = lds_addr(s_sc);
+  auto issue = [&](int t) {
+    if (t >= nsp) return;
+    if ((t & 1) == 0) dma16_raw(sp + t * 8, sc_l + (uint32_t)(((t >> 1) % SG) * 1024));
+    const uint32_t slot = ring_l + (uint32_t)((t % D) * SLOT);
+#pragma unroll
+    for (int i = 0; i < NCI; ++i) dma16_raw(cp[i] + t * 128, slot + i * 1024);
+  };
+#pragma unroll
+  for (int t = 0; t < D - 1; ++t) issue(t);
+  // Each wave quantises the row itself, one step ahead of use, while its
+  // copies fly (spread over the stream, the quantisation costs the stream
+  // less than one pass over the whole row up front).
+  quant_x_step(s_x + lane * 8, s_xq, lane);
+
+  f32x4_t acc[NF];
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) acc[nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int t = 0; t < nsp; ++t) {
+    issue(t + D - 1);
+    if (t + 1 < nsp) quant_x_step(s_x + (t + 1) * 512 + lane * 8, s_xq + ((t + 1) & 1) * (2 * REC), lane);
+    // copies still allowed in flight: steps t+1 .. t+D-1, NCI each, plus a
+    // scale unit for each even one of them
+    if (t + D - 1 < nsp) {
+      static_assert(D >= 2 && D <= 4, "wait counts cover rings of 2 to 4 steps");
+      if constexpr (D == 3) wait_vmem<2 * NCI + 1>();
+      else if (t & 1) wait_vmem<(D - 1) * NCI + D / 2>();
+      else wait_vmem<(D - 1) * NCI + (D - 2) / 2>();
+    } else {
+      wait_vmem<0>();
+    }
+    const uint8_t* slot = s_ring + (t % D) * SLOT;
+    const uint8_t* sc = s_sc + ((t >> 1) % SG) * 1024;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      i32x8_t bq[NF];
+      int bs[NF];
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const int rw = nf * 16 + ln;
+        const uint4 c = *reinterpret_cast<const uint4*>(slot + step_block_off(rw, q, lg));
+        bq[nf] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        bs[nf] = sc[rw * 16 + ((t & 1) * 2 + q) * 4 + lg];
+      }
+      const uint8_t* arow = s_xq + (t & 1) * (2 * REC) + q * REC;
+      i32x8_t a[NP];
+      int as[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(arow + (p * 8 + lg) * 16);
+        const uint4 hi = *reinterpret_cast<const uint4*>(arow + (p * 8 + 4 + lg) * 16);
+        a[p] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        as[p] = arow[(UA - 1) * 16 + p * 4 + lg];
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+          acc[nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[p], bq[nf], acc[nf], 0, 4,
+                                                                     0, as[p], 0, bs[nf]);
+    }
+  }
+  // h of the token (row 0) for the wave's 32 features, in NPH passes, as in
+  // the grouped GEMM's epilogue
+  const size_t h_row = (size_t)(f / kBK) * (NPH * 128 + 16);
+  const int fb = F / 32, hst = fb >> 2, blk = fb & 3;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = lg * 4 + r;
+    const float h0 = silu_mul(acc[0][r], acc[2][r]);
+    const float h1 = silu_mul(acc[1][r], acc[3][r]);
+    uint32_t mb = max(__float_as_uint(h0) & 0x7FFFFFFFu, __float_as_uint(h1) & 0x7FFFFFFFu);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o, 64));
+    const bool bad = mb >= kAbsInf;
+    const uint32_t sb0 = bad ? 127u + kPassStep * (NPH - 1) : first_scale<NPH>(mb);
+    uint32_t c0[NPH], c1[NPH];
+    split_passes<NPH>(h0, sb0, c0);
+    split_passes<NPH>(h1, sb0, c1);
+    if (m == 0) {
+      uint8_t* hr = hq + (size_t)j * h_row + (size_t)hst * (NPH * 128 + 16);
+#pragma unroll
+      for (int p = 0; p < NPH; ++p) {
+        hr[p * 128 + blk * 32 + ln] = (uint8_t)(bad ? kNaNCode : c0[p]);
+        hr[p * 128 + blk * 32 + 16 + ln] = (uint8_t)(bad ? kNaNCode : c1[p]);
+      }
+      if (ln == 0) {
+#pragma unroll
+        for (int p = 0; p < NPH; ++p) hr[NPH * 128 + p * 4 + blk] = (uint8_t)(sb0 - kPassStep * p);
+      }
+    }
+  }
+}
+
+template <int NF, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void down_1tok(
+    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets, float* __restrict__ y,
+    int d, int f, int E, int cpe) {
+  constexpr int NP = 3, UA = NP * 8 + 1;
+  constexpr int ROWS = NF * 16, SLOT = ROWS * 128, NCI = ROWS / 8;
+  static_assert((D - 1) * NCI <= 63, "copies in flight within the wait counter");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int s_e;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ln = lane & 15, lg = lane >> 4;
+  const int j = blockIdx.x / cpe, c = blockIdx.x - j * cpe;
+  const int nst = f / kBK, nb = f / 32, nsp = nst / 2;
+  const size_t w_row = (size_t)f / 2, s_row = (size_t)nb;
+  const int h_row = nst * UA * 16;
+  const int h_pad = (h_row + 1023) / 1024 * 1024;
+  const int sreg = (ROWS * nb + 1023) / 1024 * 1024;   // scales of the wave's rows, padded
+  uint8_t* s_hq = lds;
+  uint8_t* s_sc = lds + h_pad + wv * sreg;
+  uint8_t* s_ring = lds + h_pad + 4 * sreg + wv * D * SLOT;
+  // the pair's h row by LDS-DMA (1 KB per instruction, the waves in turn),
+  // beside the offsets scan
+  {
+    const int units = h_row / 16;
+    const uint8_t* hs = hq + (size_t)j * h_row;
+    for (int u = wv; u * 64 < units; u += 4)
+      dma16_raw(hs + min(u * 64 + lane, units - 1) * 16, lds_addr(s_hq) + (uint32_t)(u * 1024));
+  }
+  const int e = expert_at(offsets, E, j, &s_e);
+  wait_vmem<0>();
+  if (e < 0) return;
+  __syncthreads();
+  const int o0 = c * (4 * ROWS) + wv * ROWS;   // the wave's first output row
+  const size_t row0 = (size_t)e * d + o0;
+  const uint8_t* cp[NCI];
+#pragma unroll
+  for (int i = 0; i < NCI; ++i) {
+    const int r = i * 8 + (lane >> 3);
+    cp[i] = wq + (row0 + r) * w_row + (((lane & 7) ^ step_swz(r)) << 4);
+  }
+  const uint32_t ring_l = lds_addr(s_ring);
+  auto issue = [&](int t) {
+    if (t >= nsp) return;
+    const uint32_t slot = ring_l + (uint32_t)((t % D) * SLOT);
+#pragma unroll
+    for (int i = 0; i < NCI; ++i) dma16_raw(cp[i] + t * 128, slot + i * 1024);
+  };
+  // scales of the wave's rows, 16-byte units (4 stages of a row) laid out
+  // [unit k][row]: the 16 rows a scale read spans then sit in 16 distinct
+  // 4-bank groups (row-major, 16 rows of nb bytes alias onto 4 groups)
+  {
+    const int ku = nb / 16, units = ROWS * ku;
+    const uint8_t* sbase = wsc + row0 * s_row;
+    for (int u = 0; u * 64 < units; ++u) {
+      const int P = min(u * 64 + lane, units - 1);
+      const int k = P / ROWS, rw = P - k * ROWS;
+      dma16_raw(sbase + (size_t)rw * s_row + k * 16, lds_addr(s_sc) + (uint32_t)(u * 1024));
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < D - 1; ++t) issue(t);
+
+  f32x4_t acc[NF];
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) acc[nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int t = 0; t < nsp; ++t) {
+    issue(t + D - 1);
+    if (t + D - 1 < nsp) wait_vmem<(D - 1) * NCI>();
+    else wait_vmem<0>();
+    const uint8_t* slot = s_ring + (t % D) * SLOT;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int st = 2 * t + q;
+      i32x8_t bq[NF];
+      int bs[NF];
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const int rw = nf * 16 + ln;
+        const uint4 cc = *reinterpret_cast<const uint4*>(slot + step_block_off(rw, q, lg));
+        bq[nf] = i32x8_t{(int)cc.x, (int)cc.y, (int)cc.z, (int)cc.w, 0, 0, 0, 0};
+        bs[nf] = s_sc[((st >> 2) * ROWS + rw) * 16 + (st & 3) * 4 + lg];
+      }
+      const uint8_t* arow = s_hq + st * (UA * 16);
+      i32x8_t a[NP];
+      int as[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(arow + (p * 8 + lg) * 16);
+        const uint4 hi = *reinterpret_cast<const uint4*>(arow + (p * 8 + 4 + lg) * 16);
+        a[p] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        as[p] = arow[(UA - 1) * 16 + p * 4 + lg];
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+          acc[nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[p], bq[nf], acc[nf], 0, 4,
+                                                                     0, as[p], 0, bs[nf]);
+    }
+  }
+  if (lg == 0) {   // row 0 of every fragment: lanes 0 .. 15, element 0
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) y[(size_t)j * d + o0 + nf * 16 + ln] = acc[nf][0];
+  }
+}
+
+// LDS bytes of the one-token kernels (0 when the shape does not fit).
+int gateup_1tok_lds(const k3moe_shape& s, int ring) {
+  const int n = (2 * s.d + 1023) / 1024 * 1024 + 8 * 2 * 272 + 4 * kGu1ScaleRing * 1024 +
+                4 * ring * 64 * 128;
+  return n <= 160 * 1024 - 256 ? n : 0;
+}
+// NF = fragments (16 output rows each) per wave.
+int down_1tok_lds(const k3moe_shape& s, int NF) {
+  const int nst = s.f / kBK, nb = s.f / 32;
+  const int sreg = (16 * NF * nb + 1023) / 1024 * 1024;
+  const int n = (nst * 25 * 16 + 1023) / 1024 * 1024 + 4 * sreg + 4 * kDn1Ring * NF * 16 * 128;
+  return n <= 160 * 1024 - 256 && s.d % (64 * NF) == 0 ? n : 0;
+}
+
 }  // namespace
 
 size_t xq_bytes(const k3moe_shape& s) {
   return (size_t)s.T * (size_t)(s.d / kBK) * (2 * 128 + 16);
 }
 
+
 hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
                                 const int32_t* offsets, const int32_t* sorted_pair, float* h,
                                 uint8_t* xq, hipStream_t st) {
+  if (s.T == 1) {
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint8_t* w = static_cast<const uint8_t*>(b.w13);
+    const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
+    uint8_t* hb = reinterpret_cast<uint8_t*>(h);
+    const unsigned g1 = (unsigned)(s.k * (s.f / 128));
+    if (const int lds = gateup_1tok_lds(s, 4)) {
+      gateup_1tok<4><<<g1, 256, lds, st>>>(xb, w, ws, offsets, hb, s.d, s.f, s.E);
+      return hipGetLastError();
+    }
+    if (const int lds = gateup_1tok_lds(s, 3)) {
+      gateup_1tok<3><<<g1, 256, lds, st>>>(xb, w, ws, offsets, hb, s.d, s.f, s.E);
+      return hipGetLastError();
+    }
+  }
   const int64_t nblk = s.T * (int64_t)(s.d / 32);
   quant_x<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(static_cast<const uint16_t*>(x), xq,
                                                           nblk, s.d);
@@ -536,6 +929,21 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
   const uint8_t* w = static_cast<const uint8_t*>(b.w2);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w2_scale);
+  if (s.T == 1) {
+    // 7 fragments per wave where d allows (d = 7168: 256 workgroups), else 8
+    if (const int lds = down_1tok_lds(s, 7)) {
+      const int cpe = s.d / (64 * 7);
+      down_1tok<7, kDn1Ring><<<(unsigned)(s.k * cpe), 256, lds, st>>>(hb, w, ws, offsets, y, s.d,
+                                                                      s.f, s.E, cpe);
+      return hipGetLastError();
+    }
+    if (const int lds = down_1tok_lds(s, 8)) {
+      const int cpe = s.d / (64 * 8);
+      down_1tok<8, kDn1Ring><<<(unsigned)(s.k * cpe), 256, lds, st>>>(hb, w, ws, offsets, y, s.d,
+                                                                      s.f, s.E, cpe);
+      return hipGetLastError();
+    }
+  }
   const dim3 g(mfma_grid() / 2);
 #define K3_SD(MF, NF, RA, RB)                                                                 \
   mx_gemm_scaled<MF, NF, RA, RB, true><<<g, dim3(256), 0, st>>>(hb, w, ws, offsets, nullptr, y, \

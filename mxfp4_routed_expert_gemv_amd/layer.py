@@ -87,8 +87,8 @@ class MoELayer:
                             self.workspace(s, OP_EXPERT_GATEUP), stream)
         return h[:T * self.k]
 
-    def expert_down(self, h, offsets, T, y=None, stream=None):
-        s = self.shape(T)
+    def expert_down(self, h, offsets, T, y=None, stream=None, x_dtype=torch.bfloat16):
+        s = self.shape(T, x_dtype)
         if y is None:
             y = torch.empty((max(T * self.k, 1), self.d), dtype=torch.float32, device=self._dev())
         k3moe_expert_down(s, self.routed_bank, h, offsets, y, stream)

@@ -64,9 +64,13 @@ def test_workspace_sizes():
     assert k3.k3moe_workspace_bytes(big_shape(T=0), k3.OP_LAYER) == 0
     assert k3.k3moe_workspace_bytes(big_shape(d=100), k3.OP_LAYER) == 0
     assert k3.k3moe_workspace_bytes(s, 99) == 0
-    # gate/up alone: nothing in the GEMV class; in the matrix-core class the
-    # activations in two E4M3 passes, 272 bytes per token and 128-element stage
-    assert k3.k3moe_workspace_bytes(s, k3.OP_EXPERT_GATEUP) == 0
+    # gate/up alone: the activations in two E4M3 passes, 272 bytes per token
+    # and 128-element stage, wherever the routed experts take the scaled
+    # matrix-core instruction (bf16 x, d % 512 == 0, f % 512 == 0, any T);
+    # nothing for the fp32 GEMV
+    assert k3.k3moe_workspace_bytes(s, k3.OP_EXPERT_GATEUP) == 15360
+    assert k3.k3moe_workspace_bytes(big_shape(T=1, x_dtype=k3.F32), k3.OP_EXPERT_GATEUP) == 0
+    assert k3.k3moe_workspace_bytes(big_shape(T=1, f=2048 + 256), k3.OP_EXPERT_GATEUP) == 0
     big = big_shape(T=4096)
     xq = 4096 * (7168 // 128) * 272
     assert k3.k3moe_workspace_bytes(big, k3.OP_EXPERT_GATEUP) == (xq + 255) // 256 * 256

@@ -152,6 +152,95 @@ def test_mfma_class_batch_composition():
         assert torch.equal(part, full[:n]), n
 
 
+def _e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3 (FN) code -> value: bias 7, subnormals m/8 * 2^-6, 0x7F/0xFF NaN."""
+    c = codes.astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def _decode_scaled_h(buf: np.ndarray, rows: int, f: int) -> np.ndarray:
+    """The gate/up buffer in its scaled form (rows of f/128 stages of 400
+    bytes: 3 passes of 128 E4M3 codes, then byte 4p + b = E8M0 scale of pass p,
+    32-feature block b) -> fp64 values [rows][f]."""
+    st = buf.view(np.uint8)[:rows * (f // 128) * 400].reshape(rows, f // 128, 400)
+    out = np.zeros((rows, f // 128, 128))
+    for p in range(3):
+        sc = st[:, :, 384 + 4 * p:388 + 4 * p].astype(np.float64)          # [rows][stages][4]
+        out += _e4m3(st[:, :, 128 * p:128 * (p + 1)]) * np.repeat(2.0 ** (sc - 127), 32, axis=2)
+    return out.reshape(rows, f)
+
+
+@pytest.mark.parametrize("d,T", [(512, 1), (512, 2), (512, 5), (512, 31), (512, 40),
+                                 (3584, 1), (3584, 3)])
+def test_scaled_routed_experts_any_batch(orc, d, T):
+    """Routed experts on the scaled matrix-core instruction below and above 32
+    tokens (one token: the one-token kernels, with 8 down fragments per wave
+    at d = 512 and 7 at d = 3584; more: the grouped GEMMs): the layer against
+    the oracle, the gate/up half's h (decoded from its documented form)
+    against the oracle's h, and gate/up then down equal to the fused call bit
+    for bit."""
+    require_gpu()
+    from mxfp4_routed_expert_gemv_amd import PATH_GEMV, PATH_MFMA
+    cfg = gen.configs.LayerConfig(**{**MED.__dict__, "T": T, "d": d,
+                                     "name": f"medium_d{d}_T{T}"})
+    log(f"case {cfg.name}")
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    assert L.path_class(T) == (PATH_MFMA if T >= 32 else PATH_GEMV)
+    r = L.staged(wl.x)
+    x_host = gen.x(cfg)
+    ref = _full_oracle(cfg, orc, x_host)
+    _compare_full(r, ref, cfg, "f32")
+    out = L(wl.x)
+    h = L.expert_gateup(wl.x, r["offsets"], r["sorted_pair"])
+    y2 = L.expert_down(h, r["offsets"], T)
+    torch.cuda.synchronize()
+    assert torch.equal(out, r["out"])
+    assert torch.equal(y2, r["y_perm"])
+    # h of every pair against the oracle's silu(g) * u
+    P = T * cfg.k
+    h_gpu = _decode_scaled_h(to_np(h).reshape(-1), P, cfg.f)
+    bank = gen.routed_bank(cfg)
+    sp = ref["sorted_pair"]
+    offs = ref["offsets"]
+    h_ref = np.zeros((P, cfg.f))
+    for e in range(cfg.E):
+        if offs[e + 1] > offs[e]:
+            toks = sp[offs[e]:offs[e + 1]] // cfg.k
+            _, he = orc.mxfp4_ffn({kk: v[e] for kk, v in bank.items()},
+                                  oracle.to_f64(x_host[toks]), want_h=True)
+            h_ref[offs[e]:offs[e + 1]] = he
+    assert_close(h_gpu, h_ref, "h (scaled form)")
+
+
+def test_routed_bits_do_not_depend_on_batch_size():
+    """A token's routed expert outputs are the same bits alone (one-token
+    kernels), in small batches (grouped GEMMs, GEMV class) and in large ones
+    (matrix-core class)."""
+    require_gpu()
+    cfg = MED.with_tokens(200)
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    full = L.staged(wl.x)
+
+    def rows(r, t):
+        pp = to_np(r["pair_pos"])
+        return to_np(r["y_perm"])[pp[t * cfg.k:(t + 1) * cfg.k]]
+    for n in (1, 2, 7, 31, 64):
+        part = L.staged(wl.x[:n].contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(part["idx"]), to_np(full["idx"])[:n])
+        for t in range(n):
+            assert np.array_equal(rows(part, t), rows(full, t)), (n, t)
+    for t in (5, 77, 199):   # single tokens from inside the batch
+        one = L.staged(wl.x[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(rows(one, 0), rows(full, t)), t
+
+
 def test_hand_worked_two_experts(orc):
     """The closed-form 1-token / 2-expert layer (hand-worked fixture), both
     nibble positions, through the C ABI."""
@@ -359,6 +448,16 @@ def test_decode_b64(big, orc):
     full = L(x)
     torch.cuda.synchronize()
     assert torch.equal(part.view(torch.int16), full[:32].view(torch.int16))
+    # the routed outputs of single tokens (one-token kernels) equal their rows
+    # of the batch (grouped GEMMs), bit for bit
+    k = gen.get("decode_b64").k
+    pp = to_np(r["pair_pos"])
+    y = to_np(r["y_perm"])
+    for t in (0, 63):
+        one = L.staged(x[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(one["idx"])[0], to_np(r["idx"])[t])
+        assert np.array_equal(to_np(one["y_perm"]), y[pp[t * k:(t + 1) * k]]), t
 
 
 def test_prefill_4096(big, orc):
