@@ -53,26 +53,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 constexpr int kBK = 128;        // contraction elements per stage
 constexpr int kPassStep = 5;    // scale exponent step between passes
 
-// E4M3 (OCP, bias 7, no infinities) encoding of v, |v| <= 256, rounded to
-// nearest even; q receives the value the code stands for.
-__device__ __forceinline__ uint32_t e4m3_rne(float v, float& q) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const uint32_t ua = __float_as_uint(v) & 0x7FFFFFFFu;
-  uint32_t code;
-  float qa;
-  if (ua < 0x3C800000u) {   // below 2^-6: subnormal codes, steps of 2^-9
-    const float n = __builtin_rintf(__uint_as_float(ua) * 512.0f);
-    code = (uint32_t)n;     // 8 is the smallest normal, 2^-6
-    qa = n * (1.0f / 512.0f);
-  } else {
-    const uint32_t ur = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) & 0xFFF00000u;
-    code = (((ur >> 23) - 120u) << 3) | ((ur >> 20) & 7u);
-    qa = __uint_as_float(ur);
-  }
-  q = __uint_as_float(__float_as_uint(qa) | (sign << 24));
-  return code | sign;
-}
-
 // First-pass scale byte of a block from the bits of its largest magnitude
 // (finite): puts that magnitude in [2^7, 2^8); blocks below 2^-110 keep the
 // smallest byte for which every pass's byte is >= 0.
@@ -82,15 +62,48 @@ __device__ __forceinline__ uint32_t first_scale(uint32_t max_bits) {
   return (uint32_t)(s > kPassStep * (NP - 1) ? s : kPassStep * (NP - 1));
 }
 
-// The NP pass codes of one value of a block with first scale byte sb0.
+// The pass codes of values of a block with first scale byte sb0: v = a /
+// 2^(sb0 - 127) (exact), then per pass the E4M3 code of v rounded to nearest
+// even and v = (v - its value) * 32.  Every |v| met here is at most 256
+// (the first pass's largest is below 2^8, a remainder is at most half a
+// rounding step of 2^4, times 32), where the hardware conversion
+// (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even) and its inverse equal
+// a software encoder bit for bit (checked exhaustively on gfx950 over every
+// such float).
+// Four bf16 values (w0 low, w0 high, w1 low, w1 high): per pass one word of
+// 4 codes in element order.
 template <int NP>
-__device__ __forceinline__ void split_passes(float a, uint32_t sb0, uint32_t (&code)[NP]) {
-  float v = a * __uint_as_float((254u - sb0) << 23);   // a / 2^(sb0 - 127), exact
+__device__ __forceinline__ void split4(uint32_t w0, uint32_t w1, uint32_t sb0,
+                                       uint32_t (&code)[NP]) {
+  const float m = __uint_as_float((254u - sb0) << 23);
+  float v[4] = {__uint_as_float(w0 << 16) * m, __uint_as_float(w0 & 0xFFFF0000u) * m,
+                __uint_as_float(w1 << 16) * m, __uint_as_float(w1 & 0xFFFF0000u) * m};
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    float q;
-    code[p] = e4m3_rne(v, q);
-    v = (v - q) * 32.0f;
+    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
+    code[p] = (uint32_t)pk;
+    if (p + 1 < NP) {
+      v[0] = (v[0] - __builtin_amdgcn_cvt_f32_fp8(pk, 0)) * 32.0f;
+      v[1] = (v[1] - __builtin_amdgcn_cvt_f32_fp8(pk, 1)) * 32.0f;
+      v[2] = (v[2] - __builtin_amdgcn_cvt_f32_fp8(pk, 2)) * 32.0f;
+      v[3] = (v[3] - __builtin_amdgcn_cvt_f32_fp8(pk, 3)) * 32.0f;
+    }
+  }
+}
+// Two fp32 values: per pass their codes in the low two bytes (a0 first).
+template <int NP>
+__device__ __forceinline__ void split2(float a0, float a1, uint32_t sb0, uint32_t (&code)[NP]) {
+  const float m = __uint_as_float((254u - sb0) << 23);
+  float v0 = a0 * m, v1 = a1 * m;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    code[p] = (uint32_t)pk & 0xFFFFu;
+    if (p + 1 < NP) {
+      v0 = (v0 - __builtin_amdgcn_cvt_f32_fp8(pk, 0)) * 32.0f;
+      v1 = (v1 - __builtin_amdgcn_cvt_f32_fp8(pk, 1)) * 32.0f;
+    }
   }
 }
 
@@ -119,16 +132,10 @@ __device__ __forceinline__ uint32_t quant_xblock(const uint16_t* src, uint32_t (
   const uint32_t sb0 = bad ? 127u + kPassStep * (NP - 1) : first_scale<NP>(mb);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    uint32_t c[NP];
+    split4<NP>(w[2 * i], w[2 * i + 1], sb0, c);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) packed[p][i] = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t bits = e & 1 ? (w[2 * i + (e >> 1)] & 0xFFFF0000u) : (w[2 * i + (e >> 1)] << 16);
-      uint32_t c[NP];
-      split_passes<NP>(__uint_as_float(bits), sb0, c);
-#pragma unroll
-      for (int p = 0; p < NP; ++p) packed[p][i] |= (bad ? kNaNCode : c[p]) << (8 * e);
-    }
+    for (int p = 0; p < NP; ++p) packed[p][i] = bad ? kNaNCode * 0x01010101u : c[p];
   }
   return sb0;
 }
@@ -475,15 +482,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int o = 1; o < 16; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o, 64));
             const bool bad = mb >= kAbsInf;
             const uint32_t sb0 = bad ? 127u + kPassStep * (NPH - 1) : first_scale<NPH>(mb);
-            uint32_t c0[NPH], c1[NPH];
-            split_passes<NPH>(h0, sb0, c0);
-            split_passes<NPH>(h1, sb0, c1);
+            uint32_t c01[NPH];
+            split2<NPH>(h0, h1, sb0, c01);
             if (m < rows) {
               uint8_t* hr = hq + (size_t)(row0 + m) * h_row + (size_t)hst * (NPH * 128 + 16);
 #pragma unroll
               for (int p = 0; p < NPH; ++p) {
-                hr[p * 128 + blk * 32 + ln] = (uint8_t)(bad ? kNaNCode : c0[p]);
-                hr[p * 128 + blk * 32 + 16 + ln] = (uint8_t)(bad ? kNaNCode : c1[p]);
+                hr[p * 128 + blk * 32 + ln] = (uint8_t)(bad ? kNaNCode : c01[p]);
+                hr[p * 128 + blk * 32 + 16 + ln] = (uint8_t)(bad ? kNaNCode : c01[p] >> 8);
               }
               if (ln == 0) {
 #pragma unroll
@@ -596,15 +602,10 @@ __device__ __forceinline__ void quant_x_step(const uint8_t* src, uint8_t* rec, i
   for (int o = 1; o < 8; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o, 64));
   const bool bad = mb >= kAbsInf;
   const uint32_t sb0 = bad ? 127u + kPassStep * (NP - 1) : first_scale<NP>(mb);
-  uint32_t pk[NP] = {0u, 0u};
+  uint32_t pk[NP];
+  split4<NP>(w[0], w[1], sb0, pk);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t bits = e & 1 ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
-    uint32_t c[NP];
-    split_passes<NP>(__uint_as_float(bits), sb0, c);
-#pragma unroll
-    for (int p = 0; p < NP; ++p) pk[p] |= (bad ? kNaNCode : c[p]) << (8 * e);
-  }
+  for (int p = 0; p < NP; ++p) pk[p] = bad ? kNaNCode * 0x01010101u : pk[p];
   uint8_t* r = rec + (lane >> 5) * REC;
 #pragma unroll
   for (int p = 0; p < NP; ++p) *reinterpret_cast<uint32_t*>(r + p * 128 + (lane & 31) * 4) = pk[p];
@@ -737,15 +738,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int o = 1; o < 16; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o, 64));
     const bool bad = mb >= kAbsInf;
     const uint32_t sb0 = bad ? 127u + kPassStep * (NPH - 1) : first_scale<NPH>(mb);
-    uint32_t c0[NPH], c1[NPH];
-    split_passes<NPH>(h0, sb0, c0);
-    split_passes<NPH>(h1, sb0, c1);
+    uint32_t c01[NPH];
+    split2<NPH>(h0, h1, sb0, c01);
     if (m == 0) {
       uint8_t* hr = hq + (size_t)j * h_row + (size_t)hst * (NPH * 128 + 16);
 #pragma unroll
       for (int p = 0; p < NPH; ++p) {
-        hr[p * 128 + blk * 32 + ln] = (uint8_t)(bad ? kNaNCode : c0[p]);
-        hr[p * 128 + blk * 32 + 16 + ln] = (uint8_t)(bad ? kNaNCode : c1[p]);
+        hr[p * 128 + blk * 32 + ln] = (uint8_t)(bad ? kNaNCode : c01[p]);
+        hr[p * 128 + blk * 32 + 16 + ln] = (uint8_t)(bad ? kNaNCode : c01[p] >> 8);
       }
       if (ln == 0) {
 #pragma unroll

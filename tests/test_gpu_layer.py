@@ -216,6 +216,69 @@ def test_scaled_routed_experts_any_batch(orc, d, T):
     assert_close(h_gpu, h_ref, "h (scaled form)")
 
 
+def _e4m3_rne(v: np.ndarray):
+    """OCP E4M3 code of each value rounded to nearest even (|v| <= 448), and
+    the value the code stands for; written from the format's definition."""
+    a = np.abs(v)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    sub = a < 2.0 ** -6
+    n = np.round(a * 512.0)                                   # half to even
+    e = np.floor(np.log2(np.where(sub, 1.0, a)))
+    mant = np.round((a / 2.0 ** e - 1.0) * 8.0)
+    e = np.where(mant == 8, e + 1, e)
+    mant = np.where(mant == 8, 0, mant)
+    code = np.where(sub, n, (e + 7) * 8 + mant).astype(np.int64)
+    q = np.where(sub, n / 512.0, (1.0 + mant / 8.0) * 2.0 ** e)
+    return code | sign, np.where(np.signbit(v), -q, q)
+
+
+def test_activation_split_is_exact_rne():
+    """The batched gate/up first writes x as 2 E4M3 passes per 128-element
+    stage (272-byte records in the workspace): every code and scale byte equals
+    the split written out here from its definition (scale so that the block's
+    largest magnitude lies in [2^7, 2^8), round to nearest even, remainder
+    times 32), and the two passes give back bf16 x exactly for every element
+    down to 2^-15 of its block's largest magnitude."""
+    require_gpu()
+    import ctypes
+    from mxfp4_routed_expert_gemv_amd import OP_EXPERT_GATEUP, k3moe_expert_gateup
+    cfg = MED.with_tokens(5)
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    T, d = cfg.T, cfg.d
+    idx, _, _ = L.route(wl.x)
+    _, offsets, sp, _ = L.permute(idx)
+    s = L.shape(T, wl.x.dtype)
+    ws = L.workspace(s, OP_EXPERT_GATEUP)
+    h = torch.empty((T * cfg.k, cfg.f), dtype=torch.float32, device=wl.x.device)
+    k3moe_expert_gateup(s, L.routed_bank, wl.x, offsets, sp, h, ws, None)
+    torch.cuda.synchronize()
+    xq = to_np(ws)[:T * (d // 128) * 272].reshape(T, d // 128, 272)
+    xb = to_np(wl.x.view(torch.int16)).astype(np.int64) & 0xFFFF
+    bits = (xb << 16).astype(np.uint32)
+    x64 = bits.view(np.float32).astype(np.float64).reshape(T, d // 32, 32)
+    mb = (bits & 0x7FFFFFFF).reshape(T, d // 32, 32).max(axis=2).astype(np.int64)
+    sb0 = np.maximum((mb >> 23) - 7, 5)
+    v = x64 * 2.0 ** (127 - sb0)[..., None]
+    v0 = v.copy()
+    back = np.zeros_like(v)
+    for p in range(2):
+        code, q = _e4m3_rne(v)
+        got = xq[:, :, 128 * p:128 * (p + 1)].reshape(T, d // 32, 32)
+        assert np.array_equal(got, code), f"pass {p} codes"
+        back += q * 2.0 ** (-5 * p)
+        v = (v - q) * 32.0
+    scales = xq[:, :, 256:264].reshape(T, d // 128, 2, 4).astype(np.int64)
+    want = np.stack([sb0.reshape(T, d // 128, 4) - 5 * p for p in range(2)], axis=2)
+    assert np.array_equal(scales, want), "scale bytes"
+    assert np.all(xq[:, :, 264:272] == 0)
+    # exact down to 2^-7 in the scaled units (2^-15 of the block's largest
+    # magnitude); below, within half the second pass's finest step
+    err = np.abs(back - v0)
+    assert np.all(err[np.abs(v0) >= 2.0 ** -7] == 0), "2 passes are not exact"
+    assert np.all(err <= 2.0 ** -15)
+
+
 def test_routed_bits_do_not_depend_on_batch_size():
     """A token's routed expert outputs are the same bits alone (one-token
     kernels), in small batches (grouped GEMMs, GEMV class) and in large ones
