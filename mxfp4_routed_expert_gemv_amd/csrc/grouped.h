@@ -75,6 +75,12 @@ __device__ __forceinline__ void dma16_raw(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
+// The same copy for data read exactly once (a weight stream): non-temporal,
+// so it does not push reusable lines (scales, activations) out of the L2.
+__device__ __forceinline__ void dma16_raw_nt(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
 // One byte per lane: lane i's byte lands in LDS dword i (zero-extended).
 __device__ __forceinline__ void dma1_raw(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, off"

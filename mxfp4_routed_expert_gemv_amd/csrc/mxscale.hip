@@ -666,7 +666,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if ((t & 1) == 0) dma16_raw(sp + t * 8, sc_l + (uint32_t)(((t >> 1) % SG) * 1024));
     const uint32_t slot = ring_l + (uint32_t)((t % D) * SLOT);
 #pragma unroll
-    for (int i = 0; i < NCI; ++i) dma16_raw(cp[i] + t * 128, slot + i * 1024);
+    for (int i = 0; i < NCI; ++i) dma16_raw_nt(cp[i] + t * 128, slot + i * 1024);
   };
 #pragma unroll
   for (int t = 0; t < D - 1; ++t) issue(t);
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (t >= nsp) return;
     const uint32_t slot = ring_l + (uint32_t)((t % D) * SLOT);
 #pragma unroll
-    for (int i = 0; i < NCI; ++i) dma16_raw(cp[i] + t * 128, slot + i * 1024);
+    for (int i = 0; i < NCI; ++i) dma16_raw_nt(cp[i] + t * 128, slot + i * 1024);
   };
   // scales of the wave's rows, 16-byte units (4 stages of a row) laid out
   // [unit k][row]: the 16 rows a scale read spans then sit in 16 distinct
