@@ -406,6 +406,70 @@ def test_zero_weight_expert_contributes_nothing(orc):
     assert_close(out, ref["out"], "out with a NaN expert at weight 0")
 
 
+@pytest.mark.parametrize("T", [1, 40])
+def test_scaled_nan_expert_at_weight_zero(orc, T):
+    """On the scaled path (one-token kernels at T = 1, grouped GEMMs at 40) an
+    expert with NaN scales (byte 255) whose routing weight underflows to 0
+    leaves every output finite and equal to the oracle's."""
+    require_gpu()
+    cfg = MED.with_tokens(T)
+    x = gen.x(cfg).copy()
+    x[:, 0] = gen.f64_to_bf16_bits(1.0)
+    wr = gen.router(cfg).copy()
+    wr[:, 0] = 0
+    wr[3, 0] = gen.f64_to_bf16_bits(2000.0)
+    wr[9, 0] = gen.f64_to_bf16_bits(1000.0)
+    bank = gen.routed_bank(cfg)
+    bank["w2_scale"][9] = 255
+    bank["w13_scale"][9] = 255
+    sh = gen.shared_bank(cfg)
+    ref = orc.layer(oracle.to_f64(x), wr, lambda e: {k: v[e] for k, v in bank.items()}, sh,
+                    cfg.k, cfg.E)
+    assert np.all(ref["counts"][[3, 9]] == T)   # both experts chosen by every token
+    from mxfp4_routed_expert_gemv_amd.layer import MoELayer
+    dev = "cuda"
+    L = MoELayer(torch.from_numpy(wr.view(np.int16)).to(dev).view(torch.bfloat16),
+                 {k: torch.from_numpy(v).to(dev) for k, v in bank.items()},
+                 {k: torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
+                  for k, v in sh.items()}, cfg.k, out_dtype=torch.float32)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    r = L.staged(xd)
+    out = L(xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(r["idx"]), ref["idx"])
+    y = to_np(r["y_perm"])
+    o9 = ref["offsets"]
+    assert np.all(np.isnan(y[o9[9]:o9[10]])), "the NaN expert's own rows are NaN"
+    assert np.all(np.isfinite(to_np(out)))
+    assert torch.equal(out, r["out"])
+    assert_close(to_np(out), ref["out"], "out with a NaN expert at weight 0")
+
+
+def test_scaled_nonfinite_activation_stays_in_its_token():
+    """An infinite activation element on the scaled path turns its block's
+    codes into E4M3 NaN: the token's own routed rows become NaN, and every
+    other token's outputs keep their bits."""
+    require_gpu()
+    cfg = MED.with_tokens(40)
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    base = L.staged(wl.x)
+    x = wl.x.clone()
+    x[7, 100] = float("inf")
+    r = L.staged(x)
+    torch.cuda.synchronize()
+    k = cfg.k
+    pp = to_np(r["pair_pos"])
+    y = to_np(r["y_perm"])
+    assert np.all(~np.isfinite(y[pp[7 * k:8 * k]])), "token 7's routed rows"
+    others = np.array([t for t in range(cfg.T) if t != 7])
+    assert np.array_equal(to_np(r["out"])[others], to_np(base["out"])[others])
+    # the same token alone (one-token kernels)
+    one = L.staged(x[7:8].contiguous())
+    torch.cuda.synchronize()
+    assert np.all(~np.isfinite(to_np(one["y_perm"])))
+
+
 def test_nonfinite_logits_are_counted():
     require_gpu()
     cfg = gen.get("tiny")
