@@ -53,6 +53,22 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 constexpr int kBK = 128;        // contraction elements per stage
 constexpr int kPassStep = 5;    // scale exponent step between passes
 
+// A step of a weight stream that moves 128 bytes (two 128-element stages) of
+// each row at once (the one-token kernels; the grouped GEMMs with pair-wide
+// weight copies): one copy instruction covers 8 rows (lane L: row
+// L / 8 of the 8, 16-byte unit (L % 8) ^ swz(row)).  A row's 128 bytes sit
+// at row * 128 in the slot, unit u at position u ^ swz(row): the 16 lanes
+// that read one block of 16 consecutive rows then hit 16 distinct 4-bank
+// groups of LDS.
+__device__ __forceinline__ int step_swz(int row) { return (row >> 1) & 7; }
+
+// LDS offset (within a step slot) of the block the lane feeds to the
+// instruction for stage q (0, 1) of the step: row rw, block 4q + lg.
+__device__ __forceinline__ int step_block_off(int rw, int q, int lg) {
+  return rw * 128 + (((4 * q + lg) ^ step_swz(rw)) << 4);
+}
+
+
 // First-pass scale byte of a block from the bits of its largest magnitude
 // (finite): puts that magnitude in [2^7, 2^8); blocks below 2^-110 keep the
 // smallest byte for which every pass's byte is >= 0.
@@ -185,6 +201,29 @@ __global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
 }
 
 // ---------------------------------------------------------- grouped GEMMs
+// With pair-wide weight copies (PB), the copies a wave issues after the last
+// copy that a stage needs, in the steady state, for either parity of the
+// stage: per stage the wave issues NAW activation copies, then on every other
+// stage nbc2 weight-code copies (two stages of its rows, 128 bytes each),
+// then one scale copy.
+__host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2) {
+  int best = 1 << 30;
+  for (int par = 0; par < 2; ++par) {
+    const int g = 2 * (RA + RB) + par;   // the awaited stage (any with full history)
+    int na = 0, nb = 1;
+    // A(g) was issued first in iteration g - RA + 1
+    na += (((g - RA + 1) + RB - 1) % 2 == 0 ? nbc2 : 0) + 1;
+    for (int i = g - RA + 2; i <= g - 1; ++i) na += NAW + ((i + RB - 1) % 2 == 0 ? nbc2 : 0) + 1;
+    // the weight pair of stage g was issued in iteration 2 (g / 2) - RB + 1,
+    // followed by that iteration's scale copy
+    for (int i = 2 * (g / 2) - RB + 2; i <= g - 1; ++i)
+      nb += NAW + ((i + RB - 1) % 2 == 0 ? nbc2 : 0) + 1;
+    const int m = na < nb ? na : nb;
+    best = m < best ? m : best;
+  }
+  return best;
+}
+
 // One workgroup of 4 waves per CU, one wave per SIMD (so each wave may hold
 // 512 registers).  Every wave both copies and computes:
 //   * item = (m-tile of BM = 16 MF expert-sorted rows, n-tile of 4 * 16 NF
@@ -220,7 +259,11 @@ __global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
 //   nt * 64 NF + w * 16 NF + [0, 16 NF); y fp32.
 // A wave computes only the m-blocks (16 rows) that hold rows of the tile,
 // and reads the next m-block's A fragments before issuing this one's MFMAs.
-template <int MF, int NF, int RA, int RB, bool DOWN>
+// PB (pair-wide weight copies): every other stage, each weight row's next 128
+// bytes (two stages) are copied at once, non-temporally, into a ring of
+// (RB + 2) / 2 two-stage slots laid out as the one-token stream's steps:
+// whole 128-byte lines per copy, each read once.
+template <int MF, int NF, int RA, int RB, bool DOWN, bool PB = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_gemm_scaled(
     const uint8_t* __restrict__ a_src, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
@@ -249,13 +292,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // awaited, A(g) was followed by B(g + RB - RA) and the copies of RA - 2
   // later stages, B(g) by the copies of RB - 2 later stages.
   constexpr int NEWER_A = NBW + (RA - 2) * (NAW + NBW), NEWER_B = (RB - 2) * (NAW + NBW);
-  constexpr int NEWER = NEWER_A < NEWER_B ? NEWER_A : NEWER_B;
+  constexpr int RBP = (RB + 2) / 2;             // PB: two-stage weight slots
+  constexpr int B_SLOT_P = BROWS * 128;
+  constexpr int NBC = PB ? 2 * NBCW : NBCW;     // weight-code copies per wave per copy round
+  constexpr int NEWER = PB ? newer_pairs(RA, RB, NAW, NBC)
+                           : (NEWER_A < NEWER_B ? NEWER_A : NEWER_B);
   constexpr int RMAX = RA > RB ? RA : RB;
   static_assert(NF == 4 || NF == 8, "4 or 8 fragments per wave");
   static_assert(RA >= 2 && RB >= 2, "rings need two slots");
-  static_assert((RA - 1) * NAW + (RB - 1) * NBW <= 63, "memory counter range");
+  static_assert(PB ? (RA - 1) * NAW + (RB / 2 + 1) * NBC + (RB - 1) <= 63
+                   : (RA - 1) * NAW + (RB - 1) * NBW <= 63, "memory counter range");
   __shared__ __attribute__((aligned(16))) uint8_t sA[RA * A_SLOT];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[RB * B_SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[PB ? RBP * B_SLOT_P : RB * B_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sS[SG * S_SLOT];
   __shared__ int s_mt[kMaxE + 1];
   __shared__ int s_wave[4];
@@ -285,7 +333,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   int s_e = 0, s_nt = 0;
   const uint8_t* ap[NAW];
-  const uint8_t* bp[NBCW];
+  const uint8_t* bp[NBC];
   // weight row of local row r of an n-tile
   auto grow = [&](int nt, int r) -> size_t {
     if (DOWN) return (size_t)nt * BROWS + r;
@@ -313,10 +361,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
     const uint8_t* wbase = wq + (size_t)e * e_rows * w_row;
 #pragma unroll
-    for (int q = 0; q < NBCW; ++q) {
-      const int r = (wv * (NBCW * 64) + q * 64 + lane) >> 2;
-      const int b = (lane & 3) ^ ((r >> 2) & 3);
-      bp[q] = wbase + grow(nt, r) * w_row + b * 16;
+    for (int q = 0; q < NBC; ++q) {
+      if constexpr (PB) {   // 8 rows per copy, 128 bytes each
+        const int r = (wv * (NBC * 64) + q * 64 + lane) >> 3;
+        bp[q] = wbase + grow(nt, r) * w_row + (((lane & 7) ^ step_swz(r)) << 4);
+      } else {
+        const int r = (wv * (NBCW * 64) + q * 64 + lane) >> 2;
+        const int b = (lane & 3) ^ ((r >> 2) & 3);
+        bp[q] = wbase + grow(nt, r) * w_row + b * 16;
+      }
     }
   };
   auto s_setup = [&]() {
@@ -351,10 +404,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   auto issue_b = [&](int g) {
     if (b_it >= it_end) return;
-    const uint32_t base = sB_lds + (uint32_t)((g % RB) * B_SLOT);
+    if constexpr (PB) {
+      if ((b_st & 1) == 0) {
+        const uint32_t base = sB_lds + (uint32_t)(((g >> 1) % RBP) * B_SLOT_P);
 #pragma unroll
-    for (int q = 0; q < NBCW; ++q)
-      dma16_raw(bp[q] + b_st * (kBK / 2), base + (wv * (NBCW * 64) + q * 64) * 16);
+        for (int q = 0; q < NBC; ++q)
+          dma16_raw_nt(bp[q] + (b_st >> 1) * kBK, base + (wv * (NBC * 64) + q * 64) * 16);
+      }
+    } else {
+      const uint32_t base = sB_lds + (uint32_t)((g % RB) * B_SLOT);
+#pragma unroll
+      for (int q = 0; q < NBCW; ++q)
+        dma16_raw(bp[q] + b_st * (kBK / 2), base + (wv * (NBCW * 64) + q * 64) * 16);
+    }
     issue_scales(s_st & 3, s_st >> 2, (g / 4 + 1) % SG, s_it < it_end);
     if (++b_st == nst) {
       b_st = 0;
@@ -408,7 +470,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       issue_a(g + RA - 1);
       issue_b(g + RB - 1);
       const uint8_t* abase = sA + (g % RA) * A_SLOT;
-      const uint8_t* bbase = sB + (g % RB) * B_SLOT;
+      const uint8_t* bbase = PB ? sB + ((g >> 1) % RBP) * B_SLOT_P : sB + (g % RB) * B_SLOT;
       const uint8_t* sbase = sS + ((g / 4) % SG) * S_SLOT + (g & 3) * 4 + lg;
       i32x8_t bq[NF];
       int bs[NF];
@@ -416,8 +478,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int nf = 0; nf < NF; ++nf) {
         const int r = wv * WROWS + nf * 16 + ln;
         bs[nf] = sbase[r * 16];
-        const uint4 c =
-            *reinterpret_cast<const uint4*>(bbase + r * 64 + ((lg ^ ((r >> 2) & 3)) * 16));
+        const uint4 c = *reinterpret_cast<const uint4*>(
+            PB ? bbase + step_block_off(r, g & 1, lg)
+               : bbase + r * 64 + ((lg ^ ((r >> 2) & 3)) * 16));
         bq[nf] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
       }
       // A fragments of m-block i: pass p = bytes [16 lg, +16) and
@@ -564,20 +627,6 @@ __device__ int expert_at(const int32_t* __restrict__ offsets, int E, int j, int*
   }
   __syncthreads();
   return *s_e;
-}
-
-// A step of the one-token stream moves 128 bytes (two 128-element stages) of
-// each of the wave's rows; one copy instruction covers 8 rows (lane L: row
-// L / 8 of the 8, 16-byte unit (L % 8) ^ swz(row)).  A row's 128 bytes sit
-// at row * 128 in the slot, unit u at position u ^ swz(row): the 16 lanes
-// that read one block of 16 consecutive rows then hit 16 distinct 4-bank
-// groups of LDS.
-__device__ __forceinline__ int step_swz(int row) { return (row >> 1) & 7; }
-
-// LDS offset (within a step slot) of the block the lane feeds to the
-// instruction for stage q (0, 1) of the step: row rw, block 4q + lg.
-__device__ __forceinline__ int step_block_off(int rw, int q, int lg) {
-  return rw * 128 + (((4 * q + lg) ^ step_swz(rw)) << 4);
 }
 
 constexpr int kDn1Ring = 2, kGu1ScaleRing = 3;
@@ -910,16 +959,18 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   const uint8_t* w = static_cast<const uint8_t*>(b.w13);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
   const dim3 g(mfma_grid() / 2);   // one workgroup per CU
-#define K3_SC(MF, NF, RA, RB)                                                                \
-  mx_gemm_scaled<MF, NF, RA, RB, false><<<g, dim3(256), 0, st>>>(xq, w, ws, offsets,         \
-                                                                 sorted_pair, h, s.d, s.f, s.E, s.k)
-  // Short m-tiles (weight-stream bound): a deep weight ring.  Taller ones:
-  // 96-row m-tiles, so that an expert's weights are streamed once for up to
-  // 96 of its pairs.
+#define K3_SC(MF, NF, RA, RB, PB)                                                           \
+  mx_gemm_scaled<MF, NF, RA, RB, false, PB><<<g, dim3(256), 0, st>>>(                        \
+      xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k)
+  // Short m-tiles (weight-stream bound): pair-wide non-temporal weight copies
+  // with deep rings on both operands (a wave waits for its copies in issue
+  // order, so the activation ring's lead also bounds the weights').  Taller
+  // ones: 96-row m-tiles, so that an expert's weights are streamed once for
+  // up to 96 of its pairs.
   const int mf = pick_mf(s, 6);
-  if (mf <= 1) K3_SC(1, 4, 2, 7);
-  else if (mf <= 3) K3_SC(3, 4, 2, 5);
-  else K3_SC(6, 4, 2, 4);
+  if (mf <= 1) K3_SC(1, 4, 4, 4, true);
+  else if (mf <= 3) K3_SC(3, 4, 2, 5, false);
+  else K3_SC(6, 4, 2, 4, false);
 #undef K3_SC
   return hipGetLastError();
 }
@@ -945,13 +996,13 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
     }
   }
   const dim3 g(mfma_grid() / 2);
-#define K3_SD(MF, NF, RA, RB)                                                                 \
-  mx_gemm_scaled<MF, NF, RA, RB, true><<<g, dim3(256), 0, st>>>(hb, w, ws, offsets, nullptr, y, \
-                                                                s.d, s.f, s.E, s.k)
+#define K3_SD(MF, NF, RA, RB, PB)                                                           \
+  mx_gemm_scaled<MF, NF, RA, RB, true, PB><<<g, dim3(256), 0, st>>>(                         \
+      hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k)
   const int mf = pick_mf(s, 6);
-  if (mf <= 1) K3_SD(1, 4, 2, 7);
-  else if (mf <= 3) K3_SD(3, 4, 2, 5);
-  else K3_SD(6, 4, 2, 3);
+  if (mf <= 1) K3_SD(1, 4, 4, 4, true);
+  else if (mf <= 3) K3_SD(3, 4, 2, 5, false);
+  else K3_SD(6, 4, 2, 3, false);
 #undef K3_SD
   return hipGetLastError();
 }
