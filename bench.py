@@ -32,6 +32,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0      # dense fp8 matrix peak: the rate of the scal
                                    # instruction the large-batch routed path issues
 MXFP4_MFMA_PEAK_TFLOPS = 10100.0   # dense MXFP4 x MXFP4 matrix peak, for reference
 X_PASSES = 2                       # E4M3 passes that carry bf16 x exactly (one MFMA each)
+SPIN_CYCLES = 20_000_000           # ~10 ms of GPU spin ahead of a timed run of launches
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (MXFP4 bytes) at batch 1/64/4096"
 PMC_FILE = os.path.join(ROOT, "profiles", "gateup_1tok_decode_b1_counters.md")
 KERNEL_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "mxscale.hip")
@@ -183,6 +184,10 @@ def main():
     layer.expert_gateup(*prepared[0], h=h)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # a spin kernel ahead of the first event lets the host enqueue the K
+    # launches ahead of the GPU, so the events time back-to-back kernels and
+    # not the host's per-call overhead
+    torch.cuda._sleep(SPIN_CYCLES)
     a.record(stream)
     for x, offsets, sp in prepared:
         layer.expert_gateup(x, offsets, sp, h=h)
@@ -208,6 +213,7 @@ def main():
     # routed expert FFN (gate/up + down) of the same prepared batches
     y = torch.empty((T * cfg.k, cfg.d), dtype=torch.float32, device="cuda")
     fws = layer.workspace(shape, OP_EXPERT_FFN)
+    torch.cuda._sleep(SPIN_CYCLES)
     a.record(stream)
     for x, offsets, sp in prepared:
         k3moe_expert_ffn(shape, layer.routed_bank, x, offsets, sp, y, fws)
