@@ -204,20 +204,20 @@ __global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
 // With pair-wide weight copies (PB), the copies a wave issues after the last
 // copy that a stage needs, in the steady state, for either parity of the
 // stage: per stage the wave issues NAW activation copies, then on every other
-// stage nbc2 weight-code copies (two stages of its rows, 128 bytes each),
-// then one scale copy.
+// stage nbc2 weight-code copies (two stages of its rows, 128 bytes each);
+// the scale copies of every fourth stage are left out (fewer counted copies
+// only make a wait stricter).
 __host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2) {
   int best = 1 << 30;
   for (int par = 0; par < 2; ++par) {
     const int g = 2 * (RA + RB) + par;   // the awaited stage (any with full history)
-    int na = 0, nb = 1;
+    int na = 0, nb = 0;
     // A(g) was issued first in iteration g - RA + 1
-    na += (((g - RA + 1) + RB - 1) % 2 == 0 ? nbc2 : 0) + 1;
-    for (int i = g - RA + 2; i <= g - 1; ++i) na += NAW + ((i + RB - 1) % 2 == 0 ? nbc2 : 0) + 1;
-    // the weight pair of stage g was issued in iteration 2 (g / 2) - RB + 1,
-    // followed by that iteration's scale copy
+    na += (((g - RA + 1) + RB - 1) % 2 == 0 ? nbc2 : 0);
+    for (int i = g - RA + 2; i <= g - 1; ++i) na += NAW + ((i + RB - 1) % 2 == 0 ? nbc2 : 0);
+    // the weight pair of stage g was issued in iteration 2 (g / 2) - RB + 1
     for (int i = 2 * (g / 2) - RB + 2; i <= g - 1; ++i)
-      nb += NAW + ((i + RB - 1) % 2 == 0 ? nbc2 : 0) + 1;
+      nb += NAW + ((i + RB - 1) % 2 == 0 ? nbc2 : 0);
     const int m = na < nb ? na : nb;
     best = m < best ? m : best;
   }
@@ -282,16 +282,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int B_SLOT = BROWS * 64;            // weight codes of one stage
   constexpr int S_SLOT = BROWS * 16;            // weight scales of 4 stages (16 bytes a row)
   constexpr int NBCW = BROWS * 4 / 256;         // B code copies per wave per stage
-  constexpr int NBW = NBCW + 1;                 // + one scale copy (a quarter group)
-  constexpr int QR = BROWS / 16;                // scale rows per wave per stage
+  constexpr int SCW = BROWS / 256;              // scale copies per wave per group (4 stages)
   // Scale groups in flight: compute stage c reads group c / 4 while the
   // copies of stage c + RB - 1 fill group (c + RB - 1) / 4 + 1; a slot is
   // refilled only after its last stage was read (SG * 4 > RB + 6).
   constexpr int SG = (RB + 6) / 4 + 1;
-  // Per stage the copies are issued A first, then B.  When stage g is
-  // awaited, A(g) was followed by B(g + RB - RA) and the copies of RA - 2
-  // later stages, B(g) by the copies of RB - 2 later stages.
-  constexpr int NEWER_A = NBW + (RA - 2) * (NAW + NBW), NEWER_B = (RB - 2) * (NAW + NBW);
+  // Per stage the copies are issued A first, then B (then, on every fourth
+  // stage, the scales, which are not counted below: fewer counted copies
+  // only make a wait stricter).  When stage g is awaited, A(g) was followed
+  // by B(g + RB - RA) and the copies of RA - 2 later stages, B(g) by the
+  // copies of RB - 2 later stages.  The scales of a stage's group were copied
+  // at least 4 stages before its codes.
+  constexpr int NEWER_A = NBCW + (RA - 2) * (NAW + NBCW), NEWER_B = (RB - 2) * (NAW + NBCW);
   constexpr int RBP = (RB + 2) / 2;             // PB: two-stage weight slots
   constexpr int B_SLOT_P = BROWS * 128;
   constexpr int NBC = PB ? 2 * NBCW : NBCW;     // weight-code copies per wave per copy round
@@ -300,8 +302,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int RMAX = RA > RB ? RA : RB;
   static_assert(NF == 4 || NF == 8, "4 or 8 fragments per wave");
   static_assert(RA >= 2 && RB >= 2, "rings need two slots");
-  static_assert(PB ? (RA - 1) * NAW + (RB / 2 + 1) * NBC + (RB - 1) <= 63
-                   : (RA - 1) * NAW + (RB - 1) * NBW <= 63, "memory counter range");
+  static_assert((RA - 1) * NAW + (PB ? (RB / 2 + 1) * NBC : (RB - 1) * NBCW) + RB / 4 * SCW + SCW <= 63,
+                "memory counter range");
   __shared__ __attribute__((aligned(16))) uint8_t sA[RA * A_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sB[PB ? RBP * B_SLOT_P : RB * B_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sS[SG * S_SLOT];
@@ -378,18 +380,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     s_e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
   };
   const uint32_t sA_lds = lds_addr(sA), sB_lds = lds_addr(sB), sS_lds = lds_addr(sS);
-  // Scales of quarter q (rows [q BROWS / 4, (q + 1) BROWS / 4), this
-  // wave's quarter of them) of group grp of the scale cursor's item, into scale
-  // slot `slot` (16 bytes a row; lanes beyond the half stay idle).  Past the
-  // last item the copy repeats a valid row into a slot nobody reads, so every
-  // stage issues one copy.
-  auto issue_scales = [&](int q, int grp, int slot, bool valid) {
-    const int r0 = q * (BROWS / 4) + wv * QR;
-    const int r = r0 + (lane < QR ? lane : 0);
-    const uint8_t* src = valid ? wsc + ((size_t)s_e * e_rows + grow(s_nt, r)) * s_row + grp * 16
-                               : wsc + (size_t)r * s_row;
-    const uint32_t dst = sS_lds + (uint32_t)(slot * S_SLOT + r0 * 16);
-    if (lane < QR) dma16_raw(src, dst);
+  // Scales of group grp (4 stages) of the scale cursor's item, every row of
+  // the tile (16 bytes a row), this wave's quarter of the rows, into scale
+  // slot `slot`; one copy per 64 rows, on every fourth stage.  Past the last
+  // item the copy repeats rows of expert 0 into a slot nobody reads.
+  auto issue_scales = [&](int grp, int slot, bool valid) {
+#pragma unroll
+    for (int q = 0; q < SCW; ++q) {
+      const int r0 = wv * (BROWS / 4) + q * 64, r = r0 + lane;
+      const uint8_t* src = valid ? wsc + ((size_t)s_e * e_rows + grow(s_nt, r)) * s_row + grp * 16
+                                 : wsc + (size_t)r * s_row;
+      dma16_raw(src, sS_lds + (uint32_t)(slot * S_SLOT + r0 * 16));
+    }
   };
   auto issue_a = [&](int g) {
     if (a_it >= it_end) return;
@@ -417,7 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int q = 0; q < NBCW; ++q)
         dma16_raw(bp[q] + b_st * (kBK / 2), base + (wv * (NBCW * 64) + q * 64) * 16);
     }
-    issue_scales(s_st & 3, s_st >> 2, (g / 4 + 1) % SG, s_it < it_end);
+    if ((s_st & 3) == 0) issue_scales(s_st >> 2, (g / 4 + 1) % SG, s_it < it_end);
     if (++b_st == nst) {
       b_st = 0;
       b_it += it_step;
