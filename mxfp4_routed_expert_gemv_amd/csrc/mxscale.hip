@@ -968,11 +968,12 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   // with deep rings on both operands (a wave waits for its copies in issue
   // order, so the activation ring's lead also bounds the weights').  Taller
   // ones: 96-row m-tiles, so that an expert's weights are streamed once for
-  // up to 96 of its pairs.
+  // up to 96 of its pairs, with pair-wide weight copies too (half as many
+  // cache-line requests per stage for the same bytes).
   const int mf = pick_mf(s, 6);
   if (mf <= 1) K3_SC(1, 4, 4, 4, true);
   else if (mf <= 3) K3_SC(3, 4, 2, 5, false);
-  else K3_SC(6, 4, 2, 4, false);
+  else K3_SC(6, 4, 2, 2, true);
 #undef K3_SC
   return hipGetLastError();
 }
