@@ -224,21 +224,23 @@ __host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2)
   return best;
 }
 
-// One workgroup of 4 waves per CU, one wave per SIMD (so each wave may hold
-// 512 registers).  Every wave both copies and computes:
+// One workgroup of 8 waves per CU, two per SIMD: waves 0..3 only compute,
+// waves 4..7 only copy, so a copy that stalls at issue (the memory pipeline's
+// queues are full) does not hold back the matrix-core work of its SIMD.
 //   * item = (m-tile of BM = 16 MF expert-sorted rows, n-tile of 4 * 16 NF
-//     weight rows); wave w computes all BM rows against weight rows
+//     weight rows); compute wave w computes all BM rows against weight rows
 //     [16 NF w, 16 NF (w + 1)) of the n-tile;
 //   * each stage (128 contraction elements) of A (activations, from L2) and
 //     B (weight codes and scales, from HBM) is copied into LDS rings of RA
-//     and RB slots by LDS-DMA, each wave issuing a quarter of the copies;
-//     the copy cursors run RA - 1 and RB - 1 stages ahead of the compute
-//     and cross item boundaries, so the weight stream does not drain
-//     between items;
-//   * one s_barrier per stage: before it each wave waits for its own copies
-//     of the stage (a constant number of newer copies may stay in flight;
-//     none near the end) and for its LDS reads of the previous stage; after
-//     it the slots of the previous stage are refilled.
+//     and RB slots by LDS-DMA, copy wave 4 + q issuing quarter q of the
+//     copies; the copy cursors run RA - 1 and RB - 1 stages ahead of the
+//     compute and cross item boundaries, so the weight stream does not
+//     drain between items;
+//   * one s_barrier per stage, passed by both roles: before it a copy wave
+//     waits for its own copies of the stage (a constant number of newer
+//     copies may stay in flight; none near the end) and a compute wave for
+//     its LDS reads of the previous stage; after it the copy waves refill
+//     the slots of the previous stage.
 // LDS layouts:
 //   A slot: [BM rows][UA units of 16 bytes] exactly as the source row's
 //     stage (UA = 8 NP + 1, odd, so the 16 rows of a fragment read fall on
@@ -263,8 +265,8 @@ __host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2)
 // bytes (two stages) are copied at once, non-temporally, into a ring of
 // (RB + 2) / 2 two-stage slots laid out as the one-token stream's steps:
 // whole 128-byte lines per copy, each read once.
-template <int MF, int NF, int RA, int RB, bool DOWN, bool PB = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_gemm_scaled(
+template <int MF, int NF, int RA, int RB, bool DOWN, bool PB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mx_gemm_scaled(
     const uint8_t* __restrict__ a_src, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pair, void* __restrict__ out, int d, int f, int E,
@@ -308,11 +310,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) uint8_t sB[PB ? RBP * B_SLOT_P : RB * B_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sS[SG * S_SLOT];
   __shared__ int s_mt[kMaxE + 1];
-  __shared__ int s_wave[4];
+  __shared__ int s_wave[8];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  build_mtiles_n<256>(offsets, E, BM, s_mt, s_wave);
+  const bool copier = wv >= 4;
+  const int cq = wv & 3;                      // a copy wave's quarter of each stage's copies
+  build_mtiles_n<512>(offsets, E, BM, s_mt, s_wave);
   const int NT = DOWN ? d / BROWS : f / (4 * FW);
   const int nst = (DOWN ? f : d) / kBK;
   const ItemRange ir0 = item_range((long)s_mt[E] * NT);
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int rows = min(BM, offsets[e + 1] - row0);
 #pragma unroll
     for (int q = 0; q < NAW; ++q) {
-      const int unit = wv * (NAW * 64) + q * 64 + lane;
+      const int unit = cq * (NAW * 64) + q * 64 + lane;
       int r = unit / UA, u = unit - r * UA;
       if (r >= BM) r = u = 0;   // padding units: any valid source
       const int rr = min(r, rows - 1);
@@ -365,10 +369,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int q = 0; q < NBC; ++q) {
       if constexpr (PB) {   // 8 rows per copy, 128 bytes each
-        const int r = (wv * (NBC * 64) + q * 64 + lane) >> 3;
+        const int r = (cq * (NBC * 64) + q * 64 + lane) >> 3;
         bp[q] = wbase + grow(nt, r) * w_row + (((lane & 7) ^ step_swz(r)) << 4);
       } else {
-        const int r = (wv * (NBCW * 64) + q * 64 + lane) >> 2;
+        const int r = (cq * (NBCW * 64) + q * 64 + lane) >> 2;
         const int b = (lane & 3) ^ ((r >> 2) & 3);
         bp[q] = wbase + grow(nt, r) * w_row + b * 16;
       }
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto issue_scales = [&](int grp, int slot, bool valid) {
 #pragma unroll
     for (int q = 0; q < SCW; ++q) {
-      const int r0 = wv * (BROWS / 4) + q * 64, r = r0 + lane;
+      const int r0 = cq * (BROWS / 4) + q * 64, r = r0 + lane;
       const uint8_t* src = valid ? wsc + ((size_t)s_e * e_rows + grow(s_nt, r)) * s_row + grp * 16
                                  : wsc + (size_t)r * s_row;
       dma16_raw(src, sS_lds + (uint32_t)(slot * S_SLOT + r0 * 16));
@@ -395,7 +399,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   auto issue_a = [&](int g) {
     if (a_it >= it_end) return;
-    const uint32_t base = sA_lds + (uint32_t)((g % RA) * A_SLOT + wv * (NAW * 64) * 16);
+    const uint32_t base = sA_lds + (uint32_t)((g % RA) * A_SLOT + cq * (NAW * 64) * 16);
 #pragma unroll
     for (int q = 0; q < NAW; ++q) dma16_raw(ap[q] + (size_t)a_st * (UA * 16), base + q * 1024);
     if (++a_st == nst) {
@@ -411,13 +415,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint32_t base = sB_lds + (uint32_t)(((g >> 1) % RBP) * B_SLOT_P);
 #pragma unroll
         for (int q = 0; q < NBC; ++q)
-          dma16_raw_nt(bp[q] + (b_st >> 1) * kBK, base + (wv * (NBC * 64) + q * 64) * 16);
+          dma16_raw_nt(bp[q] + (b_st >> 1) * kBK, base + (cq * (NBC * 64) + q * 64) * 16);
       }
     } else {
       const uint32_t base = sB_lds + (uint32_t)((g % RB) * B_SLOT);
 #pragma unroll
       for (int q = 0; q < NBCW; ++q)
-        dma16_raw(bp[q] + b_st * (kBK / 2), base + (wv * (NBCW * 64) + q * 64) * 16);
+        dma16_raw(bp[q] + b_st * (kBK / 2), base + (cq * (NBCW * 64) + q * 64) * 16);
     }
     if ((s_st & 3) == 0) issue_scales(s_st >> 2, (g / 4 + 1) % SG, s_it < it_end);
     if (++b_st == nst) {
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (s_it < it_end) s_setup();
     }
   };
-  if (a_it < it_end) {
+  if (copier && a_it < it_end) {
     a_setup();
     b_setup();
     if (s_it < it_end) s_setup();
@@ -440,16 +444,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
 #pragma unroll
     for (int q = 0; q < BROWS / 256; ++q) {
-      const int r0 = wv * (BROWS / 4) + q * 64;
+      const int r0 = cq * (BROWS / 4) + q * 64;
       dma16_raw(wsc + ((size_t)e * e_rows + grow(nt, r0 + lane)) * s_row,
                 sS_lds + (uint32_t)(r0 * 16));
     }
   }
-  // prologue, in the loop's order: virtual stage j issues A(j + RA - 1), B(j + RB - 1)
+  if (copier) {
+    // prologue, in the loop's order: virtual stage j issues A(j + RA - 1), B(j + RB - 1)
 #pragma unroll
-  for (int j = -(RMAX - 1); j < 0; ++j) {
-    if (j + RA - 1 >= 0) issue_a(j + RA - 1);
-    if (j + RB - 1 >= 0) issue_b(j + RB - 1);
+    for (int j = -(RMAX - 1); j < 0; ++j) {
+      if (j + RA - 1 >= 0) issue_a(j + RA - 1);
+      if (j + RB - 1 >= 0) issue_b(j + RB - 1);
+    }
+    // g_total stages, as many barriers as the compute waves pass: wait for
+    // this stage's copies, barrier, copy ahead
+#pragma unroll 1
+    for (int g = 0; g < g_total; ++g) {
+      if (g + RMAX - 2 < g_total) wait_vmem<NEWER>();
+      else wait_vmem<0>();
+      wg_barrier();
+      issue_a(g + RA - 1);
+      issue_b(g + RB - 1);
+    }
+    wait_vmem<0>();
+    return;
   }
 
   int g = 0;   // global stage index of this workgroup
@@ -465,12 +483,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int nf = 0; nf < NF; ++nf) acc[i][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int s = 0; s < nst; ++s, ++g) {
-      if (g + RMAX - 2 < g_total) wait_vmem<NEWER>();
-      else wait_vmem<0>();
       wait_lds();
       wg_barrier();
-      issue_a(g + RA - 1);
-      issue_b(g + RB - 1);
       const uint8_t* abase = sA + (g % RA) * A_SLOT;
       const uint8_t* bbase = PB ? sB + ((g >> 1) % RBP) * B_SLOT_P : sB + (g % RB) * B_SLOT;
       const uint8_t* sbase = sS + ((g / 4) % SG) * S_SLOT + (g & 3) * 4 + lg;
@@ -571,7 +585,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
     const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
     const int rows = min(BM, offsets[e + 1] - row0);
-    const int nmb = (rows + 15) >> 4;
+    // 1 .. MF live blocks (an m-tile holds 1 .. BM rows); clamped, so that
+    // every item runs its nst stages and barriers
+    const int nmb = max(1, min(MF, (rows + 15) >> 4));
     static_assert(MF <= 6, "item dispatch covers up to 6 m-blocks");
     switch (nmb) {
       case 1: run_item(std::integral_constant<int, 1>(), nt, row0, rows); break;
@@ -582,7 +598,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       default: if constexpr (MF >= 6) run_item(std::integral_constant<int, 6>(), nt, row0, rows); break;
     }
   }
-  wait_vmem<0>();
 }
 
 // -------------------------------------------------------------- one token
@@ -962,7 +977,7 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
   const dim3 g(mfma_grid() / 2);   // one workgroup per CU
 #define K3_SC(MF, NF, RA, RB, PB)                                                           \
-  mx_gemm_scaled<MF, NF, RA, RB, false, PB><<<g, dim3(256), 0, st>>>(                        \
+  mx_gemm_scaled<MF, NF, RA, RB, false, PB><<<g, 512, 0, st>>>(                              \
       xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k)
   // Short m-tiles (weight-stream bound): pair-wide non-temporal weight copies
   // with deep rings on both operands (a wave waits for its copies in issue
@@ -1000,7 +1015,7 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
   }
   const dim3 g(mfma_grid() / 2);
 #define K3_SD(MF, NF, RA, RB, PB)                                                           \
-  mx_gemm_scaled<MF, NF, RA, RB, true, PB><<<g, dim3(256), 0, st>>>(                         \
+  mx_gemm_scaled<MF, NF, RA, RB, true, PB><<<g, 512, 0, st>>>(                               \
       hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k)
   const int mf = pick_mf(s, 6);
   if (mf <= 1) K3_SD(1, 4, 4, 4, true);
