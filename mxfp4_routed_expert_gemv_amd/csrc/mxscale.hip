@@ -242,11 +242,14 @@ __host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2)
 //     its LDS reads of the previous stage; after it the copy waves refill
 //     the slots of the previous stage.
 // LDS layouts:
-//   A slot: [BM rows][UA units of 16 bytes] exactly as the source row's
-//     stage (UA = 8 NP + 1, odd, so the 16 rows of a fragment read fall on
-//     distinct banks), padded to a whole number of 256-unit copy rounds;
+//   A slot: [BM rows][ULA = UA + 1 units of 16 bytes]: the source row's
+//     stage (UA = 8 NP + 1 units) and one unused unit, padded to a whole
+//     number of 256-unit copy rounds.  The 16-byte fragment reads of 16
+//     rows run at the full LDS rate when the row pitch is an odd multiple
+//     of 32 bytes (18 or 26 units), at half rate at 17 or 25 (measured);
 //   B slot: codes [64 NF rows][4 MX blocks of 16 bytes], block b of row r at
-//     position b ^ ((r >> 2) & 3).  Local weight row r belongs to wave
+//     position b ^ ((r >> 1) & 3), the swizzle of 64-byte rows that reads
+//     at the full rate (with (r >> 2) & 3 it is half).  Local weight row r belongs to wave
 //     r / (16 NF), fragment (r / 16) % NF, lane r % 16;
 //   scale slot (a ring of SG): [64 NF rows][16 bytes], the scales of 4
 //     consecutive stages of the row (4 bytes a stage), as stored.  Copying a
@@ -273,9 +276,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int k) {
   constexpr int NP = DOWN ? 3 : 2;              // activation passes
   constexpr int NPH = 3;                        // passes of the h this kernel writes
-  constexpr int UA = NP * 8 + 1;
+  constexpr int UA = NP * 8 + 1;                // units of a source row's stage
+  constexpr int ULA = UA + 1;                   // units of an A row in LDS
   constexpr int BM = 16 * MF;
-  constexpr int A_UNITS = (BM * UA + 255) / 256 * 256;
+  constexpr int A_UNITS = (BM * ULA + 255) / 256 * 256;
   constexpr int A_SLOT = A_UNITS * 16;
   constexpr int NAW = A_UNITS / 256;            // A copies per wave per stage
   constexpr int WROWS = NF * 16;                // weight rows per wave
@@ -355,8 +359,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int q = 0; q < NAW; ++q) {
       const int unit = cq * (NAW * 64) + q * 64 + lane;
-      int r = unit / UA, u = unit - r * UA;
-      if (r >= BM) r = u = 0;   // padding units: any valid source
+      int r = unit / ULA, u = unit - r * ULA;
+      if (r >= BM || u >= UA) r = u = 0;   // padding units: any valid source
       const int rr = min(r, rows - 1);
       const size_t src_row = DOWN ? (size_t)(row0 + rr) : (size_t)(sorted_pair[row0 + rr] / k);
       ap[q] = a_src + src_row * a_row + u * 16;
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bp[q] = wbase + grow(nt, r) * w_row + (((lane & 7) ^ step_swz(r)) << 4);
       } else {
         const int r = (cq * (NBCW * 64) + q * 64 + lane) >> 2;
-        const int b = (lane & 3) ^ ((r >> 2) & 3);
+        const int b = (lane & 3) ^ ((r >> 1) & 3);
         bp[q] = wbase + grow(nt, r) * w_row + b * 16;
       }
     }
@@ -496,7 +500,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bs[nf] = sbase[r * 16];
         const uint4 c = *reinterpret_cast<const uint4*>(
             PB ? bbase + step_block_off(r, g & 1, lg)
-               : bbase + r * 64 + ((lg ^ ((r >> 2) & 3)) * 16));
+               : bbase + r * 64 + ((lg ^ ((r >> 1) & 3)) * 16));
         bq[nf] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
       }
       // A fragments of m-block i: pass p = bytes [16 lg, +16) and
@@ -504,7 +508,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       i32x8_t a[2][NP];
       int as[2][NP];
       auto load_a = [&](int i, i32x8_t (&av)[NP], int (&sv)[NP]) {
-        const uint8_t* arow = abase + (i * 16 + ln) * (UA * 16);
+        const uint8_t* arow = abase + (i * 16 + ln) * (ULA * 16);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           const uint4 lo = *reinterpret_cast<const uint4*>(arow + (p * 8 + lg) * 16);
