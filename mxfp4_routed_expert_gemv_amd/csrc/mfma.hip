@@ -322,7 +322,8 @@ hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& b, 
   // (the combine stays a kernel of its own in this class: folded into this
   // epilogue its scattered reads cost more than they save)
   if (comb.y_perm) return hipErrorInvalidValue;
-  if (T >= 128) down_shared_mfma<4, false><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
+  if (T >= 1024) down_shared_mfma<8, false><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
+  else if (T >= 128) down_shared_mfma<4, false><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
   else down_shared_mfma<2, false><<<g, blk, 0, st>>>(h, w2, y, T, s.d, fs, S, comb);
   return hipGetLastError();
 }
