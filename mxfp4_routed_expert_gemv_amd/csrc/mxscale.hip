@@ -360,9 +360,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int q = 0; q < NAW; ++q) {
       const int unit = cq * (NAW * 64) + q * 64 + lane;
       int r = unit / ULA, u = unit - r * ULA;
-      if (r >= BM || u >= UA) r = u = 0;   // padding units: any valid source
-      const int rr = min(r, rows - 1);
-      const size_t src_row = DOWN ? (size_t)(row0 + rr) : (size_t)(sorted_pair[row0 + rr] / k);
+      // padding units and the rows past the tile's last: all the same 16
+      // bytes (the first row's first unit), so that their lanes' copies
+      // merge into one request; those LDS rows are never stored from
+      if (r >= rows || u >= UA) r = u = 0;
+      const size_t src_row = DOWN ? (size_t)(row0 + r) : (size_t)(sorted_pair[row0 + r] / k);
       ap[q] = a_src + src_row * a_row + u * 16;
     }
   };
