@@ -100,9 +100,13 @@ __global__ __launch_bounds__(256) void router_gemv_f64(const void* __restrict__ 
 }
 
 // Large batches: the same fp64 logits on the fp64 matrix cores
-// (MFMA 16x16x4).  A workgroup computes 32 tokens x 32 experts; wave w
-// covers the contraction slice [w d/4, (w+1) d/4), and the four partial
-// sums are added in wave order.  Lane (i = lane % 16, c = lane / 16) holds
+// (MFMA 16x16x4).  A workgroup computes 16 TA tokens x 16 EB experts (TA,
+// EB in {1, 2}: smaller tiles at small batches, so that enough workgroups
+// share the fp64 matrix work); wave w covers the contraction slice
+// [w d/4, (w+1) d/4), and the four partial sums are added in wave order.
+// Each logit's arithmetic (its MFMA chain over the wave's slice, the
+// partials' order, the norms of its two rows) does not depend on the tile
+// shape, so neither do its bits.  Lane (i = lane % 16, c = lane / 16) holds
 // elements c*8 .. c*8+7 of each 32-element group of its token row (A) and
 // expert row (B); MFMA step q (0..7) takes element c*8 + q from every lane,
 // so each product pairs x and w of the same element.  The bound uses
@@ -110,97 +114,114 @@ __global__ __launch_bounds__(256) void router_gemv_f64(const void* __restrict__ 
 // in fp64 (bf16 squares are exact) along the same pass.
 typedef __attribute__((ext_vector_type(4))) double f64x4_t;
 
+template <int TA, int EB>
 __global__ __launch_bounds__(256) void router_mfma_f64(const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ wr,
                                                        double* __restrict__ logits,
                                                        float* __restrict__ lbound, int T, int d,
                                                        int E) {
-  __shared__ double part[4][32][33];
+  constexpr int BT = 16 * TA, BE = 16 * EB;
+  __shared__ double part[4][BT][BE + 1];
   __shared__ double nrm[4][2][32];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 15, lc = lane >> 4;
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
   const int kq = d / 4;                 // contraction slice per wave (multiple of 64)
   const int kbeg = wv * kq;
-  const uint16_t* ar[2];
-  const uint16_t* br[2];
+  const uint16_t* ar[TA];
+  const uint16_t* br[EB];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    ar[f] = x + (size_t)min(t0 + f * 16 + li, T - 1) * d + kbeg + lc * 8;
-    br[f] = wr + (size_t)min(e0 + f * 16 + li, E - 1) * d + kbeg + lc * 8;
-  }
-  f64x4_t acc[2][2];
+  for (int f = 0; f < TA; ++f) ar[f] = x + (size_t)min(t0 + f * 16 + li, T - 1) * d + kbeg + lc * 8;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int f = 0; f < EB; ++f) br[f] = wr + (size_t)min(e0 + f * 16 + li, E - 1) * d + kbeg + lc * 8;
+  f64x4_t acc[TA][EB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-  double sa[2] = {0.0, 0.0}, sb[2] = {0.0, 0.0};
+  for (int a = 0; a < TA; ++a)
+#pragma unroll
+    for (int b = 0; b < EB; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  double sa[TA], sb[EB];
+#pragma unroll
+  for (int f = 0; f < TA; ++f) sa[f] = 0.0;
+#pragma unroll
+  for (int f = 0; f < EB; ++f) sb[f] = 0.0;
 
-  uint4 av[2], bv[2];
-#pragma unroll
-  for (int f = 0; f < 2; ++f) { av[f] = ldg16(ar[f]); bv[f] = ldg16(br[f]); }
+  // register ring of PD groups: group gi's loads are issued PD groups ahead
+  // (small tiles, few waves per SIMD: 4; the 32 x 32 tile: 1, which keeps
+  // its registers to 4 waves per SIMD)
+  constexpr int PD = TA * EB == 4 ? 1 : 4;
   const int ng = kq / 32;
-#pragma unroll 1
-  for (int gi = 0; gi < ng; ++gi) {
-    const int gn = min(gi + 1, ng - 1);
-    uint4 an[2], bn[2];
+  uint4 av[PD][TA], bv[PD][EB];
+  auto load = [&](int g, int slot) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) { an[f] = ldg16(ar[f] + gn * 32); bn[f] = ldg16(br[f] + gn * 32); }
-    double xa[2][8], wb[2][8];
+    for (int f = 0; f < TA; ++f) av[slot][f] = ldg16(ar[f] + g * 32);
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const uint32_t aw[4] = {av[f].x, av[f].y, av[f].z, av[f].w};
-      const uint32_t bw[4] = {bv[f].x, bv[f].y, bv[f].z, bv[f].w};
+    for (int f = 0; f < EB; ++f) bv[slot][f] = ldg16(br[f] + g * 32);
+  };
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        xa[f][2 * u] = (double)bf16_lo(aw[u]);
-        xa[f][2 * u + 1] = (double)bf16_hi(aw[u]);
-        wb[f][2 * u] = (double)bf16_lo(bw[u]);
-        wb[f][2 * u + 1] = (double)bf16_hi(bw[u]);
-      }
+  for (int q = 0; q < PD; ++q) load(min(q, ng - 1), q);
+  // bf16 pair -> two fp64 values and their squares added to a norm, in order
+  auto widen = [](const uint4& v, double (&o)[8], double& nsq) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        sa[f] = __builtin_fma(xa[f][u], xa[f][u], sa[f]);
-        sb[f] = __builtin_fma(wb[f][u], wb[f][u], sb[f]);
-      }
+    for (int u = 0; u < 4; ++u) {
+      o[2 * u] = (double)bf16_lo(w[u]);
+      o[2 * u + 1] = (double)bf16_hi(w[u]);
     }
 #pragma unroll
-    for (int qs = 0; qs < 8; ++qs)
+    for (int u = 0; u < 8; ++u) nsq = __builtin_fma(o[u], o[u], nsq);
+  };
+#pragma unroll 1
+  for (int g0 = 0; g0 < ng; g0 += PD) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+    for (int q = 0; q < PD; ++q) {
+      if (g0 + q < ng) {
+        double xa[TA][8], wb[EB][8];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[a][qs], wb[b][qs], acc[a][b], 0, 0, 0);
+        for (int f = 0; f < TA; ++f) widen(av[q][f], xa[f], sa[f]);
 #pragma unroll
-    for (int f = 0; f < 2; ++f) { av[f] = an[f]; bv[f] = bn[f]; }
+        for (int f = 0; f < EB; ++f) widen(bv[q][f], wb[f], sb[f]);
+        load(min(g0 + q + PD, ng - 1), q);   // past the end: a repeat, unused
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads PD groups ahead
+#pragma unroll
+        for (int qs = 0; qs < 8; ++qs)
+#pragma unroll
+          for (int a = 0; a < TA; ++a)
+#pragma unroll
+            for (int b = 0; b < EB; ++b)
+              acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[a][qs], wb[b][qs], acc[a][b], 0, 0,
+                                                               0);
+      }
+    }
   }
   // Output element r of fragment (a, b): token a*16 + lc + 4 r, expert b*16 + li.
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TA; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < EB; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) part[wv][a * 16 + lc + 4 * r][b * 16 + li] = acc[a][b][r];
   // squared norms: the four lanes c of a row, in lane order
+  auto lane_sum = [&](double v) {
+    v += __shfl_xor(v, 16, kWave);
+    return v + __shfl_xor(v, 32, kWave);
+  };
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    double va = sa[f], vb = sb[f];
-    va += __shfl_xor(va, 16, kWave);
-    vb += __shfl_xor(vb, 16, kWave);
-    va += __shfl_xor(va, 32, kWave);
-    vb += __shfl_xor(vb, 32, kWave);
-    if (lc == 0) {
-      nrm[wv][0][f * 16 + li] = va;
-      nrm[wv][1][f * 16 + li] = vb;
-    }
+  for (int f = 0; f < TA; ++f) {
+    const double va = lane_sum(sa[f]);
+    if (lc == 0) nrm[wv][0][f * 16 + li] = va;
+  }
+#pragma unroll
+  for (int f = 0; f < EB; ++f) {
+    const double vb = lane_sum(sb[f]);
+    if (lc == 0) nrm[wv][1][f * 16 + li] = vb;
   }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < (BT * BE + 255) / 256; ++u) {
     const int o = tid + 256 * u;
-    const int tt = o >> 5, ee = o & 31;
+    const int tt = o / BE, ee = o % BE;
     const int t = t0 + tt, e = e0 + ee;
-    if (t < T && e < E) {
+    if (tt < BT && t < T && e < E) {
       const double l = ((part[0][tt][ee] + part[1][tt][ee]) + part[2][tt][ee]) + part[3][tt][ee];
       const double nx = ((nrm[0][0][tt] + nrm[1][0][tt]) + nrm[2][0][tt]) + nrm[3][0][tt];
       const double nw = ((nrm[0][1][ee] + nrm[1][1][ee]) + nrm[2][1][ee]) + nrm[3][1][ee];
@@ -452,6 +473,22 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
                    logits_out, diag, d, E, k, perm);
 }
 
+// fp64 router tiles: 16 x 16 up to 64 tokens, 32 x 16 up to 256, else 32 x 32,
+// so that small batches still spread the fp64 matrix work over the CUs
+// (at 64 tokens and 896 experts: 224 workgroups instead of 56).
+void launch_router_mfma(const uint16_t* x, const uint16_t* wr, double* logits, float* lbound,
+                        int T, int d, int E, hipStream_t st) {
+  if (T <= 64)
+    router_mfma_f64<1, 1><<<dim3((T + 15) / 16, (E + 15) / 16), 256, 0, st>>>(x, wr, logits,
+                                                                             lbound, T, d, E);
+  else if (T <= 256)
+    router_mfma_f64<2, 1><<<dim3((T + 31) / 32, (E + 15) / 16), 256, 0, st>>>(x, wr, logits,
+                                                                             lbound, T, d, E);
+  else
+    router_mfma_f64<2, 2><<<dim3((T + 31) / 32, (E + 31) / 32), 256, 0, st>>>(x, wr, logits,
+                                                                             lbound, T, d, E);
+}
+
 // One token: the selection (wave 0 of workgroup 0) runs beside the shared
 // experts' gate/up (every other wave takes one (expert, feature) item), which
 // does not depend on the routing.  Workgroups of 4 waves; x is staged in LDS
@@ -482,8 +519,7 @@ hipError_t launch_router_logits(const k3moe_shape& s, const void* x, const uint1
                                 const RouteWs& ws, hipStream_t st) {
   const int T = (int)s.T;
   if (use_mfma(s))
-    router_mfma_f64<<<dim3((T + 31) / 32, (s.E + 31) / 32), 256, 0, st>>>(
-        static_cast<const uint16_t*>(x), wr, ws.logits, ws.lbound, T, s.d, s.E);
+    launch_router_mfma(static_cast<const uint16_t*>(x), wr, ws.logits, ws.lbound, T, s.d, s.E, st);
   else if (s.x_dtype == K3MOE_F32)
     router_gemv_f64<true><<<dim3((s.E + 3) / 4), 256, 0, st>>>(x, wr, ws.logits, ws.lbound, T, s.d,
                                                                s.E);
@@ -517,8 +553,7 @@ hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr,
   const bool xf32 = s.x_dtype == K3MOE_F32;
   const dim3 g1((s.E + 3) / 4);
   if (use_mfma(s))
-    router_mfma_f64<<<dim3((T + 31) / 32, (s.E + 31) / 32), 256, 0, st>>>(
-        static_cast<const uint16_t*>(x), wr, ws.logits, ws.lbound, T, s.d, s.E);
+    launch_router_mfma(static_cast<const uint16_t*>(x), wr, ws.logits, ws.lbound, T, s.d, s.E, st);
   else if (xf32)
     router_gemv_f64<true><<<g1, 256, 0, st>>>(x, wr, ws.logits, ws.lbound, T, s.d, s.E);
   else
