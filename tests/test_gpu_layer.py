@@ -152,6 +152,21 @@ def test_mfma_class_batch_composition():
         assert torch.equal(part, full[:n]), n
 
 
+def test_router_tiles_keep_the_bits():
+    """The fp64 matrix-core router takes 16 x 16 tiles up to 64 tokens, 32 x 16
+    up to 256 and 32 x 32 above: the same tokens get the same logits, ids and
+    weights, bit for bit, at 64, 65 and 300 tokens."""
+    require_gpu()
+    cfg = MED.with_tokens(300)
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    runs = {n: L.route(wl.x[:n].contiguous(), want_logits=True) for n in (64, 65, 300)}
+    torch.cuda.synchronize()
+    for n in (64, 65):
+        for a, b, what in zip(runs[n], runs[300], ("idx", "w", "logits")):
+            assert torch.equal(a, b[:n]), (n, what)
+
+
 def _e4m3(codes: np.ndarray) -> np.ndarray:
     """OCP E4M3 (FN) code -> value: bias 7, subnormals m/8 * 2^-6, 0x7F/0xFF NaN."""
     c = codes.astype(np.int64)
@@ -575,6 +590,11 @@ def test_decode_b64(big, orc):
     full = L(x)
     torch.cuda.synchronize()
     assert torch.equal(part.view(torch.int16), full[:32].view(torch.int16))
+    # a ragged batch in the small-batch shared-expert regime: the first 50
+    # tokens alone equal their rows of the batch of 64, bit for bit
+    part50 = L(x[:50].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(part50.view(torch.int16), full[:50].view(torch.int16))
     # the routed outputs of single tokens (one-token kernels) equal their rows
     # of the batch (grouped GEMMs), bit for bit
     k = gen.get("decode_b64").k
