@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // (down) of one expert for every token, its 4 waves splitting the tokens
 // (wave w: tokens 16 w .. 16 w + 15), so that gate/up runs S fs / 16 and
 // down d / 16 workgroups.  Operands come from memory straight into
-// registers, PD stages ahead.  Each (token, output) value is the same chain
+// registers, PD - 1 stages ahead.  Each (token, output) value is the same chain
 // as in the tiled kernels (stages of 64 elements, then the two 32-element
 // halves, the down's hi then lo pass), so it has their bits.
 template <int PD>
@@ -364,31 +364,29 @@ __global__ __launch_bounds__(kThreads) void down_shared_small(const float* __res
   for (int s0 = 0; s0 < nst; s0 += PD) {   // nst % PD == 0
 #pragma unroll
     for (int q = 0; q < PD; ++q) {
-      {
-        load(min(s0 + q + PD - 1, nst - 1), (q + PD - 1) % PD);   // past the end: a repeat
-        __builtin_amdgcn_sched_barrier(0);   // keep the loads PD - 1 stages ahead
+      load(min(s0 + q + PD - 1, nst - 1), (q + PD - 1) % PD);   // past the end: a repeat
+      __builtin_amdgcn_sched_barrier(0);   // keep the loads PD - 1 stages ahead
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          // h split into hi and lo bf16, as the tiled kernel does
-          const float fv[8] = {__uint_as_float(hv[q][j][0].x), __uint_as_float(hv[q][j][0].y),
-                               __uint_as_float(hv[q][j][0].z), __uint_as_float(hv[q][j][0].w),
-                               __uint_as_float(hv[q][j][1].x), __uint_as_float(hv[q][j][1].y),
-                               __uint_as_float(hv[q][j][1].z), __uint_as_float(hv[q][j][1].w)};
-          uint32_t hi[4], lo[4];
+      for (int j = 0; j < 2; ++j) {
+        // h split into hi and lo bf16, as the tiled kernel does
+        const float fv[8] = {__uint_as_float(hv[q][j][0].x), __uint_as_float(hv[q][j][0].y),
+                             __uint_as_float(hv[q][j][0].z), __uint_as_float(hv[q][j][0].w),
+                             __uint_as_float(hv[q][j][1].x), __uint_as_float(hv[q][j][1].y),
+                             __uint_as_float(hv[q][j][1].z), __uint_as_float(hv[q][j][1].w)};
+        uint32_t hi[4], lo[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint16_t h0 = f32_to_bf16(fv[2 * c]), h1 = f32_to_bf16(fv[2 * c + 1]);
-            const uint16_t l0 = f32_to_bf16(fv[2 * c] - __uint_as_float((uint32_t)h0 << 16));
-            const uint16_t l1 = f32_to_bf16(fv[2 * c + 1] - __uint_as_float((uint32_t)h1 << 16));
-            hi[c] = h0 | ((uint32_t)h1 << 16);
-            lo[c] = l0 | ((uint32_t)l1 << 16);
-          }
-          const bf16x8_t ah = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-          const bf16x8_t al = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-          const bf16x8_t b = as_bf16x8(bv[q][j]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
+        for (int c = 0; c < 4; ++c) {
+          const uint16_t h0 = f32_to_bf16(fv[2 * c]), h1 = f32_to_bf16(fv[2 * c + 1]);
+          const uint16_t l0 = f32_to_bf16(fv[2 * c] - __uint_as_float((uint32_t)h0 << 16));
+          const uint16_t l1 = f32_to_bf16(fv[2 * c + 1] - __uint_as_float((uint32_t)h1 << 16));
+          hi[c] = h0 | ((uint32_t)h1 << 16);
+          lo[c] = l0 | ((uint32_t)l1 << 16);
         }
+        const bf16x8_t ah = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+        const bf16x8_t al = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        const bf16x8_t b = as_bf16x8(bv[q][j]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
       }
     }
   }
