@@ -611,6 +611,14 @@ def test_prefill_4096(big, orc):
     _run_big(big, gen.get("prefill_4096"), orc, 4)
 
 
+@pytest.mark.parametrize("T", [1025, 4095])
+def test_full_size_other_batches(big, orc, T):
+    """Full size at 1025 tokens (48-row grouped tiles, 128-token shared
+    tiles, 32 x 32 router tiles) and at 4095 (ragged 96-row tiles): full
+    oracle routing and permutation, and the values of sampled tokens."""
+    _run_big(big, gen.get("prefill_4096").with_tokens(T), orc, 3)
+
+
 def test_prefill_16384_zipf(big, orc):
     r, _, _ = _run_big(big, gen.get("prefill_16384_zipf"), orc, 4)
     counts = to_np(r["counts"])
