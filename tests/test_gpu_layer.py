@@ -611,11 +611,14 @@ def test_prefill_4096(big, orc):
     _run_big(big, gen.get("prefill_4096"), orc, 4)
 
 
-@pytest.mark.parametrize("T", [1025, 4095])
+@pytest.mark.parametrize("T", [8, 33, 1025, 4095])
 def test_full_size_other_batches(big, orc, T):
-    """Full size at 1025 tokens (48-row grouped tiles, 128-token shared
-    tiles, 32 x 32 router tiles) and at 4095 (ragged 96-row tiles): full
-    oracle routing and permutation, and the values of sampled tokens."""
+    """Full size at 8 tokens (the vector-ALU router and shared experts beside
+    the scaled grouped GEMMs), 33 (16 x 16 router tiles, the small-batch
+    shared kernels with a ragged token count), 1025 (48-row grouped tiles,
+    128-token shared tiles, 32 x 32 router tiles) and 4095 (ragged 96-row
+    tiles): full oracle routing and permutation, and the values of sampled
+    tokens."""
     _run_big(big, gen.get("prefill_4096").with_tokens(T), orc, 3)
 
 
