@@ -173,3 +173,15 @@ def test_status_strings_and_path_class():
     assert k3.k3moe_path_class(big_shape(T=4096, f=2048 + 64)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, f=2048 + 256)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, d=0)) == k3.PATH_GEMV
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it exits with a message,
+    before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
