@@ -143,8 +143,9 @@ uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols);
  * shared and routed experts as matrix-core GEMMs, the routed ones on the
  * scaled MXFP4 instruction: the stored weight bytes as one operand, the
  * activations split into E4M3 passes with E8M0 block scales as the other)
- * when T >= 32, x is bf16, d % 512 == 0 and f % 512 == 0; K3MOE_PATH_GEMV (router and shared experts as GEMVs, one
- * pass over the weights per token, fp32 dot products) otherwise.  The routed
+ * when T >= 32, x is bf16, d % 512 == 0 and f % 512 == 0; K3MOE_PATH_GEMV
+ * (router and shared experts as GEMVs, one pass over the weights per token,
+ * fp32 dot products) otherwise.  The routed
  * experts take the scaled matrix-core instruction in both classes whenever x
  * is bf16, d % 512 == 0 and f % 512 == 0 (one token: one workgroup per
  * active expert and output slice; more: the grouped GEMMs), so their outputs
