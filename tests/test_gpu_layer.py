@@ -582,6 +582,39 @@ def test_decode_b1(big, orc):
     assert np.all(np.isfinite(to_np(out32)))
 
 
+def test_decode_layer_in_a_graph(big):
+    """The one-token layer records into a graph (no memset, copy, allocation
+    or host synchronisation inside the library): every replay, with eager
+    layers run between replays, equals the eager result bit for bit."""
+    import dataclasses
+    from mxfp4_routed_expert_gemv_amd.layer import MoELayer
+    cfg = gen.get("decode_b1")
+    L = MoELayer(big.w_router, big.routed, big.shared, cfg.k, out_dtype=torch.bfloat16)
+    xs = [gen.device.activations(dataclasses.replace(cfg, seed=200 + i)) for i in range(3)]
+    eager = [L(x) for x in xs]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for x in xs:
+            L(x)
+    torch.cuda.current_stream().wait_stream(side)
+    graphs, outs = [], []
+    for x in xs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            outs.append(L(x))
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, g in enumerate(graphs):
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(outs[i].view(torch.int16), eager[i].view(torch.int16)), (rep, i)
+            L(xs[(i + 1) % 3])
+            torch.cuda.synchronize()
+
+
 def test_decode_b64(big, orc):
     r, L, x = _run_big(big, gen.get("decode_b64"), orc, 6)
     # batch composition inside the matrix-core class: the first 32 tokens
