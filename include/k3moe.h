@@ -131,7 +131,9 @@ typedef struct k3moe_layer_weights {
 } k3moe_layer_weights;
 
 /* Bytes of workspace `op` needs for `shape` (0 for an invalid shape).  The
- * workspace pointer must be 256-byte aligned. */
+ * workspace pointer must be 256-byte aligned.  Host-only; no passage defines
+ * it (the pages' engines size their buffers from the shard census, translated
+ * README, "shard census"). */
 size_t k3moe_workspace_bytes(const k3moe_shape* shape, int op);
 
 /* Bytes of an MXFP4 matrix of rows x cols: rows * cols * 17 / 32 (half a byte
@@ -139,22 +141,31 @@ size_t k3moe_workspace_bytes(const k3moe_shape* shape, int op);
  * weight of the pages' shard census).  Host-only helper. */
 uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols);
 
-/* Which path class a call with this shape takes.  K3MOE_PATH_MFMA (router,
- * shared and routed experts as matrix-core GEMMs, the routed ones on the
- * scaled MXFP4 instruction: the stored weight bytes as one operand, the
- * activations split into E4M3 passes with E8M0 block scales as the other)
- * when T >= 32, x is bf16, d % 512 == 0 and f % 512 == 0; K3MOE_PATH_GEMV
- * (router and shared experts as GEMVs, one pass over the weights per token,
- * fp32 dot products) otherwise.  The routed
- * experts take the scaled matrix-core instruction in both classes whenever x
- * is bf16, d % 512 == 0 and f % 512 == 0 (one token: one workgroup per
- * active expert and output slice; more: the grouped GEMMs), so their outputs
- * for a token are the same bits at every batch size; otherwise they are fp32
- * GEMVs.  Results of the two classes agree within the stated tolerance, not
- * bit for bit.  Returns K3MOE_PATH_GEMV for an invalid shape. */
+/* Which path class a call with this shape takes (a token's output bits
+ * depend on which class its batch falls in, never on anything else about the
+ * batch).  The class is K3MOE_PATH_MFMA when T >= 32, x is bf16,
+ * d % 512 == 0 and f % 512 == 0, and K3MOE_PATH_GEMV otherwise.
+ *   - Router: fp64 matrix-core tiles in the MFMA class, fp64 GEMVs in the
+ *     GEMV class (same bits for the chosen set either way, see k3moe_route).
+ *   - Shared experts: bf16 matrix-core GEMMs in the MFMA class when
+ *     f_shared % 128 == 0; otherwise (GEMV class, or another f_shared) GEMVs
+ *     with fp32 dot products, one pass over the weights per token.
+ *   - Routed experts: whenever x is bf16, d % 512 == 0 and f % 512 == 0,
+ *     in both classes, the scaled MXFP4 matrix-core instruction (the stored
+ *     weight bytes as one operand, the activations split exactly into E4M3
+ *     passes with E8M0 block scales as the other; one workgroup per active
+ *     expert and output slice for one token, grouped GEMMs for more), so a
+ *     token's routed outputs are the same bits at every batch size; otherwise
+ *     fp32 GEMVs, the same bits at every batch size too.
+ * Results of the two classes agree within the stated tolerance, not bit for
+ * bit.  Returns K3MOE_PATH_GEMV for an invalid shape. */
 int k3moe_path_class(const k3moe_shape* shape);
 
-/* Router + top-k + softmax.
+/* Router + top-k + softmax.  Passage: 16 of 896 routed experts chosen per
+ * token by a linear router over the hidden state (kimi-k3-in-c review page,
+ * "at a glance" and "KDA/MLA/MoE" tables; translated README, "shard census");
+ * the softmax-over-the-chosen weights and the tie rule are this library's
+ * reading (the pages' model uses sigmoid scores).
  * x [T][d] (x_dtype), w_router [E][d] bf16 ->
  *   topk_idx [T][k] int32, each row in ascending expert id;
  *   topk_w   [T][k] fp32, aligned with topk_idx, summing to 1 per token;
@@ -162,34 +173,55 @@ int k3moe_path_class(const k3moe_shape* shape);
  * The chosen set equals the set an exact evaluation of the logits in fp64
  * (ascending i) picks: near-ties at the k/k+1 boundary are re-evaluated
  * exactly on the device (counted in diag[K3MOE_DIAG_RECHECKED_TOKENS]).
+ * diag: optional K3MOE_DIAG_COUNT counters (NULL = not collected); non-finite
+ * logits are counted in diag[K3MOE_DIAG_NONFINITE_LOGITS].
+ * Errors: EINVAL (NULL x, w_router, topk_idx, topk_w), EALIGN, EWORKSPACE.
  * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_ROUTE). */
 k3moe_status k3moe_route(const k3moe_shape* shape, const void* x, const void* w_router,
                          int32_t* topk_idx, float* topk_w, float* logits, int32_t* diag,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Counting sort of the T*k (token, slot) pairs by expert, stable in pair
- * order (pair p = t*k + slot):
+ * order (pair p = t*k + slot).  Passage: the experts are gathered per layer
+ * and each expert's weights are read once for all its tokens (WASTE article
+ * page, section "속도는 어디서 나왔나"; explainer page, "le cache LRU"); the
+ * grouping itself is this library's.  Outputs:
  *   counts [E], offsets [E+1] (exclusive prefix sum, offsets[E] = T*k),
  *   sorted_pair [T*k]: sorted_pair[q] = pair at sorted position q,
  *   pair_pos    [T*k]: its inverse.
  * Exact integer results.  An id outside [0, E), or an id repeated within a
  * token's row, is dropped (its pair_pos is -1, sorted positions past
  * offsets[E] hold -1) and counted in diag[K3MOE_DIAG_BAD_EXPERT_IDS].
+ * Errors: EINVAL (a NULL output), EALIGN, EWORKSPACE.
  * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_PERMUTE). */
 k3moe_status k3moe_permute(const k3moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                            int32_t* diag, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Routed expert FFN on an MXFP4 bank (n_experts = E):
+/* Expert FFN y = Wd (silu(Wg x) * (Wu x)).  Passage: routed experts stored
+ * as MXFP4 and multiplied without a dequantised copy (kimi-k3-in-c review
+ * page, "KDA/MLA/MoE" table; explainer page, "reduction one"); the gated
+ * activation is taken as SiLU (the pages name a bounded "SiTU" gate without
+ * a formula).
+ * Routed mode (bank MXFP4, n_experts = E; sorted_pair != NULL):
  *   y [T*k][d] fp32, row q = expert e's FFN of token sorted_pair[q] / k,
  *   where e is the expert whose range offsets[e] .. offsets[e+1] holds q;
  *   unweighted.  offsets and sorted_pair as written by k3moe_permute.
- * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_EXPERT_FFN). */
+ *   Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_EXPERT_FFN).
+ * Shared mode (bank BF16, n_experts = n_shared, f = f_shared;
+ *   sorted_pair == NULL, offsets ignored): every token through every expert
+ *   of the bank with weight 1, summed in bank order: y [T][d] fp32, the same
+ *   call as k3moe_shared_ffn (same kernels, same bits).
+ *   Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_SHARED_FFN).
+ * Errors: EINVAL (NULL pointers, bank not matching the shape),
+ * EUNSUPPORTED (an MXFP4 bank without sorted_pair, a BF16 bank with one),
+ * EALIGN, EWORKSPACE. */
 k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank* bank,
                               const void* x, const int32_t* offsets, const int32_t* sorted_pair,
                               float* y, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The two halves of k3moe_expert_ffn (same kernels, same bits):
+/* The two halves of k3moe_expert_ffn's routed mode (same kernels, same
+ * bits; the passage is k3moe_expert_ffn's):
  * gate/up + SiLU-GLU:  h, row q = silu(Wg x) * (Wu x) of expert e on token
  *   sorted_pair[q] / k (e as for k3moe_expert_ffn);
  * down:  y [T*k][d] fp32, row q = Wd_e h[q].
@@ -215,12 +247,21 @@ k3moe_status k3moe_expert_down(const k3moe_shape* shape, const k3moe_expert_bank
 
 /* Shared experts on a BF16 bank (n_experts = n_shared, f = f_shared):
  *   y [T][d] fp32 = sum over the bank's experts in order of each expert's FFN.
+ * Passage: 2 always-on shared experts beside the routed ones, resident and
+ * never streamed (kimi-k3-in-c review page, "at a glance" table and the
+ * memory discussion; translated README, "shard census").  Equivalent to
+ * k3moe_expert_ffn's shared mode.  Errors: EINVAL (no shared experts, NULL
+ * pointers), EUNSUPPORTED (bank not BF16), EALIGN, EWORKSPACE.
  * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_SHARED_FFN). */
 k3moe_status k3moe_shared_ffn(const k3moe_shape* shape, const k3moe_expert_bank* bank,
                               const void* x, float* y, void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Fixed-order combine:
+/* Fixed-order combine.  Passage: a fixed summation order pins the bits of
+ * the pages' engine (translated README, "why no BLAS"); the order itself
+ * (shared experts first, then the routed ones by ascending id, weight-0
+ * terms skipped) is this library's reading.  Errors: EINVAL (NULL y_perm,
+ * pair_pos, topk_w, out), EALIGN.
  *   out[t][o] = shared_y[t][o] (0 when shared_y is NULL)
  *               + sum over slots s ascending with topk_w[t][s] != 0 of
  *                 topk_w[t][s] * y_perm[pair_pos[t*k+s]][o]
@@ -230,8 +271,11 @@ k3moe_status k3moe_combine(const k3moe_shape* shape, const float* y_perm, const 
                            const float* topk_w, const float* shared_y, void* out, void* stream);
 
 /* The whole layer: route, permute, routed experts, shared experts, combine.
+ * Passage: one MoE FFN layer of the pages' model (kimi-k3-in-c review page,
+ * "at a glance" and "KDA/MLA/MoE" tables).
  * Bit-identical to calling the five stages above in sequence on the same
- * stream.  out [T][d] in out_dtype.
+ * stream.  out [T][d] in out_dtype.  diag as for k3moe_route and
+ * k3moe_permute (NULL = not collected).  Errors: those of the stages.
  * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_LAYER). */
 k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* weights,
                          const void* x, void* out, int32_t* diag, void* workspace,

@@ -4,11 +4,30 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "internal.h"
 
 namespace k3 {
+
+// One cache slot per device id; a slot is written with the same value by
+// whichever thread gets there first, so concurrent first calls agree.
+int cu_count() {
+  constexpr int kSlots = 64;
+  static std::atomic<int> cache[kSlots];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev < kSlots ? dev : kSlots - 1;
+  int cus = dev < kSlots ? cache[slot].load(std::memory_order_relaxed) : 0;
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < kSlots) cache[slot].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -274,7 +293,16 @@ k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank*
                               float* y, void* workspace, size_t workspace_bytes, void* stream) {
   K3_CHECK(check_shape(shape));
   const k3moe_shape& s = *shape;
+  if (!bank) return fail(K3MOE_EINVAL, "expert bank is NULL");
+  if (bank->format == K3MOE_FMT_BF16) {
+    // shared mode: every token through every expert of the bank, summed in order
+    if (sorted_pair)
+      return fail(K3MOE_EUNSUPPORTED, "a BF16 bank takes no sorted_pair (shared mode)");
+    return k3moe_shared_ffn(shape, bank, x, y, workspace, workspace_bytes, stream);
+  }
   K3_CHECK(check_routed_bank(s, bank));
+  if (!sorted_pair)
+    return fail(K3MOE_EUNSUPPORTED, "an MXFP4 bank needs sorted_pair (routed mode)");
   if (s.T == 0) return ok();
   K3_CHECK(need_ptr(x, "x"));
   K3_CHECK(need_ptr(offsets, "offsets"));

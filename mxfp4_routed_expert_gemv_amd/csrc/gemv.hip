@@ -784,11 +784,7 @@ inline int64_t max_active(const k3moe_shape& s) {
 
 // Persistent grid: enough workgroups for every item, at most `per_cu` per CU.
 inline unsigned persistent_grid(int64_t items, int per_cu) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
+  const int cus = cu_count();
   const int64_t cap = (int64_t)cus * per_cu;
   const int64_t need = (items + 3) / 4;
   return (unsigned)(need < cap ? (need > 0 ? need : 1) : cap);
@@ -849,11 +845,7 @@ hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& ban
   if (routed_scaled(s)) return launch_down_scaled(s, bank, h, offsets, y, st);
   if (s.T == 1 && s.d % kDownT1Chunk == 0 && (size_t)s.f * 4 <= 32768) {
     const int chunks = s.d / kDownT1Chunk;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
+    const int cus = cu_count();
     const int64_t need = (int64_t)s.k * chunks, cap = (int64_t)cus * 8;
     const unsigned g = (unsigned)(need < cap ? need : cap);
     down_t1<<<g, 256, (size_t)s.f * 4, st>>>(static_cast<const uint8_t*>(bank.w2),

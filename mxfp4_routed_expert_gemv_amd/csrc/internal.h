@@ -130,9 +130,15 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
                                 uint8_t* xq, hipStream_t st);
 hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st);
-// Persistent grid of the grouped GEMMs (two workgroups per CU, a multiple of
-// 8) and the m-tile height (in 16-row blocks) for a batch.
+// Compute units of the current device (queried once per device and cached;
+// safe to call from several threads at once).
+int cu_count();
+// Persistent grids, rounded up to a multiple of the 8 XCDs (the item split
+// of the grouped kernels gives each XCD one contiguous range): two
+// workgroups per CU (shared-expert GEMMs) or one (routed grouped GEMMs).
 int mfma_grid();
+int grouped_grid();
+// The m-tile height (in 16-row blocks) of the routed grouped GEMMs for a batch.
 int pick_mf(const k3moe_shape& s, int max_mf);
 bool shared_mfma_ok(const k3moe_shape& s);
 hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,

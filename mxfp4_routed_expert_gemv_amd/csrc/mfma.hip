@@ -399,18 +399,8 @@ __global__ __launch_bounds__(kThreads) void down_shared_small(const float* __res
 
 }  // namespace
 
-int mfma_grid() {
-  static int g = 0;
-  if (!g) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    g = ((cus * 2 + 7) / 8) * 8;   // two workgroups per CU, a multiple of the 8 XCDs
-  }
-  return g;
-}
+int mfma_grid() { return (cu_count() * 2 + 7) / 8 * 8; }
+int grouped_grid() { return (cu_count() + 7) / 8 * 8; }
 
 // Rows per m-tile from the expected pairs per expert (T k / E), with some
 // headroom so that most experts fit one tile.
@@ -423,9 +413,11 @@ int pick_mf(const k3moe_shape& s, int max_mf) {
 }
 
 
-bool shared_mfma_ok(const k3moe_shape& s) {
-  return s.T >= kMfmaMinT && s.x_dtype == K3MOE_BF16 && s.d % 256 == 0 && s.f_shared % 128 == 0;
-}
+// The shared experts take the matrix-core kernels only inside the MFMA path
+// class (so a token's bits change at no other batch size than the class
+// boundary), and only when their width fits the kernels' 128-feature tiles;
+// otherwise they stay GEMVs at every batch size.
+bool shared_mfma_ok(const k3moe_shape& s) { return use_mfma(s) && s.f_shared % 128 == 0; }
 
 hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
                               float* h, float* y, hipStream_t st, const CombineArgs& comb) {

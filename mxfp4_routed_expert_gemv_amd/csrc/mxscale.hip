@@ -981,7 +981,7 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   if (err != hipSuccess) return err;
   const uint8_t* w = static_cast<const uint8_t*>(b.w13);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
-  const dim3 g(mfma_grid() / 2);   // one workgroup per CU
+  const dim3 g(grouped_grid());   // one workgroup per CU
 #define K3_SC(MF, NF, RA, RB, PB)                                                           \
   mx_gemm_scaled<MF, NF, RA, RB, false, PB><<<g, 512, 0, st>>>(                              \
       xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k)
@@ -1019,7 +1019,7 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
       return hipGetLastError();
     }
   }
-  const dim3 g(mfma_grid() / 2);
+  const dim3 g(grouped_grid());
 #define K3_SD(MF, NF, RA, RB, PB)                                                           \
   mx_gemm_scaled<MF, NF, RA, RB, true, PB><<<g, 512, 0, st>>>(                               \
       hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k)

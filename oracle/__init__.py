@@ -222,11 +222,3 @@ def default() -> Oracle:
         _default = Oracle()
     return _default
 
-
-def bf16_round(a: np.ndarray) -> np.ndarray:
-    """fp64 -> nearest-even bf16 value (as fp64): the oracle's output rounded to
-    the layer's output dtype, for comparing bf16 outputs."""
-    a = np.asarray(a, dtype=np.float64)
-    m, e = np.frexp(a)
-    q = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)   # np.round is half-even
-    return np.where(a == 0, a, q)

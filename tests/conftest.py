@@ -24,3 +24,18 @@ def golden(name):
 def orc():
     import oracle
     return oracle.default()
+
+
+@pytest.fixture(scope="session")
+def big():
+    """Device weights of the full-size layer (d = 7168, f = 2048, 896 experts,
+    2 shared), built once and shared by every GPU test module."""
+    import torch
+    import gen
+    import gen.device
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cfg = gen.get("decode_b1")
+    print("building full-size layer weights on device", flush=True)
+    wl = gen.device.build(cfg)
+    torch.cuda.synchronize()
+    return wl

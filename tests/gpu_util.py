@@ -106,3 +106,24 @@ def check_permutation_properties(idx: np.ndarray, counts, offsets, sp, pp, E: in
 
 def float_ok(x):
     return x is not None and math.isfinite(x)
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3 (FN) code -> value: bias 7, subnormals m/8 * 2^-6, 0x7F/0xFF NaN."""
+    c = codes.astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def decode_scaled_h(buf: np.ndarray, rows: int, f: int) -> np.ndarray:
+    """The gate/up buffer in its scaled form (rows of f/128 stages of 400
+    bytes: 3 passes of 128 E4M3 codes, then byte 4p + b = E8M0 scale of pass p,
+    32-feature block b) -> fp64 values [rows][f]."""
+    st = buf.view(np.uint8)[:rows * (f // 128) * 400].reshape(rows, f // 128, 400)
+    out = np.zeros((rows, f // 128, 128))
+    for p in range(3):
+        sc = st[:, :, 384 + 4 * p:388 + 4 * p].astype(np.float64)          # [rows][stages][4]
+        out += e4m3_value(st[:, :, 128 * p:128 * (p + 1)]) * np.repeat(2.0 ** (sc - 127), 32, axis=2)
+    return out.reshape(rows, f)

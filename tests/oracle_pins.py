@@ -383,4 +383,20 @@ def pin_combine_definition(o):
             assert abs(out[t, j] - math.fsum(terms)) <= 8 * 2.0 ** -53 * sum(map(abs, terms))
 
 
+def pin_token_outputs_equal_layer(o):
+    """The per-token path (each token alone, its chosen experts' rows gathered
+    by expert, then combined in slot order) equals the batched layer's rows
+    bit for bit: out, shared_y and every (token, slot) y row."""
+    c, x, wr, bank, sh = tiny_inputs()
+    _, r = _layer_tiny(o)
+    toks = np.array([3, 0, 2])
+    out, shy, y = o.token_outputs(x[toks], r["idx"][toks], r["w"][toks],
+                                  lambda e: _expert(bank, e), sh)
+    assert np.array_equal(out, r["out"][toks])
+    assert np.array_equal(shy, r["shared_y"][toks])
+    for n, t in enumerate(toks):
+        for slot in range(c.k):
+            assert np.array_equal(y[n, slot], r["y_perm"][r["pair_pos"][t * c.k + slot]])
+
+
 ALL_PINS = [v for kname, v in sorted(globals().items()) if kname.startswith("pin_")]

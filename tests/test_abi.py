@@ -125,7 +125,7 @@ def test_bank_and_layer_validation():
     def ffn(bank):
         return k3.lib.k3moe_expert_ffn(ctypes.byref(s), ctypes.byref(bank), FAKE, FAKE, FAKE,
                                        FAKE, FAKE * 256, 1 << 40, None)
-    assert ffn(bf) == EUNSUPPORTED
+    assert ffn(bf) == EUNSUPPORTED          # a BF16 bank takes no sorted_pair
     assert ffn(wrong_n) == EINVAL
     assert ffn(no_scale) == EINVAL
     assert k3.lib.k3moe_expert_ffn(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE * 256,
@@ -134,6 +134,17 @@ def test_bank_and_layer_validation():
     sh_bad = k3.make_bank(k3.FMT_MXFP4, 2, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
     assert k3.lib.k3moe_shared_ffn(ctypes.byref(s), ctypes.byref(sh_bad), FAKE, FAKE,
                                    FAKE * 256, 1 << 40, None) == EUNSUPPORTED
+    # shared mode of k3moe_expert_ffn: a BF16 bank and sorted_pair NULL; an
+    # MXFP4 bank needs sorted_pair
+    def ffn_shared(bank, sp=None, shape=s, y=FAKE, ws=(FAKE * 256, 1 << 40)):
+        return k3.lib.k3moe_expert_ffn(ctypes.byref(shape), ctypes.byref(bank), FAKE, None, sp,
+                                       y, ws[0], ws[1], None)
+    assert ffn_shared(good) == EUNSUPPORTED
+    assert ffn_shared(bf) == EINVAL                        # 896 experts: not the 2 shared ones
+    assert ffn_shared(sh_ok, y=None) == EINVAL
+    assert ffn_shared(sh_ok, ws=(None, 0)) == EWORKSPACE
+    assert ffn_shared(sh_ok, shape=big_shape(T=0)) == 0
+    assert ffn_shared(sh_ok, shape=big_shape(n_shared=0, f_shared=0)) == EINVAL
     w_ok = k3.make_weights(FAKE, good, sh_ok)
 
     def layer(weights, x=FAKE, out=FAKE, ws=(FAKE * 256, 1 << 40), shape=s):
@@ -173,6 +184,9 @@ def test_status_strings_and_path_class():
     assert k3.k3moe_path_class(big_shape(T=4096, f=2048 + 64)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, f=2048 + 256)) == k3.PATH_GEMV
     assert k3.k3moe_path_class(big_shape(T=4096, d=0)) == k3.PATH_GEMV
+    # shapes of the GEMV class at any batch size, whatever the shared width
+    assert k3.k3moe_path_class(big_shape(T=32, f=1056)) == k3.PATH_GEMV
+    assert k3.k3moe_path_class(big_shape(T=32, d=768, f_shared=256)) == k3.PATH_GEMV
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -14,7 +14,8 @@ import gen
 import gen.device
 import oracle
 from gpu_util import (W_TOL, assert_close, assert_close_bf16, check_permutation_properties,
-                      k3layer, log, oracle_expert, require_gpu, sample_tokens, to_np)
+                      decode_scaled_h, k3layer, log, oracle_expert, require_gpu, sample_tokens,
+                      to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,27 +168,6 @@ def test_router_tiles_keep_the_bits():
             assert torch.equal(a, b[:n]), (n, what)
 
 
-def _e4m3(codes: np.ndarray) -> np.ndarray:
-    """OCP E4M3 (FN) code -> value: bias 7, subnormals m/8 * 2^-6, 0x7F/0xFF NaN."""
-    c = codes.astype(np.int64)
-    sign = np.where(c & 0x80, -1.0, 1.0)
-    e, m = (c >> 3) & 0xF, c & 7
-    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
-    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
-
-
-def _decode_scaled_h(buf: np.ndarray, rows: int, f: int) -> np.ndarray:
-    """The gate/up buffer in its scaled form (rows of f/128 stages of 400
-    bytes: 3 passes of 128 E4M3 codes, then byte 4p + b = E8M0 scale of pass p,
-    32-feature block b) -> fp64 values [rows][f]."""
-    st = buf.view(np.uint8)[:rows * (f // 128) * 400].reshape(rows, f // 128, 400)
-    out = np.zeros((rows, f // 128, 128))
-    for p in range(3):
-        sc = st[:, :, 384 + 4 * p:388 + 4 * p].astype(np.float64)          # [rows][stages][4]
-        out += _e4m3(st[:, :, 128 * p:128 * (p + 1)]) * np.repeat(2.0 ** (sc - 127), 32, axis=2)
-    return out.reshape(rows, f)
-
-
 @pytest.mark.parametrize("d,T", [(512, 1), (512, 2), (512, 5), (512, 31), (512, 40),
                                  (3584, 1), (3584, 3)])
 def test_scaled_routed_experts_any_batch(orc, d, T):
@@ -217,7 +197,7 @@ def test_scaled_routed_experts_any_batch(orc, d, T):
     assert torch.equal(y2, r["y_perm"])
     # h of every pair against the oracle's silu(g) * u
     P = T * cfg.k
-    h_gpu = _decode_scaled_h(to_np(h).reshape(-1), P, cfg.f)
+    h_gpu = decode_scaled_h(to_np(h).reshape(-1), P, cfg.f)
     bank = gen.routed_bank(cfg)
     sp = ref["sorted_pair"]
     offs = ref["offsets"]
@@ -520,19 +500,39 @@ def test_device_generator_matches_host():
 
 
 # ------------------------------------------------------------- full-size layer
-@pytest.fixture(scope="module")
-def big():
-    """Device weights of the full-size layer (d = 7168, f = 2048, 896 experts,
-    2 shared), shared by the decode and prefill workloads."""
-    require_gpu()
-    cfg = gen.get("decode_b1")
-    log("building full-size layer weights on device")
-    wl = gen.device.build(cfg)
-    torch.cuda.synchronize()
-    return wl
+def _mtile_rows(cfg) -> int:
+    """Rows per m-tile of the routed grouped GEMMs at this batch: 16 per
+    block, blocks from the expected pairs per expert with 15% headroom, at
+    most 6 (the launch rule of the scaled grouped GEMMs)."""
+    ppe = cfg.T * cfg.k / cfg.E * 1.15
+    return 16 * max(1, min(6, int((ppe + 15.0) / 16.0)))
 
 
-def _run_big(big, cfg, orc, n_sample):
+def _check_whole_experts(r, cfg, orc, x_host, counts, offsets, sp):
+    """y_perm of whole m-tiles against the oracle: the expert with the fewest
+    pairs (a tail tile), an expert spanning two m-tiles, and the first and
+    last m-tiles of the hottest expert (the ragged last one included)."""
+    bm = _mtile_rows(cfg)
+    live = np.nonzero(counts)[0]
+    tail = int(live[np.argmin(counts[live])])
+    two = [e for e in live if bm < counts[e] <= 2 * bm]
+    hot = int(np.argmax(counts))
+    ranges = [(tail, offsets[tail], offsets[tail + 1])]
+    if two:
+        e2 = int(max(two, key=lambda e: counts[e]))
+        ranges.append((e2, offsets[e2], offsets[e2 + 1]))
+    if counts[hot] > 2 * bm:
+        last0 = offsets[hot] + (counts[hot] - 1) // bm * bm
+        ranges += [(hot, offsets[hot], offsets[hot] + bm), (hot, last0, offsets[hot + 1])]
+    y_gpu = to_np(r["y_perm"])
+    for e, lo, hi in ranges:
+        toks = sp[lo:hi] // cfg.k
+        want = orc.mxfp4_ffn(gen.routed_expert(cfg, e), oracle.to_f64(x_host[toks]))
+        assert_close(y_gpu[lo:hi], want,
+                     f"y_perm expert {e} rows {lo - offsets[e]}..{hi - offsets[e]} of {counts[e]}")
+
+
+def _run_big(big, cfg, orc, n_sample, whole_experts=False):
     from mxfp4_routed_expert_gemv_amd.layer import MoELayer
     x_host = gen.x(cfg)
     x = gen.device.activations(cfg)
@@ -561,7 +561,8 @@ def _run_big(big, cfg, orc, n_sample):
     nz = counts[counts > 0]
     log(f"  experts touched {nz.size}, pairs/expert max {nz.max()} min {nz.min()}")
 
-    # values: sampled tokens, every stage, against the oracle
+    # values: sampled tokens, every stage, against the oracle; the layer's
+    # fp32 output (before any rounding to bf16) under the strict bar
     toks = sample_tokens(cfg.T, n_sample)
     out_ref, sh_ref, y_ref = orc.token_outputs(x_host[toks], idx[toks], w[toks],
                                                oracle_expert(cfg), gen.shared_bank(cfg))
@@ -571,15 +572,16 @@ def _run_big(big, cfg, orc, n_sample):
     assert_close(y_rows.reshape(-1, cfg.d), y_ref.reshape(-1, cfg.d), "y_perm (sampled)")
     assert_close(to_np(r["shared_y"])[toks], sh_ref, "shared_y (sampled)")
     assert_close_bf16(to_np(r["out"])[toks], out_ref, "out (sampled)")
+    out32 = L(x, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(to_np(out32)[toks], out_ref, "out fp32 (sampled)")
+    if whole_experts:
+        _check_whole_experts(r, cfg, orc, x_host, counts, offsets, sp)
     return r, L, x
 
 
 def test_decode_b1(big, orc):
-    r, L, x = _run_big(big, gen.get("decode_b1"), orc, 1)
-    # fp32 output too, under the strict bar
-    out32 = L(x, out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    assert np.all(np.isfinite(to_np(out32)))
+    _run_big(big, gen.get("decode_b1"), orc, 1)
 
 
 def test_decode_layer_in_a_graph(big):
@@ -616,7 +618,7 @@ def test_decode_layer_in_a_graph(big):
 
 
 def test_decode_b64(big, orc):
-    r, L, x = _run_big(big, gen.get("decode_b64"), orc, 6)
+    r, L, x = _run_big(big, gen.get("decode_b64"), orc, 16)
     # batch composition inside the matrix-core class: the first 32 tokens
     # alone equal the same tokens of the batch of 64, bit for bit
     part = L(x[:32].contiguous())
@@ -641,7 +643,7 @@ def test_decode_b64(big, orc):
 
 
 def test_prefill_4096(big, orc):
-    _run_big(big, gen.get("prefill_4096"), orc, 4)
+    _run_big(big, gen.get("prefill_4096"), orc, 8, whole_experts=True)
 
 
 @pytest.mark.parametrize("T", [8, 33, 1025, 4095])
@@ -656,9 +658,29 @@ def test_full_size_other_batches(big, orc, T):
 
 
 def test_prefill_16384_zipf(big, orc):
-    r, _, _ = _run_big(big, gen.get("prefill_16384_zipf"), orc, 4)
+    r, _, _ = _run_big(big, gen.get("prefill_16384_zipf"), orc, 8, whole_experts=True)
     counts = to_np(r["counts"])
     srt = np.sort(counts)
     gini = 1 - 2 * np.sum(np.cumsum(srt) / srt.sum()) / srt.size + 1 / srt.size
     log(f"  zipf histogram: max {counts.max()} min {counts.min()} gini {gini:.3f}")
     assert counts.max() > 1000
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("medium", 40), ("medium", 1)])
+def test_expert_ffn_shared_mode(orc, name, T):
+    """k3moe_expert_ffn with a BF16 bank and no sorted pairs is the shared
+    experts' FFN (every token through every expert, summed in bank order):
+    equal to k3moe_shared_ffn bit for bit, and to the oracle."""
+    require_gpu()
+    from mxfp4_routed_expert_gemv_amd import OP_SHARED_FFN, k3moe_expert_ffn
+    cfg = (gen.get("tiny") if name == "tiny" else MED).with_tokens(T)
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    want = L.shared_ffn(wl.x)
+    s = L.shape(T, wl.x.dtype)
+    y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    k3moe_expert_ffn(s, L.shared_bank, wl.x, None, None, y, L.workspace(s, OP_SHARED_FFN))
+    torch.cuda.synchronize()
+    assert torch.equal(y, want)
+    ref = orc.shared_ffn(gen.shared_bank(cfg), oracle.to_f64(gen.x(cfg)))
+    assert_close(to_np(y), ref, "shared mode")

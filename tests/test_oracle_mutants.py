@@ -66,3 +66,30 @@ def test_mutant_is_caught(name, tmp_path):
         except Exception as exc:  # any failure of a pin counts as caught
             caught.append(f"{pin.__name__}: {type(exc).__name__}")
     assert caught, f"no pin catches mutant {name}"
+
+
+# Mistakes planted in the oracle's per-token path (Python), which the
+# full-size GPU tests use as their expected values.
+PY_MUTANTS = {
+    "token_outputs_slot_swap": ("y[rows, slots] = self.mxfp4_ffn(",
+                                "y[rows, (slots + 1) % k] = self.mxfp4_ffn("),
+    "token_outputs_rows_of_first_token": ("self.mxfp4_ffn(get_expert(int(e)), x64[rows])",
+                                          "self.mxfp4_ffn(get_expert(int(e)), x64[rows * 0])"),
+    "token_outputs_no_shared": ("shared_y)\n    return out", "None)\n    return out"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_token_outputs_mutant_is_caught(name):
+    import inspect
+    import textwrap
+    import numpy as np
+    old, new = PY_MUTANTS[name]
+    src = textwrap.dedent(inspect.getsource(oracle.Oracle.token_outputs))
+    assert src.count(old) == 1, f"mutation site of {name} not found"
+    ns = {"np": np, "to_f64": oracle.to_f64}
+    exec(src.replace(old, new), ns)
+    o = oracle.Oracle()
+    o.token_outputs = ns["token_outputs"].__get__(o)
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_token_outputs_equal_layer(o)
