@@ -281,6 +281,27 @@ k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* we
                          const void* x, void* out, int32_t* diag, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Bytes of the fixed device scratch buffer of k3moe_layer_noalloc. */
+#define K3MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* The whole layer without allocating and without a workspace argument, for
+ * callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, hosts that forbid allocation).  Same kernels and same
+ * bits as k3moe_layer; the workspace is a fixed device array of
+ * K3MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call made with that device current).
+ * Limits: the call's k3moe_workspace_bytes(shape, K3MOE_OP_LAYER) must fit
+ * the buffer (K3MOE_EWORKSPACE otherwise, nothing enqueued); at d = 7168,
+ * f = 2048, 896 experts top-16 that is up to 103 tokens.
+ * Every call on one GPU shares that GPU's buffer: calls that may overlap on
+ * one GPU (other streams, other threads) race and must not be issued.
+ * Nothing in the buffer has to start at zero.  Errors: those of
+ * k3moe_layer, K3MOE_EWORKSPACE as above, K3MOE_EHIP if the buffer's address
+ * cannot be looked up. */
+k3moe_status k3moe_layer_noalloc(const k3moe_shape* shape, const k3moe_layer_weights* weights,
+                                 const void* x, void* out, int32_t* diag, void* stream);
+
 /* Static description of a status code. */
 const char* k3moe_status_str(k3moe_status status);
 /* Detail of the last non-OK status returned on the calling thread. */

@@ -29,8 +29,9 @@ STATUS = {0: "K3MOE_OK", 1: "K3MOE_EINVAL", 2: "K3MOE_ESHAPE", 3: "K3MOE_EALIGN"
           4: "K3MOE_EWORKSPACE", 5: "K3MOE_EUNSUPPORTED", 6: "K3MOE_EHIP"}
 EXPORTS = ["k3moe_workspace_bytes", "k3moe_mxfp4_bytes", "k3moe_path_class", "k3moe_route",
            "k3moe_permute", "k3moe_expert_ffn", "k3moe_expert_gateup", "k3moe_expert_down",
-           "k3moe_shared_ffn", "k3moe_combine", "k3moe_layer", "k3moe_status_str",
-           "k3moe_last_error"]
+           "k3moe_shared_ffn", "k3moe_combine", "k3moe_layer", "k3moe_layer_noalloc",
+           "k3moe_status_str", "k3moe_last_error"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Shape(ctypes.Structure):
@@ -90,6 +91,8 @@ def _load():
     lib.k3moe_combine.argtypes = [SP, P, P, P, P, P, P]
     lib.k3moe_layer.restype = ctypes.c_int
     lib.k3moe_layer.argtypes = [SP, ctypes.POINTER(LayerWeights), P, P, P, P, S, P]
+    lib.k3moe_layer_noalloc.restype = ctypes.c_int
+    lib.k3moe_layer_noalloc.argtypes = [SP, ctypes.POINTER(LayerWeights), P, P, P, P]
     lib.k3moe_status_str.restype = ctypes.c_char_p
     lib.k3moe_status_str.argtypes = [ctypes.c_int]
     lib.k3moe_last_error.restype = ctypes.c_char_p
@@ -195,6 +198,13 @@ def k3moe_layer(shape, weights: LayerWeights, x, out, diag=None, workspace=None,
     wp, wb = _ws(workspace)
     _check(lib.k3moe_layer(ctypes.byref(shape), ctypes.byref(weights), _addr(x), _addr(out),
                            _addr(diag), wp, wb, _stream(stream)))
+
+
+def k3moe_layer_noalloc(shape, weights: LayerWeights, x, out, diag=None, stream=None):
+    """The whole layer on the library's fixed device scratch buffer (no
+    workspace, no allocation)."""
+    _check(lib.k3moe_layer_noalloc(ctypes.byref(shape), ctypes.byref(weights), _addr(x),
+                                   _addr(out), _addr(diag), _stream(stream)))
 
 
 # --------------------------------------------------------- struct builders

@@ -213,6 +213,114 @@ LayerWs carve_layer(const k3moe_shape& s, void* ws, size_t* bytes) {
   return r;
 }
 
+// Validation of a whole-layer call, before anything is enqueued; *need
+// receives the workspace bytes (0 for an empty batch).
+k3moe_status layer_validate(const k3moe_shape* shape, const k3moe_layer_weights* weights,
+                            const void* x, const void* out, const int32_t* diag, size_t* need) {
+  *need = 0;
+  K3_CHECK(check_shape(shape));
+  const k3moe_shape& s = *shape;
+  if (!weights) return fail(K3MOE_EINVAL, "weights is NULL");
+  K3_CHECK(check_routed_bank(s, &weights->routed));
+  K3_CHECK(check_shared_bank(s, &weights->shared));
+  if (s.T == 0) return ok();
+  K3_CHECK(need_ptr(weights->w_router, "w_router"));
+  K3_CHECK(need_ptr(x, "x"));
+  K3_CHECK(need_ptr(out, "out"));
+  K3_CHECK(opt_ptr(diag, "diag"));
+  carve_layer(s, nullptr, need);
+  return K3MOE_OK;
+}
+
+k3moe_status hip_failure(hipError_t e, const char* what) { return hip_status(e, what); }
+
+k3moe_status workspace_too_small(size_t have, size_t need) {
+  return fail(K3MOE_EWORKSPACE, "the call needs %zu bytes of workspace; %zu are available", need,
+              have);
+}
+
+// The layer's stages on a validated call, with a workspace of at least
+// k3moe_workspace_bytes(shape, K3MOE_OP_LAYER) bytes.
+k3moe_status layer_run(const k3moe_shape& s, const k3moe_layer_weights& wts, const void* x,
+                       void* out, int32_t* diag, void* workspace, hipStream_t st) {
+  const k3moe_layer_weights* weights = &wts;
+  const LayerWs L = carve_layer(s, workspace, nullptr);
+  if (topk_shared_t1_ok(s) && shared_down_t1_ok(s)) {
+    // One token: router logits; then the selection (which also writes the
+    // permutation) beside the shared experts' gate/up; the routed experts;
+    // the shared experts' down finishing each output with the combine.
+    const RouteWs rws = carve_route(s, L.scratch, nullptr);
+    PermOut perm;
+    perm.counts = L.counts;
+    perm.offsets = L.offsets;
+    perm.sorted_pair = L.sorted_pair;
+    perm.pair_pos = L.pair_pos;
+    SharedWs sws;
+    sws.h = L.shared_h;
+    hipError_t e = launch_router_logits(s, x, static_cast<const uint16_t*>(weights->w_router),
+                                        rws, st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer router");
+    e = launch_topk_shared_t1(s, x, static_cast<const uint16_t*>(weights->w_router), L.topk_idx,
+                              L.topk_w, diag, rws, perm, weights->shared, sws.h, st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer top-k + shared gate/up");
+    e = launch_expert_ffn(s, weights->routed, x, L.offsets, L.sorted_pair, L.y_perm,
+                          carve_expert(s, L.scratch, nullptr), st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer routed experts");
+    CombineArgs comb;
+    comb.y_perm = L.y_perm;
+    comb.pair_pos = L.pair_pos;
+    comb.topk_w = L.topk_w;
+    comb.out = out;
+    comb.k = s.k;
+    comb.out_bf16 = s.out_dtype == K3MOE_BF16;
+    e = launch_shared_down_t1(s, weights->shared, sws, L.shared_y, st, comb);
+    return hip_status(e, "k3moe_layer shared down + combine");
+  }
+  // One token: the top-k kernel also writes the (trivial) permutation.
+  PermOut perm;
+  if (s.T == 1) {
+    perm.counts = L.counts;
+    perm.offsets = L.offsets;
+    perm.sorted_pair = L.sorted_pair;
+    perm.pair_pos = L.pair_pos;
+  }
+  hipError_t e = launch_route(s, x, static_cast<const uint16_t*>(weights->w_router), L.topk_idx,
+                              L.topk_w, nullptr, diag, carve_route(s, L.scratch, nullptr), st,
+                              perm);
+  if (e != hipSuccess) return hip_status(e, "k3moe_layer route");
+  if (s.T != 1) {
+    e = launch_permute(s, L.topk_idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, diag,
+                       carve_permute(s, L.scratch, nullptr), st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer permute");
+  }
+  e = launch_expert_ffn(s, weights->routed, x, L.offsets, L.sorted_pair, L.y_perm,
+                        carve_expert(s, L.scratch, nullptr), st);
+  if (e != hipSuccess) return hip_status(e, "k3moe_layer routed experts");
+  if (s.n_shared > 0 && !shared_mfma_ok(s)) {
+    // the shared experts' down GEMV finishes each output with the combine
+    CombineArgs comb;
+    comb.y_perm = L.y_perm;
+    comb.pair_pos = L.pair_pos;
+    comb.topk_w = L.topk_w;
+    comb.out = out;
+    comb.k = s.k;
+    comb.out_bf16 = s.out_dtype == K3MOE_BF16;
+    SharedWs sws;
+    sws.h = L.shared_h;
+    e = launch_shared_ffn(s, weights->shared, x, L.shared_y, sws, st, comb);
+    return hip_status(e, "k3moe_layer shared experts + combine");
+  }
+  if (s.n_shared > 0) {
+    SharedWs sws;
+    sws.h = L.shared_h;
+    e = launch_shared_ffn(s, weights->shared, x, L.shared_y, sws, st);
+    if (e != hipSuccess) return hip_status(e, "k3moe_layer shared experts");
+  }
+  e = launch_combine(s, L.y_perm, L.pair_pos, L.topk_w, s.n_shared > 0 ? L.shared_y : nullptr,
+                     out, st);
+  return hip_status(e, "k3moe_layer combine");
+}
+
 }  // namespace k3
 
 using namespace k3;
@@ -387,95 +495,11 @@ k3moe_status k3moe_combine(const k3moe_shape* shape, const float* y_perm, const 
 k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* weights,
                          const void* x, void* out, int32_t* diag, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  K3_CHECK(check_shape(shape));
-  const k3moe_shape& s = *shape;
-  if (!weights) return fail(K3MOE_EINVAL, "weights is NULL");
-  K3_CHECK(check_routed_bank(s, &weights->routed));
-  K3_CHECK(check_shared_bank(s, &weights->shared));
-  if (s.T == 0) return ok();
-  K3_CHECK(need_ptr(weights->w_router, "w_router"));
-  K3_CHECK(need_ptr(x, "x"));
-  K3_CHECK(need_ptr(out, "out"));
-  K3_CHECK(opt_ptr(diag, "diag"));
   size_t need = 0;
-  carve_layer(s, nullptr, &need);
+  K3_CHECK(layer_validate(shape, weights, x, out, diag, &need));
+  if (shape->T == 0) return ok();
   K3_CHECK(check_ws(workspace, workspace_bytes, need));
-  const LayerWs L = carve_layer(s, workspace, nullptr);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (topk_shared_t1_ok(s) && shared_down_t1_ok(s)) {
-    // One token: router logits; then the selection (which also writes the
-    // permutation) beside the shared experts' gate/up; the routed experts;
-    // the shared experts' down finishing each output with the combine.
-    const RouteWs rws = carve_route(s, L.scratch, nullptr);
-    PermOut perm;
-    perm.counts = L.counts;
-    perm.offsets = L.offsets;
-    perm.sorted_pair = L.sorted_pair;
-    perm.pair_pos = L.pair_pos;
-    SharedWs sws;
-    sws.h = L.shared_h;
-    hipError_t e = launch_router_logits(s, x, static_cast<const uint16_t*>(weights->w_router),
-                                        rws, st);
-    if (e != hipSuccess) return hip_status(e, "k3moe_layer router");
-    e = launch_topk_shared_t1(s, x, static_cast<const uint16_t*>(weights->w_router), L.topk_idx,
-                              L.topk_w, diag, rws, perm, weights->shared, sws.h, st);
-    if (e != hipSuccess) return hip_status(e, "k3moe_layer top-k + shared gate/up");
-    e = launch_expert_ffn(s, weights->routed, x, L.offsets, L.sorted_pair, L.y_perm,
-                          carve_expert(s, L.scratch, nullptr), st);
-    if (e != hipSuccess) return hip_status(e, "k3moe_layer routed experts");
-    CombineArgs comb;
-    comb.y_perm = L.y_perm;
-    comb.pair_pos = L.pair_pos;
-    comb.topk_w = L.topk_w;
-    comb.out = out;
-    comb.k = s.k;
-    comb.out_bf16 = s.out_dtype == K3MOE_BF16;
-    e = launch_shared_down_t1(s, weights->shared, sws, L.shared_y, st, comb);
-    return hip_status(e, "k3moe_layer shared down + combine");
-  }
-  // One token: the top-k kernel also writes the (trivial) permutation.
-  PermOut perm;
-  if (s.T == 1) {
-    perm.counts = L.counts;
-    perm.offsets = L.offsets;
-    perm.sorted_pair = L.sorted_pair;
-    perm.pair_pos = L.pair_pos;
-  }
-  hipError_t e = launch_route(s, x, static_cast<const uint16_t*>(weights->w_router), L.topk_idx,
-                              L.topk_w, nullptr, diag, carve_route(s, L.scratch, nullptr), st,
-                              perm);
-  if (e != hipSuccess) return hip_status(e, "k3moe_layer route");
-  if (s.T != 1) {
-    e = launch_permute(s, L.topk_idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, diag,
-                       carve_permute(s, L.scratch, nullptr), st);
-    if (e != hipSuccess) return hip_status(e, "k3moe_layer permute");
-  }
-  e = launch_expert_ffn(s, weights->routed, x, L.offsets, L.sorted_pair, L.y_perm,
-                        carve_expert(s, L.scratch, nullptr), st);
-  if (e != hipSuccess) return hip_status(e, "k3moe_layer routed experts");
-  if (s.n_shared > 0 && !shared_mfma_ok(s)) {
-    // the shared experts' down GEMV finishes each output with the combine
-    CombineArgs comb;
-    comb.y_perm = L.y_perm;
-    comb.pair_pos = L.pair_pos;
-    comb.topk_w = L.topk_w;
-    comb.out = out;
-    comb.k = s.k;
-    comb.out_bf16 = s.out_dtype == K3MOE_BF16;
-    SharedWs sws;
-    sws.h = L.shared_h;
-    e = launch_shared_ffn(s, weights->shared, x, L.shared_y, sws, st, comb);
-    return hip_status(e, "k3moe_layer shared experts + combine");
-  }
-  if (s.n_shared > 0) {
-    SharedWs sws;
-    sws.h = L.shared_h;
-    e = launch_shared_ffn(s, weights->shared, x, L.shared_y, sws, st);
-    if (e != hipSuccess) return hip_status(e, "k3moe_layer shared experts");
-  }
-  e = launch_combine(s, L.y_perm, L.pair_pos, L.topk_w, s.n_shared > 0 ? L.shared_y : nullptr,
-                     out, st);
-  return hip_status(e, "k3moe_layer combine");
+  return layer_run(*shape, *weights, x, out, diag, workspace, static_cast<hipStream_t>(stream));
 }
 
 const char* k3moe_status_str(k3moe_status status) {

@@ -152,4 +152,16 @@ hipError_t launch_shared_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank
 hipError_t launch_combine(const k3moe_shape& s, const float* y_perm, const int32_t* pair_pos,
                           const float* topk_w, const float* shared_y, void* out, hipStream_t st);
 
+// Whole-layer entry points: the host-side validation (nothing enqueued; *need
+// = workspace bytes, 0 for an empty batch), the status of a workspace that is
+// too small, and the stages of a validated call on a workspace of at least
+// *need bytes.
+k3moe_status layer_validate(const k3moe_shape* shape, const k3moe_layer_weights* weights,
+                            const void* x, const void* out, const int32_t* diag, size_t* need);
+k3moe_status workspace_too_small(size_t have, size_t need);
+// K3MOE_EHIP with the HIP error's text as the last error.
+k3moe_status hip_failure(hipError_t e, const char* what);
+k3moe_status layer_run(const k3moe_shape& s, const k3moe_layer_weights& weights, const void* x,
+                       void* out, int32_t* diag, void* workspace, hipStream_t st);
+
 }  // namespace k3

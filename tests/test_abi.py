@@ -161,6 +161,28 @@ def test_bank_and_layer_validation():
                               None) == EINVAL
 
 
+def test_noalloc_layer_validation():
+    """The no-allocation layer validates like k3moe_layer before touching any
+    device, and refuses a call whose workspace would not fit its buffer."""
+    good = k3.make_bank(k3.FMT_MXFP4, 896, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
+    sh_ok = k3.make_bank(k3.FMT_BF16, 2, 7168, 2048, FAKE, None, FAKE, None)
+    w = k3.make_weights(FAKE, good, sh_ok)
+
+    def call(shape, weights=w, x=FAKE, out=FAKE):
+        return k3.lib.k3moe_layer_noalloc(ctypes.byref(shape), ctypes.byref(weights), x, out,
+                                          None, None)
+    assert k3.k3moe_workspace_bytes(big_shape(T=103), k3.OP_LAYER) <= k3.NOALLOC_SCRATCH_BYTES
+    assert k3.k3moe_workspace_bytes(big_shape(T=104), k3.OP_LAYER) > k3.NOALLOC_SCRATCH_BYTES
+    assert call(big_shape(T=104)) == EWORKSPACE
+    assert "workspace" in k3.lib.k3moe_last_error().decode()
+    assert call(big_shape(T=4096)) == EWORKSPACE
+    assert call(big_shape(T=1), x=None) == EINVAL
+    assert call(big_shape(T=1), out=FAKE + 4) == EALIGN
+    assert call(big_shape(T=1), weights=k3.make_weights(None, good, sh_ok)) == EINVAL
+    assert call(big_shape(T=1, d=7000)) == ESHAPE
+    assert call(big_shape(T=0)) == 0
+
+
 def test_permute_and_combine_validation():
     s = big_shape(T=4)
     assert k3.lib.k3moe_permute(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, None, FAKE * 256,
