@@ -14,6 +14,7 @@ Tensors (all row-major):
   w2        [E][d][f/2]     packed E2M1 codes
   w2_scale  [E][d][f/32]    E8M0 bytes
   shared w13 [S][2f_s][d], shared w2 [S][d][f_s]  bf16 bits, N(0, shared_sigma)
+  router_bias [E]           fp32, N(0, 0.05) (the sigmoid router's selection bias)
 Byte i of a packed row holds element 2i in its low nibble and 2i+1 in its high
 nibble; each 32-element block shares one scale byte.
 
@@ -33,7 +34,7 @@ from .configs import CONFIGS, ORDER, LayerConfig, get  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
-T_X, T_ROUTER, T_W13, T_W13S, T_W2, T_W2S, T_SH13, T_SH2, T_ZIPF = range(1, 10)
+T_X, T_ROUTER, T_W13, T_W13S, T_W2, T_W2S, T_SH13, T_SH2, T_ZIPF, T_RBIAS = range(1, 11)
 
 _host = None
 _dev = None
@@ -188,6 +189,12 @@ def router(cfg: LayerConfig) -> np.ndarray:
         b = zipf_bias(cfg)
         w[:, cfg.d - 1] = np.array([f64_to_bf16_bits(v) for v in b], dtype=np.uint16)
     return w
+
+
+def router_bias(cfg: LayerConfig, sigma: float = 0.05) -> np.ndarray:
+    """Per-expert selection bias [E] fp32, N(0, sigma), for the sigmoid router
+    (the pages give no distribution for it)."""
+    return _normal_f32(key(cfg.seed, T_RBIAS), 0, cfg.E, sigma)
 
 
 # --------------------------------------------------------------- routed experts

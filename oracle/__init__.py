@@ -8,7 +8,10 @@ the stages in order:
 
   route    logits = x Wr^T; top-k by (logit desc, id asc); ids ascending;
            softmax over the chosen logits            (router of the pages' MoE
-           layer: 16 of 896 experts per token — review page "at a glance")
+           layer: 16 of 896 experts per token — review page "at a glance");
+           or the pages' K3 router: top-k by sigmoid(l) + bias, weights the
+           unbiased sigmoid(l), raw or renormalised (review page,
+           "KDA/MLA/MoE" table)
   permute  stable counting sort of (token, slot) pairs by expert
   experts  per pair: y = Wd (silu(Wg x) * (Wu x)) on exactly decoded MXFP4
            weights (the pages multiply the 4-bit experts directly — README,
@@ -55,6 +58,7 @@ class Oracle:
         lib.oracle_mxfp4_decode.argtypes = [_I64, _I64, _I32, _P, _P, _P]
         lib.oracle_router_logits.argtypes = [_I64, _I32, _I32, _P, _P, _P]
         lib.oracle_topk_softmax.argtypes = [_I64, _I32, _I32, _P, _P, _P]
+        lib.oracle_topk_sigmoid.argtypes = [_I64, _I32, _I32, _P, _P, _I32, _P, _P]
         lib.oracle_permute.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
         lib.oracle_mxfp4_ffn.argtypes = [_I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P]
         lib.oracle_bf16_ffn.argtypes = [_I32, _I32, _P, _P, _I64, _P, _P]
@@ -101,9 +105,31 @@ class Oracle:
         self.lib.oracle_topk_softmax(T, E, k, _ptr(logits), _ptr(idx), _ptr(w))
         return idx, w
 
-    def route(self, x64, w_router, k):
+    def topk_sigmoid(self, logits: np.ndarray, k: int, bias: np.ndarray = None,
+                     norm: bool = False):
+        """The pages' K3 router: select by sigmoid(l) + bias, weights from the
+        unbiased sigmoid(l), optionally renormalised over the chosen."""
+        logits = np.ascontiguousarray(logits, dtype=np.float64)
+        T, E = logits.shape
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        assert b is None or b.shape == (E,)
+        idx = np.empty((T, k), dtype=np.int32)
+        w = np.empty((T, k), dtype=np.float64)
+        self.lib.oracle_topk_sigmoid(T, E, k, _ptr(logits), _ptr(b), 1 if norm else 0, _ptr(idx),
+                                     _ptr(w))
+        return idx, w
+
+    def route(self, x64, w_router, k, router: str = "softmax", bias=None):
+        """router: "softmax" (softmax over the chosen logits), "sigmoid" (the
+        pages' K3 router, raw sigmoid weights) or "sigmoid_norm" (the same,
+        weights renormalised over the chosen)."""
         logits = self.router_logits(x64, w_router)
-        idx, w = self.topk_softmax(logits, k)
+        if router == "softmax":
+            assert bias is None, "the softmax router takes no bias"
+            idx, w = self.topk_softmax(logits, k)
+        else:
+            assert router in ("sigmoid", "sigmoid_norm"), router
+            idx, w = self.topk_sigmoid(logits, k, bias, norm=router == "sigmoid_norm")
         return logits, idx, w
 
     # ------------------------------------------------------------ permute
@@ -180,12 +206,13 @@ class Oracle:
         return out
 
     # -------------------------------------------------------------- layer
-    def layer(self, x, w_router, get_expert, shared, k, E):
+    def layer(self, x, w_router, get_expert, shared, k, E, router="softmax", bias=None):
         """All stages on the full batch.  x: fp32 or bf16 bits [T][d];
         get_expert(e) -> dict of expert e's packed tensors; shared: dict of
-        bf16 banks or None.  Returns every intermediate in fp64/int32."""
+        bf16 banks or None; router and bias as for route().  Returns every
+        intermediate in fp64/int32."""
         x64 = to_f64(x)
-        logits, idx, w = self.route(x64, w_router, k)
+        logits, idx, w = self.route(x64, w_router, k, router, bias)
         counts, offsets, sorted_pair, pair_pos = self.permute(idx, E)
         y_perm = self.routed_ffn(x64, get_expert, counts, offsets, sorted_pair, k)
         shared_y = self.shared_ffn(shared, x64) if shared is not None else None

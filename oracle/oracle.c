@@ -121,6 +121,49 @@ void oracle_topk_softmax(int64_t T, int E, int k, const double* logits, int32_t*
   }
 }
 
+/* The pages' K3 router (kimi-k3-in-c review page, "KDA/MLA/MoE" table: the
+ * routing bias only bends the selection; the combine weights come from the
+ * unbiased sigmoid scores):
+ *   s[e]   = 1 / (1 + exp(-l[e]))                      (sigmoid score)
+ *   S_t    = the k experts with the largest s[e] + bias[e] (ties: lower id)
+ *   w[t][e] = s[e]                 (norm == 0), or
+ *           = s[e] / sum_{j in S_t} s[j]   (norm != 0; the pages do not say
+ *             whether the weights are renormalised, so both are offered)
+ * bias may be NULL (no bias).  idx rows ascending, w aligned. */
+static double sigmoid_score(double l) { return 1.0 / (1.0 + exp(-l)); }
+
+void oracle_topk_sigmoid(int64_t T, int E, int k, const double* logits, const float* bias,
+                         int norm, int32_t* idx, double* w) {
+#pragma omp parallel
+  {
+    char* taken = (char*)malloc((size_t)E);
+    double* sel = (double*)malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      const double* l = logits + t * E;
+      for (int e = 0; e < E; ++e) sel[e] = sigmoid_score(l[e]) + (bias ? (double)bias[e] : 0.0);
+      memset(taken, 0, (size_t)E);
+      for (int r = 0; r < k; ++r) { /* r-th best selection score among the not taken */
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+          if (!taken[e] && (best < 0 || ranks_before(sel[e], e, sel[best], best))) best = e;
+        taken[best] = 1;
+      }
+      int pos = 0;
+      for (int e = 0; e < E; ++e)
+        if (taken[e]) idx[t * k + pos++] = e;
+      double z = 0.0;
+      for (int r = 0; r < k; ++r) z += sigmoid_score(l[idx[t * k + r]]);
+      for (int r = 0; r < k; ++r) {
+        double s = sigmoid_score(l[idx[t * k + r]]);
+        w[t * k + r] = norm ? s / z : s;
+      }
+    }
+    free(taken);
+    free(sel);
+  }
+}
+
 /* Counting sort of the T*k (token, slot) pairs by expert, stable in pair
  * order: counts[e], offsets[e] = sum_{e' < e} counts[e'] (E+1 entries),
  * sorted_pair[p] = t*k + slot of the p-th pair, pair_pos its inverse. */

@@ -211,6 +211,50 @@ def pin_topk_bruteforce(o):
             assert abs(w[t].sum() - 1.0) <= 1e-15 * k
 
 
+def pin_sigmoid_router_fixture(o):
+    """The K3 router fixture: selection by sigmoid(l) + bias (the bias changes
+    the chosen pair in five of six rows), weights the unbiased sigmoid(l),
+    raw or renormalised over the chosen; without the bias the chosen pairs
+    are the unbiased ones."""
+    g = _golden("sigmoid_router_fixture.json")
+    logits = np.array(g["logits"], dtype=np.float64)
+    bias = np.array(g["bias"], dtype=np.float32)
+    k = g["k"]
+    idx, w_raw = o.topk_sigmoid(logits, k, bias, norm=False)
+    idx2, w_norm = o.topk_sigmoid(logits, k, bias, norm=True)
+    assert idx.tolist() == g["idx_biased"], idx.tolist()
+    assert np.array_equal(idx2, idx)
+    flips = sum(a != b for a, b in zip(g["idx_biased"], g["idx_unbiased"]))
+    assert flips == 5
+    idx0, _ = o.topk_sigmoid(logits, k, None)
+    assert idx0.tolist() == g["idx_unbiased"], idx0.tolist()
+    for t in range(logits.shape[0]):
+        s = [sigmoid(logits[t, e]) for e in g["idx_biased"][t]]
+        assert np.allclose(w_raw[t], s, rtol=4e-16, atol=0), (t, w_raw[t], s)
+        assert np.allclose(w_norm[t], np.array(s) / sum(s), rtol=8e-16, atol=0), (t, w_norm[t])
+
+
+def pin_sigmoid_router_bruteforce(o):
+    """Random logits and biases: the chosen set is the first k of a full
+    sort by (scipy's expit(l) + bias desc, id asc), listed by ascending id;
+    the weights are expit(l); with no bias the set is the logit top-k."""
+    from scipy.special import expit
+    rng = np.random.default_rng(11)
+    T, E, k = 40, 48, 6
+    logits = rng.standard_normal((T, E)) * 2.0
+    bias = (rng.standard_normal(E) * 0.3).astype(np.float32)
+    idx, w = o.topk_sigmoid(logits, k, bias)
+    for t in range(T):
+        score = expit(logits[t]) + bias.astype(np.float64)
+        order = sorted(range(E), key=lambda e: (-score[e], e))
+        want = sorted(order[:k])
+        assert idx[t].tolist() == want, (t, idx[t], want)
+        assert np.allclose(w[t], expit(logits[t, want]), rtol=4e-16, atol=0)
+    idx0, _ = o.topk_sigmoid(logits, k, None)
+    idx_l, _ = o.topk_softmax(logits, k)
+    assert np.array_equal(idx0, idx_l)
+
+
 def pin_topk_full_and_single(o):
     """k = E gives the full softmax over all experts; k = 1 gives weight 1 on
     the argmax."""

@@ -40,6 +40,14 @@ MUTANTS = {
                              "double acc = 0.0;"),
     "combine_keeps_zero_weights": ("if (ws != 0.0) acc += ws", "if (1) acc += ws"),
     "shared_down_transposed": ("bf16_value(w2[(int64_t)o * f + j])", "bf16_value(w2[(int64_t)j * d + o])"),
+    "sigmoid_bias_ignored": ("sel[e] = sigmoid_score(l[e]) + (bias ? (double)bias[e] : 0.0);",
+                             "sel[e] = sigmoid_score(l[e]);"),
+    "sigmoid_selects_on_logit": ("sel[e] = sigmoid_score(l[e]) + (bias ? (double)bias[e] : 0.0);",
+                                 "sel[e] = l[e] + (bias ? (double)bias[e] : 0.0);"),
+    "sigmoid_weights_biased": ("double s = sigmoid_score(l[idx[t * k + r]]);",
+                               "double s = sigmoid_score(l[idx[t * k + r]]) + (bias ? bias[idx[t * k + r]] : 0.0);"),
+    "sigmoid_norm_inverted": ("w[t * k + r] = norm ? s / z : s;", "w[t * k + r] = norm ? s : s / z;"),
+    "sigmoid_sign": ("return 1.0 / (1.0 + exp(-l));", "return 1.0 / (1.0 + exp(l));"),
     "bf16_decode_wrong": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)(b & 0xFF7F) << 16;"),
 }
 
