@@ -71,6 +71,18 @@ enum {
   K3MOE_OP_LAYER = 5,
   K3MOE_OP_EXPERT_GATEUP = 6
 };
+/* Router modes (k3moe_shape.router).
+ *   SOFTMAX:      S_t = k largest logits; w = softmax of the chosen logits.
+ *   SIGMOID:      the pages' K3 router (kimi-k3-in-c review page,
+ *                 "KDA/MLA/MoE" table: the routing bias bends only the
+ *                 selection; the combine weights come from the unbiased
+ *                 sigmoid scores): S_t = k largest sigmoid(l_e) + bias_e,
+ *                 w_e = sigmoid(l_e).
+ *   SIGMOID_NORM: the same selection, w_e = sigmoid(l_e) / sum over S_t of
+ *                 sigmoid (the pages do not say whether the weights are
+ *                 renormalised; both readings are offered).
+ * Ties go to the lower expert id in every mode. */
+enum { K3MOE_ROUTER_SOFTMAX = 0, K3MOE_ROUTER_SIGMOID = 1, K3MOE_ROUTER_SIGMOID_NORM = 2 };
 /* Path classes (k3moe_path_class). */
 enum { K3MOE_PATH_GEMV = 0, K3MOE_PATH_MFMA = 1 };
 
@@ -84,7 +96,11 @@ enum {
   K3MOE_DIAG_NONFINITE_LOGITS = 1, /* NaN/inf router logits seen */
   K3MOE_DIAG_BAD_EXPERT_IDS = 2,   /* expert ids outside [0, E) given to permute
                                       (such pairs are dropped) */
-  K3MOE_DIAG_RESERVED = 3,
+  K3MOE_DIAG_SCORE_NEAR_TIES = 3,  /* sigmoid router: tokens whose chosen set,
+                                      after the exact logit recheck, still hinges
+                                      on two selection scores closer than the fp64
+                                      sigmoid evaluation can order (the set could
+                                      differ from another fp64 implementation's) */
   K3MOE_DIAG_COUNT = 4
 };
 
@@ -92,7 +108,8 @@ enum {
  * returns K3MOE_OK and enqueues nothing), T * k < 2^31; 32 <= d <= 16384 and
  * d % 32 == 0; 32 <= f <= 16384 and f % 32 == 0; 1 <= k <= min(E, 64);
  * E <= 1024; 0 <= n_shared <= 8; f_shared % 32 == 0 (>= 32 when n_shared > 0);
- * x_dtype, out_dtype in {K3MOE_F32, K3MOE_BF16}. */
+ * x_dtype, out_dtype in {K3MOE_F32, K3MOE_BF16}; router one of
+ * K3MOE_ROUTER_* (0, the softmax router, for a zero-initialised shape). */
 typedef struct k3moe_shape {
   int64_t T;         /* tokens */
   int32_t d;         /* hidden size */
@@ -103,6 +120,7 @@ typedef struct k3moe_shape {
   int32_t f_shared;  /* shared expert intermediate size */
   int32_t x_dtype;   /* activations x [T][d] */
   int32_t out_dtype; /* layer output [T][d] */
+  int32_t router;    /* K3MOE_ROUTER_* */
 } k3moe_shape;
 
 /* A bank of experts, expert-major (each expert's bytes contiguous).
@@ -128,6 +146,8 @@ typedef struct k3moe_layer_weights {
   const void* w_router;      /* [E][d] bf16 */
   k3moe_expert_bank routed;  /* MXFP4, n_experts = E, f = shape.f */
   k3moe_expert_bank shared;  /* BF16, n_experts = n_shared, f = shape.f_shared */
+  const float* router_bias;  /* [E] fp32 selection bias of the sigmoid routers,
+                                NULL = none; must be NULL for the softmax router */
 } k3moe_layer_weights;
 
 /* Bytes of workspace `op` needs for `shape` (0 for an invalid shape).  The
@@ -161,25 +181,32 @@ uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols);
  * bit.  Returns K3MOE_PATH_GEMV for an invalid shape. */
 int k3moe_path_class(const k3moe_shape* shape);
 
-/* Router + top-k + softmax.  Passage: 16 of 896 routed experts chosen per
+/* Router + top-k + weights.  Passage: 16 of 896 routed experts chosen per
  * token by a linear router over the hidden state (kimi-k3-in-c review page,
  * "at a glance" and "KDA/MLA/MoE" tables; translated README, "shard census");
- * the softmax-over-the-chosen weights and the tie rule are this library's
- * reading (the pages' model uses sigmoid scores).
- * x [T][d] (x_dtype), w_router [E][d] bf16 ->
+ * shape->router picks the selection and weight rule (K3MOE_ROUTER_*: the
+ * pages' sigmoid router with its selection-only bias, or the softmax router
+ * of the workload definitions); the tie rule is this library's reading.
+ * x [T][d] (x_dtype), w_router [E][d] bf16, router_bias [E] fp32 (sigmoid
+ * routers only, NULL = no bias) ->
  *   topk_idx [T][k] int32, each row in ascending expert id;
- *   topk_w   [T][k] fp32, aligned with topk_idx, summing to 1 per token;
+ *   topk_w   [T][k] fp32, aligned with topk_idx (summing to 1 per token for
+ *            the softmax and renormalised sigmoid routers);
  *   logits   [T][E] fp32 (optional, NULL = not written).
  * The chosen set equals the set an exact evaluation of the logits in fp64
  * (ascending i) picks: near-ties at the k/k+1 boundary are re-evaluated
- * exactly on the device (counted in diag[K3MOE_DIAG_RECHECKED_TOKENS]).
+ * exactly on the device (counted in diag[K3MOE_DIAG_RECHECKED_TOKENS]).  For
+ * the sigmoid routers the selection scores are evaluated in fp64 from those
+ * logits; see K3MOE_DIAG_SCORE_NEAR_TIES for the one case left open.
  * diag: optional K3MOE_DIAG_COUNT counters (NULL = not collected); non-finite
  * logits are counted in diag[K3MOE_DIAG_NONFINITE_LOGITS].
- * Errors: EINVAL (NULL x, w_router, topk_idx, topk_w), EALIGN, EWORKSPACE.
+ * Errors: EINVAL (NULL x, w_router, topk_idx, topk_w; a bias with the
+ * softmax router), EUNSUPPORTED (an unknown router), EALIGN, EWORKSPACE.
  * Workspace: k3moe_workspace_bytes(shape, K3MOE_OP_ROUTE). */
 k3moe_status k3moe_route(const k3moe_shape* shape, const void* x, const void* w_router,
-                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* diag,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         const float* router_bias, int32_t* topk_idx, float* topk_w,
+                         float* logits, int32_t* diag, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Counting sort of the T*k (token, slot) pairs by expert, stable in pair
  * order (pair p = t*k + slot).  Passage: the experts are gathered per layer

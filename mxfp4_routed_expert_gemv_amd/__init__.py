@@ -22,7 +22,11 @@ FMT_MXFP4, FMT_BF16 = 0, 1
 (OP_ROUTE, OP_PERMUTE, OP_EXPERT_FFN, OP_SHARED_FFN, OP_COMBINE, OP_LAYER,
  OP_EXPERT_GATEUP) = range(7)
 PATH_GEMV, PATH_MFMA = 0, 1
+ROUTER_SOFTMAX, ROUTER_SIGMOID, ROUTER_SIGMOID_NORM = 0, 1, 2
+ROUTERS = {"softmax": ROUTER_SOFTMAX, "sigmoid": ROUTER_SIGMOID,
+           "sigmoid_norm": ROUTER_SIGMOID_NORM}
 DIAG_RECHECKED_TOKENS, DIAG_NONFINITE_LOGITS, DIAG_BAD_EXPERT_IDS = 0, 1, 2
+DIAG_SCORE_NEAR_TIES = 3
 DIAG_COUNT = 4
 
 STATUS = {0: "K3MOE_OK", 1: "K3MOE_EINVAL", 2: "K3MOE_ESHAPE", 3: "K3MOE_EALIGN",
@@ -38,7 +42,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("f", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("f_shared", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("router", ctypes.c_int32)]
 
 
 class ExpertBank(ctypes.Structure):
@@ -49,7 +53,8 @@ class ExpertBank(ctypes.Structure):
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [("w_router", ctypes.c_void_p), ("routed", ExpertBank), ("shared", ExpertBank)]
+    _fields_ = [("w_router", ctypes.c_void_p), ("routed", ExpertBank), ("shared", ExpertBank),
+                ("router_bias", ctypes.c_void_p)]
 
 
 class K3moeError(RuntimeError):
@@ -76,7 +81,7 @@ def _load():
     lib.k3moe_path_class.restype = ctypes.c_int
     lib.k3moe_path_class.argtypes = [SP]
     lib.k3moe_route.restype = ctypes.c_int
-    lib.k3moe_route.argtypes = [SP, P, P, P, P, P, P, P, S, P]
+    lib.k3moe_route.argtypes = [SP, P, P, P, P, P, P, P, P, S, P]
     lib.k3moe_permute.restype = ctypes.c_int
     lib.k3moe_permute.argtypes = [SP, P, P, P, P, P, P, P, S, P]
     lib.k3moe_expert_ffn.restype = ctypes.c_int
@@ -148,10 +153,11 @@ def k3moe_path_class(shape: Shape) -> int:
 
 
 def k3moe_route(shape, x, w_router, topk_idx, topk_w, logits=None, diag=None, workspace=None,
-                stream=None):
+                stream=None, router_bias=None):
     wp, wb = _ws(workspace)
-    _check(lib.k3moe_route(ctypes.byref(shape), _addr(x), _addr(w_router), _addr(topk_idx),
-                           _addr(topk_w), _addr(logits), _addr(diag), wp, wb, _stream(stream)))
+    _check(lib.k3moe_route(ctypes.byref(shape), _addr(x), _addr(w_router), _addr(router_bias),
+                           _addr(topk_idx), _addr(topk_w), _addr(logits), _addr(diag), wp, wb,
+                           _stream(stream)))
 
 
 def k3moe_permute(shape, topk_idx, counts, offsets, sorted_pair, pair_pos, diag=None,
@@ -208,13 +214,14 @@ def k3moe_layer_noalloc(shape, weights: LayerWeights, x, out, diag=None, stream=
 
 
 # --------------------------------------------------------- struct builders
-def make_shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype) -> Shape:
-    return Shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype)
+def make_shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router=ROUTER_SOFTMAX) -> Shape:
+    return Shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router)
 
 
 def make_bank(fmt, n, d, f, w13, w13_scale, w2, w2_scale) -> ExpertBank:
     return ExpertBank(fmt, n, d, f, _addr(w13), _addr(w13_scale), _addr(w2), _addr(w2_scale))
 
 
-def make_weights(w_router, routed: ExpertBank, shared: ExpertBank) -> LayerWeights:
-    return LayerWeights(_addr(w_router), routed, shared)
+def make_weights(w_router, routed: ExpertBank, shared: ExpertBank,
+                 router_bias=None) -> LayerWeights:
+    return LayerWeights(_addr(w_router), routed, shared, _addr(router_bias))

@@ -65,6 +65,9 @@ k3moe_status check_shape(const k3moe_shape* s) {
     return fail(K3MOE_EUNSUPPORTED, "x_dtype %d is not F32 or BF16", s->x_dtype);
   if (s->out_dtype != K3MOE_F32 && s->out_dtype != K3MOE_BF16)
     return fail(K3MOE_EUNSUPPORTED, "out_dtype %d is not F32 or BF16", s->out_dtype);
+  if (s->router != K3MOE_ROUTER_SOFTMAX && s->router != K3MOE_ROUTER_SIGMOID &&
+      s->router != K3MOE_ROUTER_SIGMOID_NORM)
+    return fail(K3MOE_EUNSUPPORTED, "router %d is not one of K3MOE_ROUTER_*", s->router);
   if (s->d < 32 || s->d > 16384 || s->d % 32)
     return fail(K3MOE_ESHAPE, "d = %d: need 32 <= d <= 16384, d %% 32 == 0", s->d);
   if (s->f < 32 || s->f > 16384 || s->f % 32)
@@ -126,6 +129,12 @@ k3moe_status check_shared_bank(const k3moe_shape& s, const k3moe_expert_bank* b)
   K3_CHECK(need_ptr(b->w13, "shared.w13"));
   K3_CHECK(need_ptr(b->w2, "shared.w2"));
   return K3MOE_OK;
+}
+
+k3moe_status check_bias(const k3moe_shape& s, const float* bias) {
+  if (bias && s.router == K3MOE_ROUTER_SOFTMAX)
+    return fail(K3MOE_EINVAL, "router_bias is given but the softmax router takes none");
+  return opt_ptr(bias, "router_bias");
 }
 
 k3moe_status hip_status(hipError_t e, const char* what) {
@@ -225,6 +234,7 @@ k3moe_status layer_validate(const k3moe_shape* shape, const k3moe_layer_weights*
   K3_CHECK(check_shared_bank(s, &weights->shared));
   if (s.T == 0) return ok();
   K3_CHECK(need_ptr(weights->w_router, "w_router"));
+  K3_CHECK(check_bias(s, weights->router_bias));
   K3_CHECK(need_ptr(x, "x"));
   K3_CHECK(need_ptr(out, "out"));
   K3_CHECK(opt_ptr(diag, "diag"));
@@ -260,8 +270,9 @@ k3moe_status layer_run(const k3moe_shape& s, const k3moe_layer_weights& wts, con
     hipError_t e = launch_router_logits(s, x, static_cast<const uint16_t*>(weights->w_router),
                                         rws, st);
     if (e != hipSuccess) return hip_status(e, "k3moe_layer router");
-    e = launch_topk_shared_t1(s, x, static_cast<const uint16_t*>(weights->w_router), L.topk_idx,
-                              L.topk_w, diag, rws, perm, weights->shared, sws.h, st);
+    e = launch_topk_shared_t1(s, x, static_cast<const uint16_t*>(weights->w_router),
+                              weights->router_bias, L.topk_idx, L.topk_w, diag, rws, perm,
+                              weights->shared, sws.h, st);
     if (e != hipSuccess) return hip_status(e, "k3moe_layer top-k + shared gate/up");
     e = launch_expert_ffn(s, weights->routed, x, L.offsets, L.sorted_pair, L.y_perm,
                           carve_expert(s, L.scratch, nullptr), st);
@@ -284,9 +295,9 @@ k3moe_status layer_run(const k3moe_shape& s, const k3moe_layer_weights& wts, con
     perm.sorted_pair = L.sorted_pair;
     perm.pair_pos = L.pair_pos;
   }
-  hipError_t e = launch_route(s, x, static_cast<const uint16_t*>(weights->w_router), L.topk_idx,
-                              L.topk_w, nullptr, diag, carve_route(s, L.scratch, nullptr), st,
-                              perm);
+  hipError_t e = launch_route(s, x, static_cast<const uint16_t*>(weights->w_router),
+                              weights->router_bias, L.topk_idx, L.topk_w, nullptr, diag,
+                              carve_route(s, L.scratch, nullptr), st, perm);
   if (e != hipSuccess) return hip_status(e, "k3moe_layer route");
   if (s.T != 1) {
     e = launch_permute(s, L.topk_idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, diag,
@@ -355,13 +366,15 @@ int k3moe_path_class(const k3moe_shape* shape) {
 }
 
 k3moe_status k3moe_route(const k3moe_shape* shape, const void* x, const void* w_router,
-                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* diag,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         const float* router_bias, int32_t* topk_idx, float* topk_w,
+                         float* logits, int32_t* diag, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   K3_CHECK(check_shape(shape));
   const k3moe_shape& s = *shape;
   if (s.T == 0) return ok();
   K3_CHECK(need_ptr(x, "x"));
   K3_CHECK(need_ptr(w_router, "w_router"));
+  K3_CHECK(check_bias(s, router_bias));
   K3_CHECK(need_ptr(topk_idx, "topk_idx"));
   K3_CHECK(need_ptr(topk_w, "topk_w"));
   K3_CHECK(opt_ptr(logits, "logits"));
@@ -370,7 +383,8 @@ k3moe_status k3moe_route(const k3moe_shape* shape, const void* x, const void* w_
   carve_route(s, nullptr, &need);
   K3_CHECK(check_ws(workspace, workspace_bytes, need));
   const RouteWs ws = carve_route(s, workspace, nullptr);
-  return hip_status(launch_route(s, x, static_cast<const uint16_t*>(w_router), topk_idx, topk_w,
+  return hip_status(launch_route(s, x, static_cast<const uint16_t*>(w_router), router_bias,
+                                 topk_idx, topk_w,
                                  logits, diag, ws, static_cast<hipStream_t>(stream)),
                     "k3moe_route launch");
 }

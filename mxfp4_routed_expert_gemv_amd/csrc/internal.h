@@ -99,18 +99,18 @@ struct CombineArgs {
 };
 
 // Launchers: enqueue on `st`, return hipSuccess or the launch error.
-hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, int32_t* idx,
-                        float* w, float* logits_out, int32_t* diag, const RouteWs& ws,
-                        hipStream_t st, const PermOut& perm = PermOut());
+hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, const float* bias,
+                        int32_t* idx, float* w, float* logits_out, int32_t* diag,
+                        const RouteWs& ws, hipStream_t st, const PermOut& perm = PermOut());
 // The two halves of launch_route, and the one-token selection fused with the
 // shared experts' gate/up (which writes SharedWs::h).
 hipError_t launch_router_logits(const k3moe_shape& s, const void* x, const uint16_t* wr,
                                 const RouteWs& ws, hipStream_t st);
 bool topk_shared_t1_ok(const k3moe_shape& s);
 hipError_t launch_topk_shared_t1(const k3moe_shape& s, const void* x, const uint16_t* wr,
-                                 int32_t* idx, float* w, int32_t* diag, const RouteWs& ws,
-                                 const PermOut& perm, const k3moe_expert_bank& shared, float* hs,
-                                 hipStream_t st);
+                                 const float* bias, int32_t* idx, float* w, int32_t* diag,
+                                 const RouteWs& ws, const PermOut& perm,
+                                 const k3moe_expert_bank& shared, float* hs, hipStream_t st);
 bool shared_down_t1_ok(const k3moe_shape& s);
 hipError_t launch_shared_down_t1(const k3moe_shape& s, const k3moe_expert_bank& bank,
                                  const SharedWs& ws, float* y, hipStream_t st,

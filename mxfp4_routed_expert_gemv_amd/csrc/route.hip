@@ -12,6 +12,14 @@
 //      when that fails it re-evaluates the undecided experts sequentially in
 //      fp64, ascending i — the exact same operations as the oracle, hence the
 //      same bits — and selects among them.
+// The pages' own K3 router (kimi-k3-in-c review page, "KDA/MLA/MoE" table)
+// is the other mode: selection by sigmoid(l) + bias, where the bias bends
+// only the selection, and weights from the unbiased sigmoid(l), raw or
+// renormalised over the chosen.  Its selection key carries the logit's bound
+// through the sigmoid (slope at most 1/4) plus the fp64 evaluation of the
+// sigmoid and the bias addition on either side; after a recheck the logits
+// are the oracle's bits and only the sigmoid evaluation can still separate
+// the two sides, which is counted when it could decide the set.
 #include "internal.h"
 #include "kern_common.h"
 #include "decode_t1.h"
@@ -289,12 +297,26 @@ __device__ __forceinline__ void wave_sync() {
 // Token t's selection by one wave.  Lane l holds experts l + 64 j as
 // order-preserving 64-bit keys; each of k rounds takes the wave maximum with
 // DPP, ties between lanes going to the lower expert id.
+// fp64 sigmoid score, 1 / (1 + e^-l); the same formula as the oracle's.
+__device__ __forceinline__ double sigmoid_score(double l) { return 1.0 / (1.0 + exp(-l)); }
+// Relative bound on the difference between the two sides' fp64 selection
+// scores for the same logit: each side's exp within 1 ulp, the sigmoid's add
+// and divide and the bias add within half an ulp each, with margin.
+constexpr double kScoreEps = 8.0 * 0x1p-53;
+
+struct RouterMode {
+  int mode = K3MOE_ROUTER_SOFTMAX;
+  const float* bias = nullptr;   // [E] fp32 or nullptr (sigmoid modes only)
+};
+
 template <bool XF32>
 __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restrict__ logits,
                            const float* __restrict__ lbound, const void* __restrict__ x,
                            const uint16_t* __restrict__ wr, int32_t* __restrict__ idx_out,
                            float* __restrict__ w_out, float* __restrict__ logits_out,
-                           int32_t* __restrict__ diag, int d, int E, int k, const PermOut& perm) {
+                           int32_t* __restrict__ diag, int d, int E, int k, const PermOut& perm,
+                           const RouterMode rm) {
+  const bool sig = rm.mode != K3MOE_ROUTER_SOFTMAX;
   double* candL = sm.candL;
   int* candId = sm.candId;
   int* candTaken = sm.candTaken;
@@ -308,18 +330,29 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
   int nonfin = 0;
   // Every load is issued (clamped index) before any is used.
   double lv[kMaxJ];
+  float bias[kMaxJ];
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) {
     const int e = min(lane + kWave * j, E - 1);
     lv[j] = lrow[e];
     b[j] = brow[e];
+    bias[j] = rm.bias ? rm.bias[e] : 0.0f;
   }
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) {
     const int e = lane + kWave * j;
     const bool ok = j < nj && e < E;
     if (ok && !isfinite(lv[j])) ++nonfin;
-    key[j] = ok ? order_key(isnan(lv[j]) ? -INFINITY : lv[j]) : 0;
+    if (sig) {
+      // selection score and its bound: the logit's bound through the slope
+      // of the sigmoid (at most 1/4), plus the two sides' score evaluation
+      const double sc = sigmoid_score(lv[j]) + (double)bias[j];
+      key[j] = ok ? order_key(isnan(sc) ? -INFINITY : sc) : 0;
+      b[j] = (float)((0.25 * (double)b[j] + kScoreEps * (1.0 + fabs((double)bias[j]))) *
+                     (1.0 + 0x1p-20));
+    } else {
+      key[j] = ok ? order_key(isnan(lv[j]) ? -INFINITY : lv[j]) : 0;
+    }
     // masked with bit operations so the loads above stay unconditional
     b[j] = __uint_as_float(__float_as_uint(b[j]) & (0u - (uint32_t)ok));
   }
@@ -383,7 +416,8 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
     for (int q = lane; q < 1024; q += kWave) chosen[q] = 0;
     wave_sync();
     for (int q = lane; q < n; q += kWave) {
-      candL[q] = exact_logit<XF32>(x, wr, t, candId[q], d);
+      const double l = exact_logit<XF32>(x, wr, t, candId[q], d);
+      candL[q] = sig ? sigmoid_score(l) + (double)(rm.bias ? rm.bias[candId[q]] : 0.0f) : l;
       candTaken[q] = 0;
     }
     wave_sync();
@@ -410,12 +444,28 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
       if (j < nj && e < E && chosen[e]) taken |= 1u << j;
     }
     if (lane == 0 && diag) atomicAdd(&diag[K3MOE_DIAG_RECHECKED_TOKENS], 1);
+    if (sig) {
+      // with the logits exact, two different scores closer than the sides'
+      // evaluation bound could still order differently on the two sides
+      double lo_in = INFINITY, hi_out = -INFINITY, mag = 0.0;
+      for (int q = lane; q < n; q += kWave) {
+        mag = fmax(mag, fabs(candL[q]));
+        if (chosen[candId[q]]) lo_in = fmin(lo_in, candL[q]);
+        else hi_out = fmax(hi_out, candL[q]);
+      }
+      lo_in = wave_min(lo_in);
+      hi_out = -wave_min(-hi_out);
+      mag = -wave_min(-mag);
+      const double gap = lo_in - hi_out;
+      if (lane == 0 && diag && gap > 0.0 && gap <= 2.0 * kScoreEps * (2.0 + mag))
+        atomicAdd(&diag[K3MOE_DIAG_SCORE_NEAR_TIES], 1);
+    }
   }
 
-  // Softmax over the chosen logits; outputs in ascending expert id.  The
-  // chosen (id, logit) pairs are first compacted in ascending id into
-  // chosen[] / candL[] (slot p = rank among the chosen), so each slot's
-  // exponential is evaluated once, by lane p.
+  // Softmax over the chosen logits (or their sigmoid scores); outputs in
+  // ascending expert id.  The chosen (id, logit) pairs are first compacted in
+  // ascending id into chosen[] / candL[] (slot p = rank among the chosen), so
+  // each slot's exponential is evaluated once, by lane p.
   uint64_t kmax = 0;
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j)
@@ -429,7 +479,7 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
     const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
     if (mine) {
       chosen[pos] = lane + kWave * j;
-      candL[pos] = key_value(key[j]);
+      candL[pos] = sig ? lv[j] : key_value(key[j]);
     }
     // one token: expert e = lane + 64 j has count 0/1 and offset = the
     // number of chosen experts below it (ids run j-major, then lane)
@@ -449,11 +499,11 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
   }
   wave_sync();
   // k <= 64: one slot per lane; z summed by the fixed butterfly
-  const double ep = lane < k ? exp(candL[lane] - m) : 0.0;
+  const double ep = lane < k ? (sig ? sigmoid_score(candL[lane]) : exp(candL[lane] - m)) : 0.0;
   const double z = wave_sum(ep);
   if (lane < k) {
     idx_out[(size_t)t * k + lane] = chosen[lane];
-    w_out[(size_t)t * k + lane] = (float)(ep / z);
+    w_out[(size_t)t * k + lane] = (float)(rm.mode == K3MOE_ROUTER_SIGMOID ? ep : ep / z);
   }
 }
 
@@ -466,11 +516,11 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
                                                    float* __restrict__ w_out,
                                                    float* __restrict__ logits_out,
                                                    int32_t* __restrict__ diag, int T, int d, int E,
-                                                   int k, PermOut perm) {
+                                                   int k, PermOut perm, RouterMode rm) {
   __shared__ TopkLds sm;
   if ((int)blockIdx.x >= T) return;
   topk_token<XF32>(blockIdx.x, threadIdx.x, sm, logits, lbound, x, wr, idx_out, w_out,
-                   logits_out, diag, d, E, k, perm);
+                   logits_out, diag, d, E, k, perm, rm);
 }
 
 // fp64 router tiles: 16 x 16 up to 64 tokens, 32 x 16 up to 256, else 32 x 32,
@@ -498,7 +548,7 @@ __global__ __launch_bounds__(256) void topk_shared_t1(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ diag, int d,
     int E, int k, PermOut perm, const uint16_t* __restrict__ w13s, float* __restrict__ hs, int fs,
-    int S) {
+    int S, RouterMode rm) {
   __shared__ TopkLds sm;
   __shared__ uint4 xs[kSgU * kWave];
   stage_row(reinterpret_cast<const uint4*>(x), d / 8, xs);
@@ -507,7 +557,7 @@ __global__ __launch_bounds__(256) void topk_shared_t1(
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gw == 0) {
     topk_token<false>(0, lane, sm, logits, lbound, x, wr, idx_out, w_out, nullptr, diag, d, E, k,
-                      perm);
+                      perm, rm);
   } else if (gw - 1 < S * fs) {
     shared_gateup_item(gw - 1, w13s, xs, hs, d, fs, lane);
   }
@@ -534,20 +584,26 @@ bool topk_shared_t1_ok(const k3moe_shape& s) {
 }
 
 hipError_t launch_topk_shared_t1(const k3moe_shape& s, const void* x, const uint16_t* wr,
-                                 int32_t* idx, float* w, int32_t* diag, const RouteWs& ws,
-                                 const PermOut& perm, const k3moe_expert_bank& shared, float* hs,
-                                 hipStream_t st) {
+                                 const float* bias, int32_t* idx, float* w, int32_t* diag,
+                                 const RouteWs& ws, const PermOut& perm,
+                                 const k3moe_expert_bank& shared, float* hs, hipStream_t st) {
   if (!topk_shared_t1_ok(s)) return hipErrorInvalidValue;
   const int items = shared.n_experts * shared.f;
+  RouterMode rm;
+  rm.mode = s.router;
+  rm.bias = bias;
   topk_shared_t1<<<(items + 1 + 3) / 4, 256, 0, st>>>(
       ws.logits, ws.lbound, static_cast<const uint16_t*>(x), wr, idx, w, diag, s.d, s.E, s.k, perm,
-      static_cast<const uint16_t*>(shared.w13), hs, shared.f, shared.n_experts);
+      static_cast<const uint16_t*>(shared.w13), hs, shared.f, shared.n_experts, rm);
   return hipGetLastError();
 }
 
-hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, int32_t* idx,
-                        float* w, float* logits_out, int32_t* diag, const RouteWs& ws,
-                        hipStream_t st, const PermOut& perm) {
+hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr, const float* bias,
+                        int32_t* idx, float* w, float* logits_out, int32_t* diag,
+                        const RouteWs& ws, hipStream_t st, const PermOut& perm) {
+  RouterMode rm;
+  rm.mode = s.router;
+  rm.bias = bias;
   if (perm.counts && s.T != 1) return hipErrorInvalidValue;
   const int T = (int)s.T;
   const bool xf32 = s.x_dtype == K3MOE_F32;
@@ -562,10 +618,10 @@ hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr,
   if (err != hipSuccess) return err;
   if (xf32)
     topk_softmax<true><<<T, 64, 0, st>>>(ws.logits, ws.lbound, x, wr, idx, w, logits_out, diag,
-                                         T, s.d, s.E, s.k, perm);
+                                         T, s.d, s.E, s.k, perm, rm);
   else
     topk_softmax<false><<<T, 64, 0, st>>>(ws.logits, ws.lbound, x, wr, idx, w, logits_out, diag,
-                                          T, s.d, s.E, s.k, perm);
+                                          T, s.d, s.E, s.k, perm, rm);
   return hipGetLastError();
 }
 

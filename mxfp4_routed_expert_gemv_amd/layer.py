@@ -4,7 +4,8 @@ computation happens in libk3moe's kernels; this file only marshals."""
 import torch
 
 from . import (BF16, DIAG_COUNT, F32, FMT_BF16, FMT_MXFP4, OP_EXPERT_FFN, OP_EXPERT_GATEUP,
-               OP_LAYER, OP_PERMUTE, OP_ROUTE, OP_SHARED_FFN, k3moe_combine, k3moe_expert_down,
+               OP_LAYER, OP_PERMUTE, OP_ROUTE, OP_SHARED_FFN, ROUTERS, k3moe_combine,
+               k3moe_expert_down,
                k3moe_expert_ffn, k3moe_expert_gateup, k3moe_layer, k3moe_path_class,
                k3moe_permute, k3moe_route, k3moe_shared_ffn, k3moe_workspace_bytes, make_bank, make_shape, make_weights)
 
@@ -14,10 +15,12 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16}
 class MoELayer:
     """One routed MoE FFN layer.  routed: dict of uint8 tensors w13 [E][2f][d/2],
     w13_scale [E][2f][d/32], w2 [E][d][f/2], w2_scale [E][d][f/32]; shared:
-    dict of bf16 tensors w13 [S][2fs][d], w2 [S][d][fs] (or empty)."""
+    dict of bf16 tensors w13 [S][2fs][d], w2 [S][d][fs] (or empty); router:
+    "softmax", "sigmoid" or "sigmoid_norm", with router_bias an fp32 [E]
+    tensor (or None) for the sigmoid routers."""
 
     def __init__(self, w_router, routed: dict, shared: dict, k: int,
-                 out_dtype=torch.bfloat16):
+                 out_dtype=torch.bfloat16, router: str = "softmax", router_bias=None):
         self.w_router = w_router
         self.routed = routed
         self.shared = shared
@@ -27,17 +30,19 @@ class MoELayer:
         self.n_shared = shared["w13"].shape[0] if shared else 0
         self.f_shared = shared["w13"].shape[1] // 2 if shared else 0
         self.out_dtype = out_dtype
+        self.router = ROUTERS[router]
+        self.router_bias = router_bias
         self.routed_bank = make_bank(FMT_MXFP4, self.E, self.d, self.f, routed["w13"],
                                      routed["w13_scale"], routed["w2"], routed["w2_scale"])
         self.shared_bank = make_bank(FMT_BF16, self.n_shared, self.d, self.f_shared,
                                      shared.get("w13"), None, shared.get("w2"), None)
-        self.weights = make_weights(w_router, self.routed_bank, self.shared_bank)
+        self.weights = make_weights(w_router, self.routed_bank, self.shared_bank, router_bias)
 
     # ------------------------------------------------------------ helpers
     def shape(self, T: int, x_dtype=torch.bfloat16, out_dtype=None):
         out_dtype = self.out_dtype if out_dtype is None else out_dtype
         return make_shape(T, self.d, self.f, self.E, self.k, self.n_shared, self.f_shared,
-                          _DT[x_dtype], _DT[out_dtype])
+                          _DT[x_dtype], _DT[out_dtype], self.router)
 
     def workspace(self, shape, op):
         n = k3moe_workspace_bytes(shape, op)
@@ -56,7 +61,8 @@ class MoELayer:
         idx = torch.empty((T, self.k), dtype=torch.int32, device=self._dev())
         w = torch.empty((T, self.k), dtype=torch.float32, device=self._dev())
         logits = torch.empty((T, self.E), dtype=torch.float32, device=self._dev()) if want_logits else None
-        k3moe_route(s, x, self.w_router, idx, w, logits, diag, self.workspace(s, OP_ROUTE), stream)
+        k3moe_route(s, x, self.w_router, idx, w, logits, diag, self.workspace(s, OP_ROUTE), stream,
+                    router_bias=self.router_bias)
         return idx, w, logits
 
     def permute(self, idx, diag=None, stream=None):

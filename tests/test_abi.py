@@ -90,13 +90,15 @@ def test_gateup_workspace_validation():
     assert gateup(big, FAKE * 256 + 16, need) == EALIGN
 
 
-def _route(shape, x=FAKE, wr=FAKE, idx=FAKE, w=FAKE, ws=(FAKE * 256, 1 << 40)):
-    return k3.lib.k3moe_route(ctypes.byref(shape), x, wr, idx, w, None, None, ws[0], ws[1], None)
+def _route(shape, x=FAKE, wr=FAKE, idx=FAKE, w=FAKE, ws=(FAKE * 256, 1 << 40), bias=None):
+    return k3.lib.k3moe_route(ctypes.byref(shape), x, wr, bias, idx, w, None, None, ws[0], ws[1],
+                              None)
 
 
 def test_route_validation():
     assert _route(big_shape(T=-1)) == EINVAL
-    assert k3.lib.k3moe_route(None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, None) == EINVAL
+    assert k3.lib.k3moe_route(None, FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, 1,
+                              None) == EINVAL
     assert _route(big_shape(d=7170)) == ESHAPE
     assert _route(big_shape(d=16)) == ESHAPE
     assert _route(big_shape(f=2050)) == ESHAPE
@@ -106,6 +108,12 @@ def test_route_validation():
     assert _route(big_shape(T=1 << 28)) == ESHAPE          # T * k >= 2^31
     assert _route(big_shape(x_dtype=7)) == EUNSUPPORTED
     assert _route(big_shape(out_dtype=3)) == EUNSUPPORTED
+    # router modes: an unknown one, a bias given to the softmax router, a
+    # misaligned bias
+    assert _route(big_shape(router=3)) == EUNSUPPORTED
+    assert _route(big_shape(), bias=FAKE) == EINVAL
+    assert _route(big_shape(router=k3.ROUTER_SIGMOID), bias=FAKE + 4) == EALIGN
+    assert _route(big_shape(router=k3.ROUTER_SIGMOID_NORM, T=0), bias=FAKE) == 0
     assert _route(big_shape(), x=None) == EINVAL
     assert _route(big_shape(), wr=FAKE + 8) == EALIGN
     assert _route(big_shape(), ws=(None, 0)) == EWORKSPACE
@@ -151,6 +159,7 @@ def test_bank_and_layer_validation():
         return k3.lib.k3moe_layer(ctypes.byref(shape), ctypes.byref(weights), x, out, None,
                                   ws[0], ws[1], None)
     assert layer(k3.make_weights(None, good, sh_ok)) == EINVAL
+    assert layer(k3.make_weights(FAKE, good, sh_ok, router_bias=FAKE)) == EINVAL   # softmax
     assert layer(k3.make_weights(FAKE, bf, sh_ok)) == EUNSUPPORTED
     assert layer(k3.make_weights(FAKE, good, k3.make_bank(k3.FMT_BF16, 1, 7168, 2048, FAKE, None, FAKE, None))) == EINVAL
     assert layer(w_ok, out=None) == EINVAL
