@@ -61,6 +61,8 @@ class Oracle:
         lib.oracle_topk_sigmoid.argtypes = [_I64, _I32, _I32, _P, _P, _I32, _P, _P]
         lib.oracle_permute.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
         lib.oracle_mxfp4_ffn.argtypes = [_I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P]
+        lib.oracle_quantize_mxfp4.argtypes = [_I64, _P, _P, _P]
+        lib.oracle_mxfp4_ffn_qact.argtypes = [_I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P]
         lib.oracle_bf16_ffn.argtypes = [_I32, _I32, _P, _P, _I64, _P, _P]
         lib.oracle_combine.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
         lib.oracle_threads.restype = _I32
@@ -162,6 +164,33 @@ class Oracle:
                                   _ptr(x64), _ptr(y), _ptr(h))
         return (y, h) if want_h else y
 
+    def quantize_mxfp4(self, v: np.ndarray):
+        """OCP MX quantisation to MXFP4 of rows whose length is a multiple of
+        32: [..., n] fp64 -> (codes [..., n/2] u8 packed, scales [..., n/32] u8)."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        assert v.shape[-1] % 32 == 0
+        nblk = v.size // 32
+        codes = np.empty(v.shape[:-1] + (v.shape[-1] // 2,), dtype=np.uint8)
+        scales = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), dtype=np.uint8)
+        self.lib.oracle_quantize_mxfp4(nblk, _ptr(v), _ptr(codes), _ptr(scales))
+        return codes, scales
+
+    def mxfp4_ffn_qact(self, expert: dict, x64: np.ndarray, want_h: bool = False):
+        """One MXFP4 expert with activations quantised to MXFP4 (x before
+        gate/up, h before down)."""
+        x64 = np.ascontiguousarray(x64, dtype=np.float64)
+        n, d = x64.shape
+        w13 = np.ascontiguousarray(expert["w13"], dtype=np.uint8)
+        w13s = np.ascontiguousarray(expert["w13_scale"], dtype=np.uint8)
+        w2 = np.ascontiguousarray(expert["w2"], dtype=np.uint8)
+        w2s = np.ascontiguousarray(expert["w2_scale"], dtype=np.uint8)
+        f = w13.shape[0] // 2
+        y = np.empty((n, d), dtype=np.float64)
+        h = np.empty((n, f), dtype=np.float64) if want_h else None
+        self.lib.oracle_mxfp4_ffn_qact(d, f, _ptr(w13), _ptr(w13s), _ptr(w2), _ptr(w2s), n,
+                                       _ptr(x64), _ptr(y), _ptr(h))
+        return (y, h) if want_h else y
+
     def bf16_ffn(self, w13: np.ndarray, w2: np.ndarray, x64: np.ndarray):
         x64 = np.ascontiguousarray(x64, dtype=np.float64)
         n, d = x64.shape
@@ -181,15 +210,21 @@ class Oracle:
             acc = s if acc is None else acc + s
         return acc
 
-    def routed_ffn(self, x64, get_expert, counts, offsets, sorted_pair, k):
+    def expert(self, act: str):
+        """The expert FFN of an activation mode: "exact" (activations as given)
+        or "mxfp4" (x and h quantised to MXFP4)."""
+        return {"exact": self.mxfp4_ffn, "mxfp4": self.mxfp4_ffn_qact}[act]
+
+    def routed_ffn(self, x64, get_expert, counts, offsets, sorted_pair, k, act="exact"):
         """y_perm [P][d]: row p = expert e's output on the token of pair
         sorted_pair[p], for the experts e with counts[e] > 0."""
         d = x64.shape[1]
+        ffn = self.expert(act)
         y = np.zeros((len(sorted_pair), d), dtype=np.float64)
         for e in np.nonzero(counts)[0]:
             lo, hi = int(offsets[e]), int(offsets[e + 1])
             toks = sorted_pair[lo:hi] // k
-            y[lo:hi] = self.mxfp4_ffn(get_expert(int(e)), x64[toks])
+            y[lo:hi] = ffn(get_expert(int(e)), x64[toks])
         return y
 
     # ------------------------------------------------------------ combine
@@ -206,22 +241,24 @@ class Oracle:
         return out
 
     # -------------------------------------------------------------- layer
-    def layer(self, x, w_router, get_expert, shared, k, E, router="softmax", bias=None):
+    def layer(self, x, w_router, get_expert, shared, k, E, router="softmax", bias=None,
+              act="exact"):
         """All stages on the full batch.  x: fp32 or bf16 bits [T][d];
         get_expert(e) -> dict of expert e's packed tensors; shared: dict of
-        bf16 banks or None; router and bias as for route().  Returns every
-        intermediate in fp64/int32."""
+        bf16 banks or None; router and bias as for route(); act: the routed
+        experts' activation mode (expert()).  Returns every intermediate in
+        fp64/int32."""
         x64 = to_f64(x)
         logits, idx, w = self.route(x64, w_router, k, router, bias)
         counts, offsets, sorted_pair, pair_pos = self.permute(idx, E)
-        y_perm = self.routed_ffn(x64, get_expert, counts, offsets, sorted_pair, k)
+        y_perm = self.routed_ffn(x64, get_expert, counts, offsets, sorted_pair, k, act)
         shared_y = self.shared_ffn(shared, x64) if shared is not None else None
         out = self.combine(y_perm, pair_pos, w, shared_y)
         return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
                     sorted_pair=sorted_pair, pair_pos=pair_pos, y_perm=y_perm,
                     shared_y=shared_y, out=out)
 
-    def token_outputs(self, x_rows, idx_rows, w_rows, get_expert, shared):
+    def token_outputs(self, x_rows, idx_rows, w_rows, get_expert, shared, act="exact"):
         """out for a few tokens alone (each token's output depends only on its own
         activation row, chosen experts and weights): x_rows [n][d] activations,
         idx_rows/w_rows [n][k] their routing.  Sums in the same order as
@@ -230,9 +267,10 @@ class Oracle:
         n, k = idx_rows.shape
         d = x64.shape[1]
         y = np.zeros((n, k, d), dtype=np.float64)
+        ffn = self.expert(act)
         for e in np.unique(idx_rows):
             rows, slots = np.nonzero(idx_rows == e)
-            y[rows, slots] = self.mxfp4_ffn(get_expert(int(e)), x64[rows])
+            y[rows, slots] = ffn(get_expert(int(e)), x64[rows])
         shared_y = self.shared_ffn(shared, x64) if shared is not None else None
         pair_pos = np.arange(n * k, dtype=np.int32)
         out = self.combine(y.reshape(n * k, d), pair_pos, np.asarray(w_rows, np.float64),

@@ -229,6 +229,126 @@ void oracle_mxfp4_ffn(int d, int f, const uint8_t* w13, const uint8_t* w13s, con
   free(h);
 }
 
+/* ---------------------------------------------------------------------------
+ * Quantised-activation mode (not a method of the pages: they never quantise
+ * activations — review page, "KDA/MLA/MoE" table; explainer page, "reduction
+ * one".  It is the single-pass MXFP4 x MXFP4 form of the same FFN, checked
+ * apart from the exact layer).  The quantiser is OCP MX v1.0's for MXFP4:
+ *   X = max |v| over a 32-element block;
+ *   shared exponent E = floor(log2 X) - 2   (2: exponent of E2M1's largest
+ *     value, 6 = 1.5 * 2^2), so X / 2^E lies in [4, 8);
+ *   scale byte = E + 127, clamped to [0, 254]; X = 0 gives byte 0;
+ *   each element: the E2M1 value nearest to v / 2^s (s = byte - 127), ties
+ *     to the code with an even mantissa bit, magnitudes above 6 saturating
+ *     to 6; the sign is kept (a zero keeps its sign);
+ *   a block holding a NaN or an infinity: scale byte 255 (NaN), codes 0.
+ * Codes are packed as the weights are: byte i = element 2i (low nibble),
+ * element 2i+1 (high nibble).
+ * ------------------------------------------------------------------------- */
+void oracle_quantize_mxfp4(int64_t nblk, const double* v, uint8_t* codes, uint8_t* scales) {
+  for (int64_t b = 0; b < nblk; ++b) {
+    const double* vb = v + b * 32;
+    double X = 0.0;
+    int bad = 0;
+    for (int i = 0; i < 32; ++i) {
+      if (!isfinite(vb[i])) bad = 1;
+      else if (fabs(vb[i]) > X) X = fabs(vb[i]);
+    }
+    uint8_t* cb = codes + b * 16;
+    if (bad) {
+      scales[b] = 255;
+      for (int i = 0; i < 16; ++i) cb[i] = 0;
+      continue;
+    }
+    int byte = 0;
+    if (X > 0.0) {
+      int E = (int)floor(log2(X)) - 2;
+      byte = E + 127;
+      if (byte < 0) byte = 0;
+      if (byte > 254) byte = 254;
+    }
+    scales[b] = (uint8_t)byte;
+    double unit = ldexp(1.0, byte - 127);
+    for (int i = 0; i < 32; ++i) {
+      double a = fabs(vb[i]) / unit;
+      int best = 0; /* code of the nearest magnitude (codes 0..7 are the magnitudes) */
+      for (int c = 1; c < 8; ++c) {
+        double dc = fabs(a - oracle_e2m1(c)), db = fabs(a - oracle_e2m1(best));
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+      }
+      int code = best | (signbit(vb[i]) ? 8 : 0);
+      if (i % 2 == 0) cb[i / 2] = (uint8_t)code;
+      else cb[i / 2] |= (uint8_t)(code << 4);
+    }
+  }
+}
+
+/* Values of n rows of `cols` elements after MXFP4 quantisation (in place). */
+static void quantize_rows(int64_t n, int cols, double* v) {
+  int64_t nblk = n * (cols / 32);
+  uint8_t* codes = (uint8_t*)malloc((size_t)nblk * 16);
+  uint8_t* scales = (uint8_t*)malloc((size_t)nblk);
+  oracle_quantize_mxfp4(nblk, v, codes, scales);
+  for (int64_t b = 0; b < nblk; ++b)
+    for (int i = 0; i < 32; ++i) {
+      uint8_t byte = codes[b * 16 + i / 2];
+      int code = (i % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+      v[b * 32 + i] = oracle_e2m1(code) * oracle_e8m0(scales[b]);
+    }
+  free(codes);
+  free(scales);
+}
+
+/* The MXFP4 expert with quantised activations: x rows quantised to MXFP4,
+ * g = Wg xq, u = Wu xq, h = silu(g) u, h rows quantised to MXFP4, y = Wd hq;
+ * sums in fp64 in ascending order.  h_out (optional) receives hq. */
+void oracle_mxfp4_ffn_qact(int d, int f, const uint8_t* w13, const uint8_t* w13s,
+                           const uint8_t* w2, const uint8_t* w2s, int64_t n, const double* x,
+                           double* y, double* h_out) {
+  double* xq = (double*)malloc(sizeof(double) * (size_t)(n * d));
+  memcpy(xq, x, sizeof(double) * (size_t)(n * d));
+  quantize_rows(n, d, xq);
+  double* g = (double*)malloc(sizeof(double) * (size_t)(n * f));
+  double* u = (double*)malloc(sizeof(double) * (size_t)(n * f));
+  double* h = (double*)malloc(sizeof(double) * (size_t)(n * f));
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * (size_t)(d > f ? d : f));
+#pragma omp for schedule(static)
+    for (int j = 0; j < 2 * f; ++j) {
+      oracle_mxfp4_decode(j, 1, d, w13, w13s, row);
+      for (int64_t r = 0; r < n; ++r) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += row[i] * xq[r * d + i];
+        if (j < f) g[r * f + j] = acc;
+        else u[r * f + (j - f)] = acc;
+      }
+    }
+    free(row);
+  }
+  for (int64_t q = 0; q < n * f; ++q) h[q] = silu(g[q]) * u[q];
+  quantize_rows(n, f, h);
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * (size_t)(d > f ? d : f));
+#pragma omp for schedule(static)
+    for (int o = 0; o < d; ++o) {
+      oracle_mxfp4_decode(o, 1, f, w2, w2s, row);
+      for (int64_t r = 0; r < n; ++r) {
+        double acc = 0.0;
+        for (int j = 0; j < f; ++j) acc += row[j] * h[r * f + j];
+        y[r * d + o] = acc;
+      }
+    }
+    free(row);
+  }
+  if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)(n * f));
+  free(xq);
+  free(g);
+  free(u);
+  free(h);
+}
+
 /* One bf16 expert (the always-on shared experts): same FFN with
  * w13 [2f][d] and w2 [d][f] bf16. */
 void oracle_bf16_ffn(int d, int f, const uint16_t* w13, const uint16_t* w2, int64_t n,

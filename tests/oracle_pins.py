@@ -352,6 +352,86 @@ def pin_metamorphic_scales_and_signs(o):
     assert np.array_equal(h4, 2 * h) and np.array_equal(y4, 2 * y)
 
 
+# ------------------------------------------------ MXFP4 activation quantiser
+E2M1_POS = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # codes 0..7 (OCP MX v1.0)
+
+
+def np_quantize_mxfp4(v):
+    """OCP MX v1.0 MXFP4 quantiser written out independently: per block of
+    32, scale 2^(floor(log2 max|v|) - 2) (X / scale in [4, 8)), each element
+    the nearest E2M1 magnitude by exhaustive search (ties: the even code),
+    above 6 saturating; returns the quantised values (fp64)."""
+    v = np.asarray(v, dtype=np.float64).reshape(-1, 32)
+    out = np.empty_like(v)
+    for b in range(v.shape[0]):
+        X = np.max(np.abs(v[b]))
+        e = 0 if X == 0 else int(math.floor(math.log2(X))) - 2
+        unit = 2.0 ** e if X > 0 else 2.0 ** -127
+        for i in range(32):
+            a = abs(v[b, i]) / unit
+            cands = sorted(range(8), key=lambda c: (abs(a - E2M1_POS[c]), c & 1))
+            out[b, i] = math.copysign(E2M1_POS[cands[0]] * unit, v[b, i])
+    return out
+
+
+def pin_mxfp4_quantizer_definition(o):
+    """The oracle's MXFP4 quantiser against the written-out definition: random
+    blocks over many magnitudes, exact midpoints (ties to the even code),
+    saturation above 6, zeros of both signs, and an all-zero block."""
+    rng = np.random.default_rng(3)
+    blocks = [rng.standard_normal(32) * 2.0 ** rng.integers(-20, 20) for _ in range(60)]
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.9, 7.5, -0.25, -2.5, -5.0,
+                     4.0, 0.0, -0.0] + [1.0] * 17)
+    blocks += [mids, mids * 2.0 ** -9, np.zeros(32), -mids * 2.0 ** 30]
+    v = np.concatenate(blocks)
+    codes, scales = o.quantize_mxfp4(v.reshape(1, -1))
+    got = o.mxfp4_decode(codes, scales).ravel()
+    want = np_quantize_mxfp4(v).ravel()
+    assert np.array_equal(np.signbit(got[want == 0]), np.signbit(want[want == 0]))
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:5]
+    # the worked midpoints: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2,
+    # 2.5 -> 2, 3.5 -> 4, 5 -> 4, 6.9 -> 6 (saturated), 7.5 -> 6
+    m = got[60 * 32:60 * 32 + 9]
+    assert m.tolist() == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, 6.0], m
+
+
+def pin_mxfp4_quantizer_roundtrip(o):
+    """Every block that is already MXFP4 with its largest magnitude 4 or 6 (so
+    the rule picks the same scale) comes back unchanged, codes and scale
+    byte, over all 16 codes and many scales; a NaN block gets scale 255."""
+    rng = np.random.default_rng(4)
+    for s in (90, 117, 127, 128, 150):
+        q = rng.integers(0, 256, size=(16, 16), dtype=np.uint8)
+        q[:, 0] = (q[:, 0] & 0xF0) | np.where(np.arange(16) % 2, 7, 14)   # +6 or -4 at element 0
+        sc = np.full((16, 1), s, dtype=np.uint8)
+        vals = o.mxfp4_decode(q, sc)
+        q2, s2 = o.quantize_mxfp4(vals)
+        vals2 = o.mxfp4_decode(q2, s2)
+        assert np.array_equal(s2, sc), s
+        assert np.array_equal(vals2, vals), s
+    bad = np.zeros(32)
+    bad[5] = np.nan
+    _, s3 = o.quantize_mxfp4(bad.reshape(1, 32))
+    assert s3.tolist() == [[255]]
+
+
+def pin_qact_ffn_dense(o):
+    """The quantised-activation expert equals dense numpy: independent decode,
+    x quantised by the written-out rule, gate/up, SiLU-GLU, h quantised, down."""
+    c, x, _, bank, _ = tiny_inputs()
+    x64 = to_f64(x)
+    ex = _expert(bank, 5)
+    y, h = o.mxfp4_ffn_qact(ex, x64, want_h=True)
+    W13 = np_decode(ex["w13"], ex["w13_scale"])
+    W2 = np_decode(ex["w2"], ex["w2_scale"])
+    xq = np_quantize_mxfp4(x64).reshape(x64.shape)
+    gu = xq @ W13.T
+    hq = np_quantize_mxfp4(np_silu(gu[:, :c.f]) * gu[:, c.f:]).reshape(h.shape)
+    assert np.array_equal(h, hq)
+    want = hq @ W2.T
+    assert np.max(np.abs(y - want)) <= 1e-12 * np.max(np.abs(want))
+
+
 # ----------------------------------------------------------------- layer
 def _layer_tiny(o, x=None, wr=None, bank=None, sh="default"):
     c, x0, wr0, bank0, sh0 = tiny_inputs()

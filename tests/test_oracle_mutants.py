@@ -48,6 +48,13 @@ MUTANTS = {
                                "double s = sigmoid_score(l[idx[t * k + r]]) + (bias ? bias[idx[t * k + r]] : 0.0);"),
     "sigmoid_norm_inverted": ("w[t * k + r] = norm ? s / z : s;", "w[t * k + r] = norm ? s : s / z;"),
     "sigmoid_sign": ("return 1.0 / (1.0 + exp(-l));", "return 1.0 / (1.0 + exp(l));"),
+    "mx_quant_emax_wrong": ("int E = (int)floor(log2(X)) - 2;", "int E = (int)floor(log2(X)) - 1;"),
+    "mx_quant_ceil_scale": ("int E = (int)floor(log2(X)) - 2;", "int E = (int)ceil(log2(X)) - 2;"),
+    "mx_quant_ties_odd": ("(dc == db && (c & 1) == 0)", "(dc == db && (c & 1) == 1)"),
+    "mx_quant_ties_away": ("(dc == db && (c & 1) == 0)", "(dc == db)"),
+    "mx_quant_sign_dropped": ("int code = best | (signbit(vb[i]) ? 8 : 0);", "int code = best;"),
+    "qact_h_not_quantised": ("  quantize_rows(n, f, h);\n", "\n"),
+    "qact_x_not_quantised": ("  quantize_rows(n, d, xq);\n", "\n"),
     "bf16_decode_wrong": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)(b & 0xFF7F) << 16;"),
 }
 
@@ -79,10 +86,9 @@ def test_mutant_is_caught(name, tmp_path):
 # Mistakes planted in the oracle's per-token path (Python), which the
 # full-size GPU tests use as their expected values.
 PY_MUTANTS = {
-    "token_outputs_slot_swap": ("y[rows, slots] = self.mxfp4_ffn(",
-                                "y[rows, (slots + 1) % k] = self.mxfp4_ffn("),
-    "token_outputs_rows_of_first_token": ("self.mxfp4_ffn(get_expert(int(e)), x64[rows])",
-                                          "self.mxfp4_ffn(get_expert(int(e)), x64[rows * 0])"),
+    "token_outputs_slot_swap": ("y[rows, slots] = ffn(", "y[rows, (slots + 1) % k] = ffn("),
+    "token_outputs_rows_of_first_token": ("ffn(get_expert(int(e)), x64[rows])",
+                                          "ffn(get_expert(int(e)), x64[rows * 0])"),
     "token_outputs_no_shared": ("shared_y)\n    return out", "None)\n    return out"),
 }
 
