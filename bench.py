@@ -10,6 +10,9 @@ of the metric, each with the same seeded synthetic weights:
   decode_b64          64 tokens a step
   prefill_4096        4096 tokens a step
   prefill_16384_zipf  16384 tokens a step, expert popularity skewed Zipf(1.1)
+and the two prefill batches again with the quantised-activation mode
+(x and h in MXFP4, so the routed products run on the FP4 matrix rate): an
+approximation of the layer, reported beside the exact one, never in its place.
 Decode steps each take fresh tokens, so every step routes to another expert
 set and the routed weights stream from HBM, not from a cache warmed by the
 previous step; prefill batches touch every expert at every step.
@@ -41,7 +44,9 @@ MXFP4_MFMA_PEAK_TFLOPS = 10100.0   # dense MXFP4 x MXFP4 matrix peak, for refere
 X_PASSES = 2                       # E4M3 passes that carry bf16 x exactly (one MFMA each)
 SPIN_CYCLES = 20_000_000           # ~10 ms of GPU spin ahead of a timed run of launches
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (MXFP4 bytes) at batch 1/64/4096"
-WORKLOADS = ["decode_b1", "decode_b64", "prefill_4096", "prefill_16384_zipf"]
+WORKLOADS = ["decode_b1", "decode_b64", "prefill_4096", "prefill_16384_zipf",
+             "prefill_4096_mxfp4act", "prefill_16384_zipf_mxfp4act"]
+QACT = "_mxfp4act"   # suffix: the routed experts' activations quantised to MXFP4
 KERNEL_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "mxscale.hip")
 
 
@@ -101,7 +106,7 @@ def cpu_baseline_one_token(cfg, budget_s: float):
                        f"{cfg.n_shared} shared, combine); {spent:.1f} s of oracle time")
 
 
-def cpu_baseline_batch(cfg, budget_s: float):
+def cpu_baseline_batch(cfg, budget_s: float, act: str = "exact"):
     """A batch: the oracle's router and permute on the whole batch (timed);
     then expert FFNs of a seeded random sample of the touched experts, each
     on up to 256 of its pairs (the oracle decodes an expert's weights once for
@@ -115,6 +120,7 @@ def cpu_baseline_batch(cfg, budget_s: float):
     import gen
     import oracle
     orc = oracle.default()
+    ffn = orc.expert(act)
     T = cfg.T
     x64 = oracle.to_f64(gen.x(cfg))
     wr = gen.router(cfg)
@@ -129,14 +135,14 @@ def cpu_baseline_batch(cfg, budget_s: float):
     ex = gen.routed_expert(cfg, int(order[0]))
     for nr in (1, min(256, T)):
         t0 = time.perf_counter()
-        orc.mxfp4_ffn(ex, x64[:nr])
+        ffn(ex, x64[:nr])
         secs.append(time.perf_counter() - t0)
         rows.append(nr)
     for e in order:
         ex = gen.routed_expert(cfg, int(e))   # untimed
         toks = sp[offsets[e]:offsets[e + 1]][:256] // cfg.k
         t0 = time.perf_counter()
-        orc.mxfp4_ffn(ex, x64[toks])
+        ffn(ex, x64[toks])
         secs.append(time.perf_counter() - t0)
         rows.append(len(toks))
         if sum(secs) > budget_s / 2 and len(secs) >= 2:
@@ -161,7 +167,8 @@ def cpu_baseline_batch(cfg, budget_s: float):
     t_comb = (time.perf_counter() - t0) * T / n_c
     total = t_route + t_routed + t_shared + t_comb
     return dict(value=T / total, unit="tokens/s", cores=orc.threads(), kind="oracle",
-                sample=f"{cfg.name}: fp64 router + permute on all {T} tokens ({t_route:.1f} s, "
+                sample=f"{cfg.name} ({act} activations): fp64 router + permute on all {T} tokens "
+                       f"({t_route:.1f} s, "
                        f"measured); routed experts: {len(secs) - 2} of the {touched.size} "
                        f"touched experts (seeded random), each on up to 256 of its pairs, and "
                        f"one on 1 and on 256 rows, "
@@ -181,7 +188,8 @@ def run_workload(name, args, weights):
     from mxfp4_routed_expert_gemv_amd import DIAG_COUNT, OP_EXPERT_FFN, OP_LAYER, k3moe_expert_ffn, lib
     from mxfp4_routed_expert_gemv_amd.layer import MoELayer
 
-    cfg = gen.get(name)
+    qact = name.endswith(QACT)
+    cfg = gen.get(name[:-len(QACT)] if qact else name)
     big = cfg.T >= 1024
     K = args.steps if args.steps is not None else (10 if big else 50)
     W = args.warmup if args.warmup is not None else (3 if big else 5)
@@ -190,7 +198,8 @@ def run_workload(name, args, weights):
     w_router = weights.w_router
     if cfg.zipf_s is not None:
         w_router = gen.device._to_dev_bf16(gen.router(cfg), "cuda")
-    layer = MoELayer(w_router, weights.routed, weights.shared, cfg.k, out_dtype=torch.bfloat16)
+    layer = MoELayer(w_router, weights.routed, weights.shared, cfg.k, out_dtype=torch.bfloat16,
+                     act="mxfp4" if qact else "exact")
     T = cfg.T
     # decode: K + W distinct batches (fresh expert sets every step); prefill
     # batches touch every expert anyway, so two batches alternate
@@ -293,8 +302,16 @@ def run_workload(name, args, weights):
     # whole-layer algorithmic bytes (MXFP4 experts touched + shared + router + x, out)
     layer_bytes = (ffn_bytes + cfg.n_shared * 3 * cfg.f_shared * cfg.d * 2
                    + cfg.E * cfg.d * 2 + 2 * T * cfg.d * 2)
-    traffic = stored_traffic(cfg.name)
-    if mfma_bound:
+    traffic = stored_traffic(name)
+    if qact:
+        # MXFP4 x MXFP4 in one pass: the matrix-core target is the FP4 peak
+        roof = {"bound": "mfma", "achieved": gu_tflops, "peak": MXFP4_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": gu_tflops / MXFP4_MFMA_PEAK_TFLOPS,
+                "traffic": traffic, "kernel": "mx_gemm_scaled (gate/up, MXFP4 activations)",
+                "flops_per_launch": gu_flops, "avg_launch_us": gu_avg_s * 1e6,
+                "bytes_per_launch": gu_bytes, "mxfp4_gbs": gu_gbs,
+                "frac_of_hbm_peak": gu_gbs / HBM_PEAK_GBS}
+    elif mfma_bound:
         roof = {"bound": "mfma", "achieved": gu_tflops, "peak": FP8_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": gu_tflops / FP8_MFMA_PEAK_TFLOPS, "traffic": traffic,
                 "kernel": "mx_gemm_scaled (gate/up)", "flops_per_launch": gu_flops,
@@ -322,9 +339,10 @@ def run_workload(name, args, weights):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens_per_step": T, "d": cfg.d, "f": cfg.f,
+        "config": {"workload": name, "tokens_per_step": T, "d": cfg.d, "f": cfg.f,
                    "experts": cfg.E, "top_k": cfg.k, "shared_experts": cfg.n_shared,
                    "weights": "routed MXFP4 (E2M1 + E8M0/32), shared and router bf16",
+                   "routed_activations": "MXFP4 (quantised)" if qact else "exact",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
@@ -393,10 +411,12 @@ def main():
     if not args.no_cpu_baseline:
         for n in names:
             log(f"timing the CPU oracle on {n}")
-            cfg = gen.get(n)
+            qact = n.endswith(QACT)
+            cfg = gen.get(n[:-len(QACT)] if qact else n)
             results[n]["cpu_baseline"] = (cpu_baseline_one_token(cfg, args.cpu_seconds)
                                           if cfg.T == 1 else
-                                          cpu_baseline_batch(cfg, args.cpu_seconds))
+                                          cpu_baseline_batch(cfg, args.cpu_seconds,
+                                                             "mxfp4" if qact else "exact"))
     line = dict(results[names[0]])
     if len(names) > 1:
         line["workloads"] = results

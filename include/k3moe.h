@@ -83,6 +83,20 @@ enum {
  *                 renormalised; both readings are offered).
  * Ties go to the lower expert id in every mode. */
 enum { K3MOE_ROUTER_SOFTMAX = 0, K3MOE_ROUTER_SIGMOID = 1, K3MOE_ROUTER_SIGMOID_NORM = 2 };
+/* Activation modes of the routed experts (k3moe_shape.act).
+ *   EXACT: the activations enter the products as given (the pages' engines
+ *          never quantise activations: kimi-k3-in-c review page,
+ *          "KDA/MLA/MoE" table; explainer page, "reduction one").
+ *   MXFP4: x before gate/up and h before down are quantised to MXFP4 (OCP MX
+ *          v1.0: per 32-element block, scale 2^(floor(log2 max|v|) - 2),
+ *          elements rounded to the nearest E2M1 value, ties to even,
+ *          saturating at 6), so both operands of the matrix-core products
+ *          are MXFP4 and one pass runs at the FP4 rate.  An approximation of
+ *          the layer, not the layer: its outputs follow the quantised
+ *          definition, not the exact one.  Needs bf16 x, d % 512 == 0 and
+ *          f % 512 == 0; the routed experts then take the grouped GEMMs at
+ *          every batch size. */
+enum { K3MOE_ACT_EXACT = 0, K3MOE_ACT_MXFP4 = 1 };
 /* Path classes (k3moe_path_class). */
 enum { K3MOE_PATH_GEMV = 0, K3MOE_PATH_MFMA = 1 };
 
@@ -109,7 +123,8 @@ enum {
  * d % 32 == 0; 32 <= f <= 16384 and f % 32 == 0; 1 <= k <= min(E, 64);
  * E <= 1024; 0 <= n_shared <= 8; f_shared % 32 == 0 (>= 32 when n_shared > 0);
  * x_dtype, out_dtype in {K3MOE_F32, K3MOE_BF16}; router one of
- * K3MOE_ROUTER_* (0, the softmax router, for a zero-initialised shape). */
+ * K3MOE_ROUTER_* (0, the softmax router, for a zero-initialised shape);
+ * act one of K3MOE_ACT_* (0, exact activations, when zero-initialised). */
 typedef struct k3moe_shape {
   int64_t T;         /* tokens */
   int32_t d;         /* hidden size */
@@ -121,6 +136,7 @@ typedef struct k3moe_shape {
   int32_t x_dtype;   /* activations x [T][d] */
   int32_t out_dtype; /* layer output [T][d] */
   int32_t router;    /* K3MOE_ROUTER_* */
+  int32_t act;       /* K3MOE_ACT_* (routed experts' activation mode) */
 } k3moe_shape;
 
 /* A bank of experts, expert-major (each expert's bytes contiguous).
@@ -259,8 +275,12 @@ k3moe_status k3moe_expert_ffn(const k3moe_shape* shape, const k3moe_expert_bank*
  * bytes, the value split into 3 E4M3 passes with one E8M0 scale per pass and
  * 32-feature block (h ~ sum_p code_p * 2^(scale_p - 127)): 3 x 128 code bytes
  * in feature order, then byte 4p + b = scale of pass p, block b, then 4
- * unused bytes; this is the operand form of the instruction.  Otherwise (fp32
- * x, or other d, f) h holds fp32 values, row q at word q * f.  A buffer
+ * unused bytes; this is the operand form of the instruction.  With
+ * act == K3MOE_ACT_MXFP4, row q starts at byte q * (f/128) * 80 and is f/128
+ * stages of 80 bytes: 4 blocks of 16 E2M1 code bytes (byte i = feature 2i
+ * low nibble, 2i+1 high nibble), then byte b = E8M0 scale of block b, then
+ * 12 unused bytes.  Otherwise (fp32 x, or other d, f) h holds fp32 values,
+ * row q at word q * f.  A buffer
  * written by k3moe_expert_gateup is meant for k3moe_expert_down with the same
  * shape.
  * Workspace (gate/up only): k3moe_workspace_bytes(shape, K3MOE_OP_EXPERT_GATEUP)

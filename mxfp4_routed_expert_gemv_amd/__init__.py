@@ -27,6 +27,8 @@ ROUTERS = {"softmax": ROUTER_SOFTMAX, "sigmoid": ROUTER_SIGMOID,
            "sigmoid_norm": ROUTER_SIGMOID_NORM}
 DIAG_RECHECKED_TOKENS, DIAG_NONFINITE_LOGITS, DIAG_BAD_EXPERT_IDS = 0, 1, 2
 DIAG_SCORE_NEAR_TIES = 3
+ACT_EXACT, ACT_MXFP4 = 0, 1
+ACTS = {"exact": ACT_EXACT, "mxfp4": ACT_MXFP4}
 DIAG_COUNT = 4
 
 STATUS = {0: "K3MOE_OK", 1: "K3MOE_EINVAL", 2: "K3MOE_ESHAPE", 3: "K3MOE_EALIGN",
@@ -42,7 +44,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("f", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("f_shared", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("router", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("router", ctypes.c_int32),
+                ("act", ctypes.c_int32)]
 
 
 class ExpertBank(ctypes.Structure):
@@ -214,8 +217,9 @@ def k3moe_layer_noalloc(shape, weights: LayerWeights, x, out, diag=None, stream=
 
 
 # --------------------------------------------------------- struct builders
-def make_shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router=ROUTER_SOFTMAX) -> Shape:
-    return Shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router)
+def make_shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router=ROUTER_SOFTMAX,
+               act=ACT_EXACT) -> Shape:
+    return Shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router, act)
 
 
 def make_bank(fmt, n, d, f, w13, w13_scale, w2, w2_scale) -> ExpertBank:

@@ -68,6 +68,12 @@ k3moe_status check_shape(const k3moe_shape* s) {
   if (s->router != K3MOE_ROUTER_SOFTMAX && s->router != K3MOE_ROUTER_SIGMOID &&
       s->router != K3MOE_ROUTER_SIGMOID_NORM)
     return fail(K3MOE_EUNSUPPORTED, "router %d is not one of K3MOE_ROUTER_*", s->router);
+  if (s->act != K3MOE_ACT_EXACT && s->act != K3MOE_ACT_MXFP4)
+    return fail(K3MOE_EUNSUPPORTED, "act %d is not one of K3MOE_ACT_*", s->act);
+  if (s->act == K3MOE_ACT_MXFP4 && !(s->x_dtype == K3MOE_BF16 && s->d % 512 == 0 &&
+                                     s->f % 512 == 0))
+    return fail(K3MOE_EUNSUPPORTED,
+                "MXFP4 activations need bf16 x, d %% 512 == 0 and f %% 512 == 0");
   if (s->d < 32 || s->d > 16384 || s->d % 32)
     return fail(K3MOE_ESHAPE, "d = %d: need 32 <= d <= 16384, d %% 32 == 0", s->d);
   if (s->f < 32 || s->f > 16384 || s->f % 32)

@@ -200,7 +200,104 @@ __global__ __launch_bounds__(256) void quant_x(const uint16_t* __restrict__ x,
   store_xblock(xq + ((size_t)t * nst + st) * (2 * 128 + 16), blk, packed, sb0, gb < nblk);
 }
 
+// ------------------------------------------- MXFP4 activations (one pass)
+// The quantised-activation mode takes x and h as MXFP4 (OCP MX v1.0): per
+// block of 32, scale byte s = e - 2 from the exponent field e of the block's
+// largest magnitude X (so X / 2^(s-127) lies in [4, 8)), clamped to
+// [0, 254] (X = 0 gives 0); each element the nearest E2M1 value of
+// v / 2^(s-127), ties to the code with an even mantissa bit, above 6
+// saturating to 6; a block holding a NaN or an infinity gets scale 255 and
+// codes 0.  One pass, so the matrix core runs at its FP4 rate.  A record
+// (a row's 128-element stage) is 5 units: 4 blocks of 16 code bytes (byte i
+// = element 2i low nibble, 2i+1 high nibble, as the weights), then a unit
+// whose byte b is block b's scale (bytes 4..15 unused).
+constexpr int kQ4Units = 5;
+
+// Scale byte of a block from the bits of its largest magnitude (finite).
+__device__ __forceinline__ uint32_t q4_scale(uint32_t max_bits) {
+  const int s = (int)(max_bits >> 23) - 2;
+  return (uint32_t)(s < 0 ? 0 : (s > 254 ? 254 : s));
+}
+// E2M1 code of v under scale byte sb: a = |v| 2^(127 - sb) is exact, and the
+// comparisons with the midpoints between E2M1 values alternate strict and
+// non-strict so that ties go to the even code.
+__device__ __forceinline__ uint32_t q4_code(float v, uint32_t sb) {
+  const float a = ldexpf(fabsf(v), 127 - (int)sb);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// x [T][d] bf16 -> xq [T][d/128][kQ4Units units]: one thread per 32-element
+// block; the 4 threads of a stage are adjacent lanes.
+__global__ __launch_bounds__(256) void quant_x4(const uint16_t* __restrict__ x,
+                                                uint8_t* __restrict__ xq, int64_t nblk, int d) {
+  const int64_t gb = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = gb < nblk ? gb : nblk - 1;   // lanes past the end redo the last block
+  const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = src[q];
+    w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+  }
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    mb = max(mb, (w[i] << 16) & 0x7FFFFFFFu);
+    mb = max(mb, w[i] & 0x7FFF0000u);
+  }
+  const bool bad = mb >= kAbsInf;
+  const uint32_t sb = bad ? 255u : q4_scale(mb);
+  uint32_t packed[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {   // word q: elements 8q .. 8q+7, two per byte
+      const uint32_t wv = w[4 * q + h];
+      const uint32_t lo = q4_code(__uint_as_float(wv << 16), sb);
+      const uint32_t hi = q4_code(__uint_as_float(wv & 0xFFFF0000u), sb);
+      word |= (lo | (hi << 4)) << (8 * h);
+    }
+    packed[q] = bad ? 0u : word;
+  }
+  const int nst = d / kBK;
+  const int64_t nb_row = d / 32;
+  const int64_t t = b / nb_row;
+  const int j = (int)(b - t * nb_row), st = j >> 2, blk = j & 3;
+  uint8_t* rec = xq + ((size_t)t * nst + st) * (kQ4Units * 16);
+  const int l0 = threadIdx.x & ~3;
+  uint32_t sc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sc |= (__shfl(sb, (l0 + q) & 63, 64) & 0xFFu) << (8 * q);
+  if (gb < nblk) {
+    *reinterpret_cast<uint4*>(rec + blk * 16) = uint4{packed[0], packed[1], packed[2], packed[3]};
+    if (blk == 0) *reinterpret_cast<uint4*>(rec + 64) = uint4{sc, 0u, 0u, 0u};
+  }
+}
+
 // ---------------------------------------------------------- grouped GEMMs
+// Tile of item `it`.  Expert e owns items [s_mt[e] NT, s_mt[e+1] NT): its
+// m-tiles times the NT n-tiles.  Within an expert the items run in blocks of
+// G consecutive m-tiles, the n-tile slowest inside a block.  Consecutive
+// items run at the same time on the workgroups of one XCD, which then share
+// each weight tile (up to G m-tiles of the expert) and each activation tile
+// (consecutive n-tiles) through that XCD's L2.  G = 1 is m-tile-major.
+__device__ __forceinline__ void item_tile(const int* s_mt, int E, int it, int NT, int G, int& mt,
+                                          int& nt) {
+  const int e = mtile_expert(s_mt, E, it / NT);
+  const int m0 = s_mt[e], me = s_mt[e + 1] - m0;
+  const int li = it - m0 * NT;
+  const int blk = li / (G * NT);
+  const int g0 = blk * G;
+  const int gs = min(G, me - g0);
+  const int r = li - blk * G * NT;
+  nt = r / gs;
+  mt = m0 + g0 + (r - nt * gs);
+}
+
 // With pair-wide weight copies (PB), the copies a wave issues after the last
 // copy that a stage needs, in the steady state, for either parity of the
 // stage: per stage the wave issues NAW activation copies, then on every other
@@ -268,15 +365,18 @@ __host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2)
 // bytes (two stages) are copied at once, non-temporally, into a ring of
 // (RB + 2) / 2 two-stage slots laid out as the one-token stream's steps:
 // whole 128-byte lines per copy, each read once.
-template <int MF, int NF, int RA, int RB, bool DOWN, bool PB>
+// Q4: the quantised-activation mode (A in MXFP4, one pass; gate/up writes h
+// in MXFP4); otherwise A in exact E4M3 passes.
+template <int MF, int NF, int RA, int RB, bool DOWN, bool PB, bool Q4>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mx_gemm_scaled(
     const uint8_t* __restrict__ a_src, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pair, void* __restrict__ out, int d, int f, int E,
-    int k) {
-  constexpr int NP = DOWN ? 3 : 2;              // activation passes
-  constexpr int NPH = 3;                        // passes of the h this kernel writes
-  constexpr int UA = NP * 8 + 1;                // units of a source row's stage
+    int k, int G) {
+  constexpr int NP = Q4 ? 1 : (DOWN ? 3 : 2);   // activation passes
+  constexpr int NPH = 3;                        // passes of the h this kernel writes (exact)
+  constexpr int UA = Q4 ? kQ4Units : NP * 8 + 1;   // units of a source row's stage
+  constexpr int A_FMT = Q4 ? 4 : 0;             // A operand format: FP4 or E4M3
   constexpr int ULA = UA + 1;                   // units of an A row in LDS
   constexpr int BM = 16 * MF;
   constexpr int A_UNITS = (BM * ULA + 255) / 256 * 256;
@@ -352,7 +452,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     (r & 15));
   };
   auto a_setup = [&]() {
-    const int mt = a_it / NT;
+    int mt, nt_unused;
+    item_tile(s_mt, E, a_it, NT, G, mt, nt_unused);
     const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
     const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
     const int rows = min(BM, offsets[e + 1] - row0);
@@ -369,7 +470,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
   auto b_setup = [&]() {
-    const int mt = b_it / NT, nt = b_it - mt * NT;
+    int mt, nt;
+    item_tile(s_mt, E, b_it, NT, G, mt, nt);
     const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
     const uint8_t* wbase = wq + (size_t)e * e_rows * w_row;
 #pragma unroll
@@ -385,8 +487,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
   auto s_setup = [&]() {
-    const int mt = s_it / NT;
-    s_nt = s_it - mt * NT;
+    int mt;
+    item_tile(s_mt, E, s_it, NT, G, mt, s_nt);
     s_e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
   };
   const uint32_t sA_lds = lds_addr(sA), sB_lds = lds_addr(sB), sS_lds = lds_addr(sS);
@@ -420,8 +522,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if ((b_st & 1) == 0) {
         const uint32_t base = sB_lds + (uint32_t)(((g >> 1) % RBP) * B_SLOT_P);
 #pragma unroll
-        for (int q = 0; q < NBC; ++q)
-          dma16_raw_nt(bp[q] + (b_st >> 1) * kBK, base + (cq * (NBC * 64) + q * 64) * 16);
+        for (int q = 0; q < NBC; ++q) {
+          // read once per m-tile: non-temporal, except with MXFP4 activations,
+          // where the items of a block share each weight tile through the L2
+          if constexpr (Q4)
+            dma16_raw(bp[q] + (b_st >> 1) * kBK, base + (cq * (NBC * 64) + q * 64) * 16);
+          else
+            dma16_raw_nt(bp[q] + (b_st >> 1) * kBK, base + (cq * (NBC * 64) + q * 64) * 16);
+        }
       }
     } else {
       const uint32_t base = sB_lds + (uint32_t)((g % RB) * B_SLOT);
@@ -446,7 +554,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     b_setup();
     if (s_it < it_end) s_setup();
     // scales of the first item's first group (older than every counted copy)
-    const int mt = it_first / NT, nt = it_first - mt * NT;
+    int mt, nt;
+    item_tile(s_mt, E, it_first, NT, G, mt, nt);
     const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
 #pragma unroll
     for (int q = 0; q < BROWS / 256; ++q) {
@@ -511,13 +620,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       int as[2][NP];
       auto load_a = [&](int i, i32x8_t (&av)[NP], int (&sv)[NP]) {
         const uint8_t* arow = abase + (i * 16 + ln) * (ULA * 16);
+        if constexpr (Q4) {   // the lane's MX block of the row, as a weight lane
+          const uint4 c = *reinterpret_cast<const uint4*>(arow + lg * 16);
+          av[0] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+          sv[0] = arow[(UA - 1) * 16 + lg];
+        } else {
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(arow + (p * 8 + lg) * 16);
-          const uint4 hi = *reinterpret_cast<const uint4*>(arow + (p * 8 + 4 + lg) * 16);
-          av[p] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sv[p] = arow[(UA - 1) * 16 + p * 4 + lg];
+          for (int p = 0; p < NP; ++p) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(arow + (p * 8 + lg) * 16);
+            const uint4 hi = *reinterpret_cast<const uint4*>(arow + (p * 8 + 4 + lg) * 16);
+            av[p] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sv[p] = arow[(UA - 1) * 16 + p * 4 + lg];
+          }
         }
       };
       load_a(0, a[0], as[0]);
@@ -529,7 +644,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
             acc[i][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                a[i & 1][p], bq[nf], acc[i][nf], 0, 4, 0, as[i & 1][p], 0, bs[nf]);
+                a[i & 1][p], bq[nf], acc[i][nf], A_FMT, 4, 0, as[i & 1][p], 0, bs[nf]);
       }
     }
     if (DOWN) {
@@ -545,6 +660,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int nf = 0; nf < NF; ++nf) yr[nf * 16] = acc[i][nf][r];
           }
         }
+    } else if constexpr (Q4) {
+      // h = silu(g) * u for this wave's 32-feature blocks, quantised to
+      // MXFP4; a block's largest magnitude is reduced over the 16 lanes of the
+      // row (lanes with the same lg), and two neighbouring lanes' codes share
+      // a byte (every lane takes part in both exchanges).
+      uint8_t* hq = static_cast<uint8_t*>(out);
+      const size_t h_row = (size_t)(f / kBK) * (kQ4Units * 16);
+#pragma unroll
+      for (int hb = 0; hb < NF / 4; ++hb) {
+        const int fb = (nt * (4 * FW) + wv * FW) / 32 + hb, hst = fb >> 2, blk = fb & 3;
+#pragma unroll
+        for (int i = 0; i < NMB; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = i * 16 + lg * 4 + r;
+            const float h0 = silu_mul(acc[i][2 * hb][r], acc[i][2 * hb + NF / 2][r]);
+            const float h1 = silu_mul(acc[i][2 * hb + 1][r], acc[i][2 * hb + 1 + NF / 2][r]);
+            uint32_t mb =
+                max(__float_as_uint(h0) & 0x7FFFFFFFu, __float_as_uint(h1) & 0x7FFFFFFFu);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o, 64));
+            const bool bad = mb >= kAbsInf;
+            const uint32_t sb = bad ? 255u : q4_scale(mb);
+            const uint32_t c0 = bad ? 0u : q4_code(h0, sb), c1 = bad ? 0u : q4_code(h1, sb);
+            const uint32_t n0 = (uint32_t)__shfl_xor((int)c0, 1, 64);
+            const uint32_t n1 = (uint32_t)__shfl_xor((int)c1, 1, 64);
+            if (m < rows) {
+              uint8_t* hr = hq + (size_t)(row0 + m) * h_row + (size_t)hst * (kQ4Units * 16);
+              if ((ln & 1) == 0) {   // features ln, ln + 1 and 16 + ln, 17 + ln of the block
+                hr[blk * 16 + (ln >> 1)] = (uint8_t)(c0 | (n0 << 4));
+                hr[blk * 16 + 8 + (ln >> 1)] = (uint8_t)(c1 | (n1 << 4));
+              }
+              if (ln == 0) hr[64 + blk] = (uint8_t)sb;
+            }
+          }
+      }
     } else {
       // h = silu(g) * u for this wave's 32-feature blocks, written as NPH
       // passes; a block's largest magnitude is reduced over the 16 lanes of
@@ -587,7 +738,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
   for (int it = it_first; it < it_end; it += it_step) {
-    const int mt = it / NT, nt = it - mt * NT;
+    int mt, nt;
+    item_tile(s_mt, E, it, NT, G, mt, nt);
     const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
     const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
     const int rows = min(BM, offsets[e + 1] - row0);
@@ -952,14 +1104,25 @@ int down_1tok_lds(const k3moe_shape& s, int NF) {
 }  // namespace
 
 size_t xq_bytes(const k3moe_shape& s) {
-  return (size_t)s.T * (size_t)(s.d / kBK) * (2 * 128 + 16);
+  const size_t rec = s.act == K3MOE_ACT_MXFP4 ? kQ4Units * 16 : 2 * 128 + 16;
+  return (size_t)s.T * (size_t)(s.d / kBK) * rec;
 }
 
+namespace {
+// m-tiles per item block: with MXFP4 activations, blocks of 8 when an
+// expert is expected to span several m-tiles (the weights of a block are then
+// shared through the L2); the exact passes keep m-tile-major order, whose
+// activation tiles (the larger stream there) are shared instead.
+int pick_g(const k3moe_shape& s, int mf) {
+  return s.act == K3MOE_ACT_MXFP4 && (double)s.T * s.k / s.E > 16.0 * mf ? 8 : 1;
+}
+}  // namespace
 
 hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
                                 const int32_t* offsets, const int32_t* sorted_pair, float* h,
                                 uint8_t* xq, hipStream_t st) {
-  if (s.T == 1) {
+  const bool q4 = s.act == K3MOE_ACT_MXFP4;
+  if (s.T == 1 && !q4) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint8_t* w = static_cast<const uint8_t*>(b.w13);
     const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
@@ -975,25 +1138,42 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
     }
   }
   const int64_t nblk = s.T * (int64_t)(s.d / 32);
-  quant_x<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(static_cast<const uint16_t*>(x), xq,
-                                                          nblk, s.d);
+  if (q4)
+    quant_x4<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(static_cast<const uint16_t*>(x), xq,
+                                                             nblk, s.d);
+  else
+    quant_x<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(static_cast<const uint16_t*>(x), xq,
+                                                            nblk, s.d);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const uint8_t* w = static_cast<const uint8_t*>(b.w13);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
   const dim3 g(grouped_grid());   // one workgroup per CU
-#define K3_SC(MF, NF, RA, RB, PB)                                                           \
-  mx_gemm_scaled<MF, NF, RA, RB, false, PB><<<g, 512, 0, st>>>(                              \
-      xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k)
+  const int mf = pick_mf(s, 6);
+  const int G = pick_g(s, mf);
+#define K3_SC(MF, NF, RA, RB, PB)                                                            \
+  do {                                                                                        \
+    if (q4)                                                                                   \
+      mx_gemm_scaled<MF, NF, RA, RB, false, PB, true><<<g, 512, 0, st>>>(                     \
+          xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k, G);                         \
+    else                                                                                      \
+      mx_gemm_scaled<MF, NF, RA, RB, false, PB, false><<<g, 512, 0, st>>>(                    \
+          xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k, G);                         \
+  } while (0)
   // Short m-tiles (weight-stream bound): pair-wide non-temporal weight copies
   // with deep rings on both operands (a wave waits for its copies in issue
   // order, so the activation ring's lead also bounds the weights').  Taller
   // ones: 96-row m-tiles, so that an expert's weights are streamed once for
   // up to 96 of its pairs, with pair-wide weight copies too (half as many
   // cache-line requests per stage for the same bytes).
-  const int mf = pick_mf(s, 6);
+  // With MXFP4 activations a stage holds a quarter of the matrix-core work
+  // of the exact passes, so the 96-row tiles take deeper rings (3 activation
+  // stages, 4 weight stages) to keep more copies in flight.
   if (mf <= 1) K3_SC(1, 4, 4, 4, true);
   else if (mf <= 3) K3_SC(3, 4, 2, 5, false);
+  else if (q4)
+    mx_gemm_scaled<6, 4, 3, 4, false, true, true><<<g, 512, 0, st>>>(
+        xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k, G);
   else K3_SC(6, 4, 2, 2, true);
 #undef K3_SC
   return hipGetLastError();
@@ -1001,10 +1181,11 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
 
 hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st) {
+  const bool q4 = s.act == K3MOE_ACT_MXFP4;
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
   const uint8_t* w = static_cast<const uint8_t*>(b.w2);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w2_scale);
-  if (s.T == 1) {
+  if (s.T == 1 && !q4) {
     // 7 fragments per wave where d allows (d = 7168: 256 workgroups), else 8
     if (const int lds = down_1tok_lds(s, 7)) {
       const int cpe = s.d / (64 * 7);
@@ -1020,12 +1201,22 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
     }
   }
   const dim3 g(grouped_grid());
-#define K3_SD(MF, NF, RA, RB, PB)                                                           \
-  mx_gemm_scaled<MF, NF, RA, RB, true, PB><<<g, 512, 0, st>>>(                               \
-      hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k)
   const int mf = pick_mf(s, 6);
+  const int G = pick_g(s, mf);
+#define K3_SD(MF, NF, RA, RB, PB)                                                            \
+  do {                                                                                        \
+    if (q4)                                                                                   \
+      mx_gemm_scaled<MF, NF, RA, RB, true, PB, true><<<g, 512, 0, st>>>(                      \
+          hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);                             \
+    else                                                                                      \
+      mx_gemm_scaled<MF, NF, RA, RB, true, PB, false><<<g, 512, 0, st>>>(                     \
+          hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);                             \
+  } while (0)
   if (mf <= 1) K3_SD(1, 4, 4, 4, true);
   else if (mf <= 3) K3_SD(3, 4, 2, 5, false);
+  else if (q4)
+    mx_gemm_scaled<6, 4, 3, 4, true, true, true><<<g, 512, 0, st>>>(
+        hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);
   else K3_SD(6, 4, 2, 3, false);
 #undef K3_SD
   return hipGetLastError();

@@ -4,7 +4,7 @@ computation happens in libk3moe's kernels; this file only marshals."""
 import torch
 
 from . import (BF16, DIAG_COUNT, F32, FMT_BF16, FMT_MXFP4, OP_EXPERT_FFN, OP_EXPERT_GATEUP,
-               OP_LAYER, OP_PERMUTE, OP_ROUTE, OP_SHARED_FFN, ROUTERS, k3moe_combine,
+               OP_LAYER, OP_PERMUTE, OP_ROUTE, OP_SHARED_FFN, ACTS, ROUTERS, k3moe_combine,
                k3moe_expert_down,
                k3moe_expert_ffn, k3moe_expert_gateup, k3moe_layer, k3moe_path_class,
                k3moe_permute, k3moe_route, k3moe_shared_ffn, k3moe_workspace_bytes, make_bank, make_shape, make_weights)
@@ -17,10 +17,12 @@ class MoELayer:
     w13_scale [E][2f][d/32], w2 [E][d][f/2], w2_scale [E][d][f/32]; shared:
     dict of bf16 tensors w13 [S][2fs][d], w2 [S][d][fs] (or empty); router:
     "softmax", "sigmoid" or "sigmoid_norm", with router_bias an fp32 [E]
-    tensor (or None) for the sigmoid routers."""
+    tensor (or None) for the sigmoid routers; act: "exact" or "mxfp4" (the
+    routed experts' activations quantised to MXFP4)."""
 
     def __init__(self, w_router, routed: dict, shared: dict, k: int,
-                 out_dtype=torch.bfloat16, router: str = "softmax", router_bias=None):
+                 out_dtype=torch.bfloat16, router: str = "softmax", router_bias=None,
+                 act: str = "exact"):
         self.w_router = w_router
         self.routed = routed
         self.shared = shared
@@ -32,6 +34,7 @@ class MoELayer:
         self.out_dtype = out_dtype
         self.router = ROUTERS[router]
         self.router_bias = router_bias
+        self.act = ACTS[act]
         self.routed_bank = make_bank(FMT_MXFP4, self.E, self.d, self.f, routed["w13"],
                                      routed["w13_scale"], routed["w2"], routed["w2_scale"])
         self.shared_bank = make_bank(FMT_BF16, self.n_shared, self.d, self.f_shared,
@@ -42,7 +45,7 @@ class MoELayer:
     def shape(self, T: int, x_dtype=torch.bfloat16, out_dtype=None):
         out_dtype = self.out_dtype if out_dtype is None else out_dtype
         return make_shape(T, self.d, self.f, self.E, self.k, self.n_shared, self.f_shared,
-                          _DT[x_dtype], _DT[out_dtype], self.router)
+                          _DT[x_dtype], _DT[out_dtype], self.router, self.act)
 
     def workspace(self, shape, op):
         n = k3moe_workspace_bytes(shape, op)
