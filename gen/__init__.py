@@ -34,7 +34,8 @@ from .configs import CONFIGS, ORDER, LayerConfig, get  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
-T_X, T_ROUTER, T_W13, T_W13S, T_W2, T_W2S, T_SH13, T_SH2, T_ZIPF, T_RBIAS = range(1, 11)
+(T_X, T_ROUTER, T_W13, T_W13S, T_W2, T_W2S, T_SH13, T_SH2, T_ZIPF, T_RBIAS, T_RVQ13, T_RVQ2,
+ T_RVQCB13, T_RVQCB2) = range(1, 15)
 
 _host = None
 _dev = None
@@ -247,6 +248,52 @@ def fill_routed_bank_device(cfg: LayerConfig, ptrs: dict, stream: int = 0):
             rc = lib.k3gen_dev_bytes(kk, 0, n, ptrs[name], stream)
         if rc != 0:
             raise RuntimeError(f"device fill of {name} failed with HIP error {rc}")
+
+
+# ------------------------------------------------------------- RVQ3 experts
+RVQ_SIGMA = (0.05, 0.0125, 0.003)   # codebook spread per stage (residual stages shrink)
+
+
+def rvq_sizes(cfg: LayerConfig) -> dict:
+    """Bytes per expert of each RVQ3 tensor: 3 index bytes per 8 weights
+    (3.00 bits per weight) and three [256][8] fp32 codebooks per matrix."""
+    return dict(w13=3 * 2 * cfg.f * cfg.d // 8, w2=3 * cfg.d * cfg.f // 8, w13_cb=3 * 256 * 8 * 4,
+                w2_cb=3 * 256 * 8 * 4)
+
+
+def rvq_codebooks(cfg: LayerConfig, e0: int, e1: int, which: str) -> np.ndarray:
+    """Codebooks [e1-e0][3][256][8] fp32 of matrix `which` ("w13" or "w2"):
+    stage s ~ N(0, RVQ_SIGMA[s])."""
+    k = key(cfg.seed, T_RVQCB13 if which == "w13" else T_RVQCB2)
+    out = np.empty((e1 - e0, 3, 256, 8), dtype=np.float32)
+    for e in range(e0, e1):
+        for st in range(3):
+            out[e - e0, st] = _normal_f32(k, (e * 3 + st) * 2048, 2048,
+                                          RVQ_SIGMA[st]).reshape(256, 8)
+    return out
+
+
+def rvq_expert(cfg: LayerConfig, e: int) -> dict:
+    """Expert e of the RVQ3 bank: w13 [3][d/128][2f][16] u8 indices (rows 0..f-1
+    gate, f..2f-1 up), w2 [3][f/128][d][16], and their codebooks."""
+    sz = rvq_sizes(cfg)
+    w13 = _bytes(key(cfg.seed, T_RVQ13), e * sz["w13"], sz["w13"])
+    w2 = _bytes(key(cfg.seed, T_RVQ2), e * sz["w2"], sz["w2"])
+    return dict(w13=w13.reshape(3, cfg.d // 128, 2 * cfg.f, 16),
+                w2=w2.reshape(3, cfg.f // 128, cfg.d, 16),
+                w13_cb=rvq_codebooks(cfg, e, e + 1, "w13")[0],
+                w2_cb=rvq_codebooks(cfg, e, e + 1, "w2")[0])
+
+
+def fill_rvq_bank_device(cfg: LayerConfig, ptrs: dict, stream: int = 0):
+    """Write all E experts' RVQ3 indices into device buffers (name -> address);
+    the codebooks come from rvq_codebooks (host)."""
+    lib = _load_dev()
+    sz = rvq_sizes(cfg)
+    for name, tid in (("w13", T_RVQ13), ("w2", T_RVQ2)):
+        rc = lib.k3gen_dev_bytes(key(cfg.seed, tid), 0, sz[name] * cfg.E, ptrs[name], stream)
+        if rc != 0:
+            raise RuntimeError(f"device fill of rvq {name} failed with HIP error {rc}")
 
 
 # --------------------------------------------------------------- shared experts

@@ -63,6 +63,8 @@ class Oracle:
         lib.oracle_mxfp4_ffn.argtypes = [_I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P]
         lib.oracle_quantize_mxfp4.argtypes = [_I64, _P, _P, _P]
         lib.oracle_mxfp4_ffn_qact.argtypes = [_I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P]
+        lib.oracle_rvq_decode.argtypes = [_I64, _I64, _I64, _I32, _P, _P, _P]
+        lib.oracle_rvq_ffn.argtypes = [_I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P]
         lib.oracle_bf16_ffn.argtypes = [_I32, _I32, _P, _P, _I64, _P, _P]
         lib.oracle_combine.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
         lib.oracle_threads.restype = _I32
@@ -191,6 +193,32 @@ class Oracle:
                                        _ptr(x64), _ptr(y), _ptr(h))
         return (y, h) if want_h else y
 
+    def rvq_decode(self, idx: np.ndarray, cb: np.ndarray, rows: int, cols: int) -> np.ndarray:
+        """RVQ3 matrix (idx [3][cols/128][rows][16] u8, cb [3][256][8] fp32) ->
+        [rows][cols] fp64, each weight the sum of its three codeword entries."""
+        idx = np.ascontiguousarray(idx, dtype=np.uint8)
+        cb = np.ascontiguousarray(cb, dtype=np.float32)
+        assert idx.size == 3 * rows * cols // 8 and cb.shape == (3, 256, 8)
+        out = np.empty((rows, cols), dtype=np.float64)
+        self.lib.oracle_rvq_decode(0, rows, rows, cols, _ptr(idx), _ptr(cb), _ptr(out))
+        return out
+
+    def rvq_ffn(self, expert: dict, x64: np.ndarray, want_h: bool = False):
+        """One RVQ3 expert (dict w13, w13_cb, w2, w2_cb) over rows x64."""
+        x64 = np.ascontiguousarray(x64, dtype=np.float64)
+        n, d = x64.shape
+        w13 = np.ascontiguousarray(expert["w13"], dtype=np.uint8)
+        w13c = np.ascontiguousarray(expert["w13_cb"], dtype=np.float32)
+        w2 = np.ascontiguousarray(expert["w2"], dtype=np.uint8)
+        w2c = np.ascontiguousarray(expert["w2_cb"], dtype=np.float32)
+        f = w13.size * 8 // 3 // d // 2
+        assert w13.size == 3 * 2 * f * d // 8 and w2.size == 3 * d * f // 8
+        y = np.empty((n, d), dtype=np.float64)
+        h = np.empty((n, f), dtype=np.float64) if want_h else None
+        self.lib.oracle_rvq_ffn(d, f, _ptr(w13), _ptr(w13c), _ptr(w2), _ptr(w2c), n, _ptr(x64),
+                                _ptr(y), _ptr(h))
+        return (y, h) if want_h else y
+
     def bf16_ffn(self, w13: np.ndarray, w2: np.ndarray, x64: np.ndarray):
         x64 = np.ascontiguousarray(x64, dtype=np.float64)
         n, d = x64.shape
@@ -211,9 +239,10 @@ class Oracle:
         return acc
 
     def expert(self, act: str):
-        """The expert FFN of an activation mode: "exact" (activations as given)
-        or "mxfp4" (x and h quantised to MXFP4)."""
-        return {"exact": self.mxfp4_ffn, "mxfp4": self.mxfp4_ffn_qact}[act]
+        """The expert FFN of a mode: "exact" (MXFP4 experts, activations as
+        given), "mxfp4" (MXFP4 experts, x and h quantised to MXFP4) or "rvq3"
+        (RVQ3 experts)."""
+        return {"exact": self.mxfp4_ffn, "mxfp4": self.mxfp4_ffn_qact, "rvq3": self.rvq_ffn}[act]
 
     def routed_ffn(self, x64, get_expert, counts, offsets, sorted_pair, k, act="exact"):
         """y_perm [P][d]: row p = expert e's output on the token of pair

@@ -349,6 +349,74 @@ void oracle_mxfp4_ffn_qact(int d, int f, const uint8_t* w13, const uint8_t* w13s
   free(h);
 }
 
+/* ---------------------------------------------------------------------------
+ * RVQ3 experts (WASTE article page, section "정확성 검증과 양자화": expert
+ * weights in residual vector quantisation at 3.00 bits per weight, three
+ * stages of 256-entry codebooks per 8-dimensional vector).  A matrix of
+ * rows x cols has, for every row r and group g of 8 columns, three 8-bit
+ * indices i_s[r][g]; its weights are
+ *   W[r][8g + j] = C_0[i_0[r][g]][j] + C_1[i_1[r][g]][j] + C_2[i_2[r][g]][j]
+ * with C_s [256][8] fp32 codebooks of the matrix.  Index layout (this
+ * library's): idx[s][cols/128][rows][16], i.e. per stage, per slice of 16
+ * groups, every row's 16 indices contiguous; codebooks cb[s][256][8].
+ * ------------------------------------------------------------------------- */
+static double rvq_elem(const uint8_t* idx, const float* cb, int64_t rows, int cols, int64_t r,
+                       int c) {
+  int g = c / 8, j = c % 8, sl = g / 16, gi = g % 16;
+  double w = 0.0;
+  for (int s = 0; s < 3; ++s) {
+    uint8_t i = idx[(((int64_t)s * (cols / 128) + sl) * rows + r) * 16 + gi];
+    w += (double)cb[((int64_t)s * 256 + i) * 8 + j];
+  }
+  return w;
+}
+
+/* Decode rows [r0, r0 + nr) of an RVQ3 matrix to fp64 (codeword sums in fp64). */
+void oracle_rvq_decode(int64_t r0, int64_t nr, int64_t rows, int cols, const uint8_t* idx,
+                       const float* cb, double* out) {
+  for (int64_t r = 0; r < nr; ++r)
+    for (int c = 0; c < cols; ++c) out[r * cols + c] = rvq_elem(idx, cb, rows, cols, r0 + r, c);
+}
+
+/* One RVQ3 expert over n activation rows: the same FFN as the MXFP4 expert,
+ * g, u from w13 (rows 0..f-1 gate, f..2f-1 up), y from w2, fp64, ascending. */
+void oracle_rvq_ffn(int d, int f, const uint8_t* w13i, const float* w13c, const uint8_t* w2i,
+                    const float* w2c, int64_t n, const double* x, double* y, double* h_out) {
+  double* g = (double*)malloc(sizeof(double) * (size_t)(n * f));
+  double* u = (double*)malloc(sizeof(double) * (size_t)(n * f));
+  double* h = (double*)malloc(sizeof(double) * (size_t)(n * f));
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * (size_t)(d > f ? d : f));
+#pragma omp for schedule(static)
+    for (int j = 0; j < 2 * f; ++j) {
+      oracle_rvq_decode(j, 1, 2 * f, d, w13i, w13c, row);
+      for (int64_t r = 0; r < n; ++r) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += row[i] * x[r * d + i];
+        if (j < f) g[r * f + j] = acc;
+        else u[r * f + (j - f)] = acc;
+      }
+    }
+#pragma omp for schedule(static)
+    for (int64_t q = 0; q < n * f; ++q) h[q] = silu(g[q]) * u[q];
+#pragma omp for schedule(static)
+    for (int o = 0; o < d; ++o) {
+      oracle_rvq_decode(o, 1, d, f, w2i, w2c, row);
+      for (int64_t r = 0; r < n; ++r) {
+        double acc = 0.0;
+        for (int j = 0; j < f; ++j) acc += row[j] * h[r * f + j];
+        y[r * d + o] = acc;
+      }
+    }
+    free(row);
+  }
+  if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)(n * f));
+  free(g);
+  free(u);
+  free(h);
+}
+
 /* One bf16 expert (the always-on shared experts): same FFN with
  * w13 [2f][d] and w2 [d][f] bf16. */
 void oracle_bf16_ffn(int d, int f, const uint16_t* w13, const uint16_t* w2, int64_t n,

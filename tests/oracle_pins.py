@@ -432,6 +432,82 @@ def pin_qact_ffn_dense(o):
     assert np.max(np.abs(y - want)) <= 1e-12 * np.max(np.abs(want))
 
 
+# ------------------------------------------------------------- RVQ3 experts
+def _rvq_tiny():
+    cfg = gen.configs.LayerConfig(name="rvq_tiny", T=3, d=256, f=128, E=4, k=2, n_shared=0,
+                                  f_shared=0, x_dtype="f32", out_dtype="f32", scale_lo=-4,
+                                  scale_hi=0)
+    return cfg, gen.rvq_expert(cfg, 2), to_f64(gen.x(cfg))
+
+
+def np_rvq_decode(idx, cb, rows, cols):
+    """Independent decode: gather the three codewords of every (row, group)
+    from the index layout [3][cols/128][rows][16] and add them."""
+    idx = np.asarray(idx).reshape(3, cols // 128, rows, 16)
+    groups = idx.transpose(0, 2, 1, 3).reshape(3, rows, cols // 8)      # [s][row][group]
+    w = np.zeros((rows, cols // 8, 8))
+    for st in range(3):
+        w = w + cb[st].astype(np.float64)[groups[st]]
+    return w.reshape(rows, cols)
+
+
+def pin_rvq_decode_definition(o):
+    """The oracle's RVQ3 decode equals the codeword sums gathered by numpy."""
+    c, ex, _ = _rvq_tiny()
+    got = o.rvq_decode(ex["w13"], ex["w13_cb"], 2 * c.f, c.d)
+    assert np.array_equal(got, np_rvq_decode(ex["w13"], ex["w13_cb"], 2 * c.f, c.d))
+    got2 = o.rvq_decode(ex["w2"], ex["w2_cb"], c.d, c.f)
+    assert np.array_equal(got2, np_rvq_decode(ex["w2"], ex["w2_cb"], c.d, c.f))
+
+
+def pin_rvq_partial_dot_tables(o):
+    """The pages' evaluation, partial-dot tables: per token T_s[g][j] =
+    C_s[j] . x_g, then y_r = sum over groups and stages of T_s[g][i_s[r][g]];
+    it equals the oracle's FFN on the materialised weights (fp64 rounding)."""
+    c, ex, x64 = _rvq_tiny()
+    y, h = o.rvq_ffn(ex, x64, want_h=True)
+    def table_gemv(idx, cb, rows, cols, v):
+        groups = np.asarray(idx).reshape(3, cols // 128, rows, 16).transpose(0, 2, 1, 3)
+        groups = groups.reshape(3, rows, cols // 8)
+        out = np.zeros((v.shape[0], rows))
+        for t in range(v.shape[0]):
+            vg = v[t].reshape(cols // 8, 8)
+            for st in range(3):
+                table = vg @ cb[st].astype(np.float64).T                 # [group][entry]
+                out[t] += table[np.arange(cols // 8)[None, :], groups[st]].sum(axis=1)
+        return out
+    gu = table_gemv(ex["w13"], ex["w13_cb"], 2 * c.f, c.d, x64)
+    hh = np_silu(gu[:, :c.f]) * gu[:, c.f:]
+    yy = table_gemv(ex["w2"], ex["w2_cb"], c.d, c.f, hh)
+    assert np.max(np.abs(h - hh)) <= 1e-12 * np.max(np.abs(hh))
+    assert np.max(np.abs(y - yy)) <= 1e-12 * np.max(np.abs(yy))
+
+
+def pin_rvq_bytes_per_weight(o):
+    """3 stages of 8-bit indices per 8 weights = 3.00 bits per weight; at the
+    pages' expert size, 16 experts in each of 92 layers read about 17 GB per
+    token."""
+    g = _golden("rvq_byte_accounting.json")
+    c, ex, _ = _rvq_tiny()
+    assert ex["w13"].size * 8 / (2 * c.f * c.d) == g["bits_per_weight"]
+    assert ex["w2"].size * 8 / (c.d * c.f) == g["bits_per_weight"]
+    assert ex["w13_cb"].shape == (g["stages"], g["codebook_entries"], g["vector_dim"])
+    per_token = g["experts_per_token"] * g["expert_params"] * g["bits_per_weight"] / 8
+    assert abs(per_token / 2 ** 30 - g["gb_read_per_token_page"]) < 0.05
+
+
+def pin_rvq_single_codeword(o):
+    """Closed form: with stages 1 and 2 zero and stage 0's entry j equal to
+    (j, j+1, ..., j+7) / 64, weight (r, 8g + k) is (i_0[r][g] + k) / 64."""
+    c, ex, _ = _rvq_tiny()
+    cb = np.zeros((3, 256, 8), dtype=np.float32)
+    cb[0] = (np.arange(256)[:, None] + np.arange(8)[None, :]) / 64.0
+    w = o.rvq_decode(ex["w13"], cb, 2 * c.f, c.d)
+    i0 = ex["w13"][0].transpose(1, 0, 2).reshape(2 * c.f, c.d // 8)
+    want = (np.repeat(i0, 8, axis=1) + np.tile(np.arange(8), c.d // 8)) / 64.0
+    assert np.array_equal(w, want)
+
+
 # ----------------------------------------------------------------- layer
 def _layer_tiny(o, x=None, wr=None, bank=None, sh="default"):
     c, x0, wr0, bank0, sh0 = tiny_inputs()

@@ -55,6 +55,11 @@ MUTANTS = {
     "mx_quant_sign_dropped": ("int code = best | (signbit(vb[i]) ? 8 : 0);", "int code = best;"),
     "qact_h_not_quantised": ("  quantize_rows(n, f, h);\n", "\n"),
     "qact_x_not_quantised": ("  quantize_rows(n, d, xq);\n", "\n"),
+    "rvq_two_stages": ("for (int s = 0; s < 3; ++s) {\n    uint8_t i = idx[", "for (int s = 0; s < 2; ++s) {\n    uint8_t i = idx["),
+    "rvq_slice_group_swapped": ("int g = c / 8, j = c % 8, sl = g / 16, gi = g % 16;",
+                                "int g = c / 8, j = c % 8, sl = g % 16 % (cols / 128), gi = g / 16 % 16;"),
+    "rvq_codeword_offset": ("w += (double)cb[((int64_t)s * 256 + i) * 8 + j];",
+                            "w += (double)cb[((int64_t)s * 256 + i) * 8 + (j + 1) % 8];"),
     "bf16_decode_wrong": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)(b & 0xFF7F) << 16;"),
 }
 
