@@ -12,7 +12,10 @@ of the metric, each with the same seeded synthetic weights:
   prefill_16384_zipf  16384 tokens a step, expert popularity skewed Zipf(1.1)
 and the two prefill batches again with the quantised-activation mode
 (x and h in MXFP4, so the routed products run on the FP4 matrix rate): an
-approximation of the layer, reported beside the exact one, never in its place.
+approximation of the layer, reported beside the exact one, never in its place;
+and the decode batches with the routed experts in the pages' second format,
+RVQ3 (three 256-entry codebooks per 8-weight vector, 3.00 bits per weight),
+multiplied through per-token partial-dot tables.
 Decode steps each take fresh tokens, so every step routes to another expert
 set and the routed weights stream from HBM, not from a cache warmed by the
 previous step; prefill batches touch every expert at every step.
@@ -45,8 +48,11 @@ X_PASSES = 2                       # E4M3 passes that carry bf16 x exactly (one 
 SPIN_CYCLES = 20_000_000           # ~10 ms of GPU spin ahead of a timed run of launches
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (MXFP4 bytes) at batch 1/64/4096"
 WORKLOADS = ["decode_b1", "decode_b64", "prefill_4096", "prefill_16384_zipf",
-             "prefill_4096_mxfp4act", "prefill_16384_zipf_mxfp4act"]
+             "prefill_4096_mxfp4act", "prefill_16384_zipf_mxfp4act", "decode_b1_rvq3",
+             "decode_b64_rvq3"]
 QACT = "_mxfp4act"   # suffix: the routed experts' activations quantised to MXFP4
+RVQ = "_rvq3"        # suffix: the routed experts in the RVQ3 format (3.00 bits per weight)
+RVQ_CODEBOOK_BYTES = 3 * 256 * 8 * 4   # per expert matrix
 KERNEL_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "mxscale.hip")
 
 
@@ -80,7 +86,7 @@ def stored_traffic(workload: str):
 
 
 # ---------------------------------------------------------------- CPU oracle
-def cpu_baseline_one_token(cfg, budget_s: float):
+def cpu_baseline_one_token(cfg, budget_s: float, act: str = "exact"):
     """Decode at batch 1: the oracle's whole layer (fp64 router, top-k, the
     token's experts, the shared experts, combine), one token after another,
     until about budget_s seconds of oracle time are spent."""
@@ -95,14 +101,15 @@ def cpu_baseline_one_token(cfg, budget_s: float):
         t0 = time.perf_counter()
         _, idx, w = orc.route(oracle.to_f64(x), wr, cfg.k)
         spent += time.perf_counter() - t0
-        need = {int(e): gen.routed_expert(cfg, int(e)) for e in idx.ravel()}   # untimed
+        get = gen.rvq_expert if act == "rvq3" else gen.routed_expert
+        need = {int(e): get(cfg, int(e)) for e in idx.ravel()}   # untimed
         t0 = time.perf_counter()
-        orc.token_outputs(x, idx, w, lambda e: need[e], shared)
+        orc.token_outputs(x, idx, w, lambda e: need[e], shared, act)
         spent += time.perf_counter() - t0
         done += 1
     return dict(value=done / spent, unit="tokens/s", cores=orc.threads(), kind="oracle",
                 sample=f"the first {done} token(s) of {cfg.name}, one at a time through the "
-                       f"whole oracle layer (fp64 router, top-k, {cfg.k} MXFP4 experts, "
+                       f"whole oracle layer (fp64 router, top-k, {cfg.k} {act} experts, "
                        f"{cfg.n_shared} shared, combine); {spent:.1f} s of oracle time")
 
 
@@ -132,14 +139,15 @@ def cpu_baseline_batch(cfg, budget_s: float, act: str = "exact"):
     order = np.random.default_rng(0).permutation(touched)
     rows, secs = [], []
     # two anchors for the line: one expert on 1 row and on 256 rows
-    ex = gen.routed_expert(cfg, int(order[0]))
+    ex = (gen.rvq_expert if act == "rvq3" else gen.routed_expert)(cfg, int(order[0]))
     for nr in (1, min(256, T)):
         t0 = time.perf_counter()
         ffn(ex, x64[:nr])
         secs.append(time.perf_counter() - t0)
         rows.append(nr)
+    get = gen.rvq_expert if act == "rvq3" else gen.routed_expert
     for e in order:
-        ex = gen.routed_expert(cfg, int(e))   # untimed
+        ex = get(cfg, int(e))   # untimed
         toks = sp[offsets[e]:offsets[e + 1]][:256] // cfg.k
         t0 = time.perf_counter()
         ffn(ex, x64[toks])
@@ -189,7 +197,8 @@ def run_workload(name, args, weights):
     from mxfp4_routed_expert_gemv_amd.layer import MoELayer
 
     qact = name.endswith(QACT)
-    cfg = gen.get(name[:-len(QACT)] if qact else name)
+    rvq = name.endswith(RVQ)
+    cfg = gen.get(name[:-len(QACT)] if qact else name[:-len(RVQ)] if rvq else name)
     big = cfg.T >= 1024
     K = args.steps if args.steps is not None else (10 if big else 50)
     W = args.warmup if args.warmup is not None else (3 if big else 5)
@@ -198,8 +207,11 @@ def run_workload(name, args, weights):
     w_router = weights.w_router
     if cfg.zipf_s is not None:
         w_router = gen.device._to_dev_bf16(gen.router(cfg), "cuda")
-    layer = MoELayer(w_router, weights.routed, weights.shared, cfg.k, out_dtype=torch.bfloat16,
-                     act="mxfp4" if qact else "exact")
+    if rvq and "rvq" not in weights.extra:
+        log("building the RVQ3 bank")
+        weights.extra["rvq"] = gen.device.build_rvq(gen.get("decode_b1"))
+    layer = MoELayer(w_router, weights.extra["rvq"] if rvq else weights.routed, weights.shared,
+                     cfg.k, out_dtype=torch.bfloat16, act="mxfp4" if qact else "exact")
     T = cfg.T
     # decode: K + W distinct batches (fresh expert sets every step); prefill
     # batches touch every expert anyway, so two batches alternate
@@ -267,14 +279,15 @@ def run_workload(name, args, weights):
     b.record(stream)
     torch.cuda.synchronize()
     gu_avg_s = a.elapsed_time(b) / K / 1e3
-    per_expert_gu = lib.k3moe_mxfp4_bytes(2 * cfg.f, cfg.d)
+    per_expert_gu = (2 * cfg.f * cfg.d * 3 // 8 + RVQ_CODEBOOK_BYTES if rvq
+                     else lib.k3moe_mxfp4_bytes(2 * cfg.f, cfg.d))
     gu_bytes = sum(touched) / len(touched) * per_expert_gu
     gu_gbs = gu_bytes / gu_avg_s / 1e9
     gu_flops = 2.0 * T * cfg.k * 2 * cfg.f * cfg.d      # useful gate/up FLOPs per launch
     gu_tflops = gu_flops / gu_avg_s / 1e12
     # the routed experts take the scaled matrix-core instruction at any batch
     # size for bf16 activations and d, f multiples of 512
-    routed_scaled = cfg.x_dtype == "bf16" and cfg.d % 512 == 0 and cfg.f % 512 == 0
+    routed_scaled = cfg.x_dtype == "bf16" and cfg.d % 512 == 0 and cfg.f % 512 == 0 and not rvq
     # the bound of the gate/up kernel: useful FLOPs per weight byte against the
     # ridge of the instruction it issues (fp8 matrix peak / HBM peak)
     mfma_bound = routed_scaled and gu_flops / gu_bytes >= FP8_MFMA_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
@@ -292,7 +305,8 @@ def run_workload(name, args, weights):
     torch.cuda.synchronize()
     ffn_ms = a.elapsed_time(b) / K
     ffn_flops = 2.0 * T * cfg.k * 3 * cfg.f * cfg.d
-    per_expert = lib.k3moe_mxfp4_bytes(2 * cfg.f, cfg.d) + lib.k3moe_mxfp4_bytes(cfg.d, cfg.f)
+    per_expert = (3 * cfg.f * cfg.d * 3 // 8 + 2 * RVQ_CODEBOOK_BYTES if rvq else
+                  lib.k3moe_mxfp4_bytes(2 * cfg.f, cfg.d) + lib.k3moe_mxfp4_bytes(cfg.d, cfg.f))
     ffn_bytes = sum(touched) / len(touched) * per_expert
     ffn_tflops = ffn_flops / (ffn_ms / 1e3) / 1e12
     ffn_gbs = ffn_bytes / (ffn_ms / 1e3) / 1e9
@@ -321,7 +335,8 @@ def run_workload(name, args, weights):
     else:
         roof = {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": ("gateup_1tok" if T == 1 and routed_scaled
+                "kernel": ("rvq_partial + rvq_reduce_gateup" if rvq
+                           else "gateup_1tok" if T == 1 and routed_scaled
                            else "mx_gemm_scaled (gate/up)" if routed_scaled
                            else "gateup_persistent"),
                 "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg_s * 1e6,
@@ -343,6 +358,7 @@ def run_workload(name, args, weights):
                    "experts": cfg.E, "top_k": cfg.k, "shared_experts": cfg.n_shared,
                    "weights": "routed MXFP4 (E2M1 + E8M0/32), shared and router bf16",
                    "routed_activations": "MXFP4 (quantised)" if qact else "exact",
+                   "routed_format": "RVQ3 (3.00 bits/weight)" if rvq else "MXFP4",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
@@ -411,12 +427,12 @@ def main():
     if not args.no_cpu_baseline:
         for n in names:
             log(f"timing the CPU oracle on {n}")
-            qact = n.endswith(QACT)
-            cfg = gen.get(n[:-len(QACT)] if qact else n)
-            results[n]["cpu_baseline"] = (cpu_baseline_one_token(cfg, args.cpu_seconds)
+            qact, rvq = n.endswith(QACT), n.endswith(RVQ)
+            cfg = gen.get(n[:-len(QACT)] if qact else n[:-len(RVQ)] if rvq else n)
+            act = "mxfp4" if qact else "rvq3" if rvq else "exact"
+            results[n]["cpu_baseline"] = (cpu_baseline_one_token(cfg, args.cpu_seconds, act)
                                           if cfg.T == 1 else
-                                          cpu_baseline_batch(cfg, args.cpu_seconds,
-                                                             "mxfp4" if qact else "exact"))
+                                          cpu_baseline_batch(cfg, args.cpu_seconds, act))
     line = dict(results[names[0]])
     if len(names) > 1:
         line["workloads"] = results

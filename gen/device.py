@@ -9,8 +9,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-from . import (fill_routed_bank_device, routed_bank, routed_sizes, router, shared_bank,
-               x as gen_x)
+from . import (fill_routed_bank_device, fill_rvq_bank_device, routed_bank, routed_sizes, router,
+               rvq_codebooks, rvq_expert, rvq_sizes, shared_bank, x as gen_x)
 from .configs import LayerConfig
 
 
@@ -55,3 +55,22 @@ def build(cfg: LayerConfig, device="cuda", routed_on_device: bool = None) -> Dev
         sh = shared_bank(cfg)
         shared = {k: _to_dev_bf16(v, device) for k, v in sh.items()}
     return DeviceWorkload(cfg, x, wr, routed, shared)
+
+
+def build_rvq(cfg: LayerConfig, device="cuda", on_device: bool = None) -> dict:
+    """The RVQ3 routed bank of cfg in device memory: w13 [E][3][d/128][2f][16],
+    w2 [E][3][f/128][d][16] uint8 indices (device fill, or host for small
+    banks) and their fp32 codebooks w13_cb, w2_cb [E][3][256][8]."""
+    if on_device is None:
+        on_device = cfg.E * cfg.d * cfg.f > (1 << 24)
+    shapes = dict(w13=(cfg.E, 3, cfg.d // 128, 2 * cfg.f, 16), w2=(cfg.E, 3, cfg.f // 128, cfg.d, 16))
+    if on_device:
+        bank = {k: torch.empty(v, dtype=torch.uint8, device=device) for k, v in shapes.items()}
+        fill_rvq_bank_device(cfg, {k: v.data_ptr() for k, v in bank.items()},
+                             torch.cuda.current_stream().cuda_stream)
+    else:
+        ex = [rvq_expert(cfg, e) for e in range(cfg.E)]
+        bank = {k: torch.from_numpy(np.stack([x[k] for x in ex])).to(device) for k in shapes}
+    for k in ("w13", "w2"):
+        bank[k + "_cb"] = torch.from_numpy(rvq_codebooks(cfg, 0, cfg.E, k)).to(device)
+    return bank

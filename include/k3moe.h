@@ -60,7 +60,7 @@ typedef enum k3moe_status {
 /* Activation / output element types. */
 enum { K3MOE_F32 = 0, K3MOE_BF16 = 1 };
 /* Expert weight formats. */
-enum { K3MOE_FMT_MXFP4 = 0, K3MOE_FMT_BF16 = 1 };
+enum { K3MOE_FMT_MXFP4 = 0, K3MOE_FMT_BF16 = 1, K3MOE_FMT_RVQ3 = 2 };
 /* Operation ids for k3moe_workspace_bytes(). */
 enum {
   K3MOE_OP_ROUTE = 0,
@@ -124,7 +124,9 @@ enum {
  * E <= 1024; 0 <= n_shared <= 8; f_shared % 32 == 0 (>= 32 when n_shared > 0);
  * x_dtype, out_dtype in {K3MOE_F32, K3MOE_BF16}; router one of
  * K3MOE_ROUTER_* (0, the softmax router, for a zero-initialised shape);
- * act one of K3MOE_ACT_* (0, exact activations, when zero-initialised). */
+ * act one of K3MOE_ACT_* (0, exact activations, when zero-initialised);
+ * routed_format K3MOE_FMT_MXFP4 (0) or K3MOE_FMT_RVQ3 (with exact activations,
+ * d % 128 == 0, f % 128 == 0). */
 typedef struct k3moe_shape {
   int64_t T;         /* tokens */
   int32_t d;         /* hidden size */
@@ -137,6 +139,7 @@ typedef struct k3moe_shape {
   int32_t out_dtype; /* layer output [T][d] */
   int32_t router;    /* K3MOE_ROUTER_* */
   int32_t act;       /* K3MOE_ACT_* (routed experts' activation mode) */
+  int32_t routed_format; /* K3MOE_FMT_MXFP4 (0) or K3MOE_FMT_RVQ3: the routed bank's format */
 } k3moe_shape;
 
 /* A bank of experts, expert-major (each expert's bytes contiguous).
@@ -147,7 +150,17 @@ typedef struct k3moe_shape {
  *   w2_scale  [n][d][f/32]  u8
  *   Byte i of a row holds element 2i in its low nibble, 2i+1 in its high
  *   nibble; elements 32b..32b+31 share scale byte b of the row.
- * BF16 (shared experts): w13 [n][2f][d], w2 [n][d][f] bf16; scales NULL. */
+ * BF16 (shared experts): w13 [n][2f][d], w2 [n][d][f] bf16; scales NULL.
+ * RVQ3 (routed experts, the pages' second format: residual vector
+ * quantisation at 3.00 bits per weight — WASTE article page, section
+ * "정확성 검증과 양자화"): every 8-weight vector is the sum of one entry of
+ * each of three 256-entry codebooks of its matrix,
+ *   W[r][8g + j] = C_0[i_0[r][g]][j] + C_1[i_1[r][g]][j] + C_2[i_2[r][g]][j];
+ *   w13       [n][3][d/128][2f][16] u8 indices (stage, slice of 16 groups,
+ *             row, group within the slice); rows 0..f-1 gate, f..2f-1 up
+ *   w13_scale [n][3][256][8] fp32 codebooks C_s of w13
+ *   w2        [n][3][f/128][d][16] u8, w2_scale [n][3][256][8] fp32
+ *   (needs d % 128 == 0 and f % 128 == 0; shape.routed_format = RVQ3). */
 typedef struct k3moe_expert_bank {
   int32_t format;    /* K3MOE_FMT_MXFP4 or K3MOE_FMT_BF16 */
   int32_t n_experts;
@@ -246,7 +259,9 @@ k3moe_status k3moe_permute(const k3moe_shape* shape, const int32_t* topk_idx, in
  * page, "KDA/MLA/MoE" table; explainer page, "reduction one"); the gated
  * activation is taken as SiLU (the pages name a bounded "SiTU" gate without
  * a formula).
- * Routed mode (bank MXFP4, n_experts = E; sorted_pair != NULL):
+ * Routed mode (bank MXFP4 or RVQ3 as shape.routed_format says, n_experts = E;
+ * sorted_pair != NULL; RVQ3 banks are multiplied through per-token
+ * partial-dot tables of their codebooks, the WASTE article page's method):
  *   y [T*k][d] fp32, row q = expert e's FFN of token sorted_pair[q] / k,
  *   where e is the expert whose range offsets[e] .. offsets[e+1] holds q;
  *   unweighted.  offsets and sorted_pair as written by k3moe_permute.
@@ -289,6 +304,8 @@ k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_ba
                                  const void* x, const int32_t* offsets,
                                  const int32_t* sorted_pair, float* h, void* workspace,
                                  size_t workspace_bytes, void* stream);
+/* (k3moe_expert_down takes MXFP4 banks only: the RVQ3 down product keeps its
+ * slice partial sums in a workspace, which k3moe_expert_ffn provides.) */
 k3moe_status k3moe_expert_down(const k3moe_shape* shape, const k3moe_expert_bank* bank,
                                const float* h, const int32_t* offsets, float* y, void* stream);
 

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libk3moe.so")
 
 F32, BF16 = 0, 1
-FMT_MXFP4, FMT_BF16 = 0, 1
+FMT_MXFP4, FMT_BF16, FMT_RVQ3 = 0, 1, 2
 (OP_ROUTE, OP_PERMUTE, OP_EXPERT_FFN, OP_SHARED_FFN, OP_COMBINE, OP_LAYER,
  OP_EXPERT_GATEUP) = range(7)
 PATH_GEMV, PATH_MFMA = 0, 1
@@ -45,7 +45,7 @@ class Shape(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("f_shared", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("router", ctypes.c_int32),
-                ("act", ctypes.c_int32)]
+                ("act", ctypes.c_int32), ("routed_format", ctypes.c_int32)]
 
 
 class ExpertBank(ctypes.Structure):
@@ -218,8 +218,9 @@ def k3moe_layer_noalloc(shape, weights: LayerWeights, x, out, diag=None, stream=
 
 # --------------------------------------------------------- struct builders
 def make_shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router=ROUTER_SOFTMAX,
-               act=ACT_EXACT) -> Shape:
-    return Shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router, act)
+               act=ACT_EXACT, routed_format=FMT_MXFP4) -> Shape:
+    return Shape(T, d, f, E, k, n_shared, f_shared, x_dtype, out_dtype, router, act,
+                 routed_format)
 
 
 def make_bank(fmt, n, d, f, w13, w13_scale, w2, w2_scale) -> ExpertBank:

@@ -74,6 +74,12 @@ k3moe_status check_shape(const k3moe_shape* s) {
                                      s->f % 512 == 0))
     return fail(K3MOE_EUNSUPPORTED,
                 "MXFP4 activations need bf16 x, d %% 512 == 0 and f %% 512 == 0");
+  if (s->routed_format != K3MOE_FMT_MXFP4 && s->routed_format != K3MOE_FMT_RVQ3)
+    return fail(K3MOE_EUNSUPPORTED, "routed_format %d is not MXFP4 or RVQ3", s->routed_format);
+  if (s->routed_format == K3MOE_FMT_RVQ3 && (s->d % 128 || s->f % 128))
+    return fail(K3MOE_ESHAPE, "RVQ3 experts need d %% 128 == 0 and f %% 128 == 0");
+  if (s->routed_format == K3MOE_FMT_RVQ3 && s->act != K3MOE_ACT_EXACT)
+    return fail(K3MOE_EUNSUPPORTED, "MXFP4 activations are for MXFP4 experts");
   if (s->d < 32 || s->d > 16384 || s->d % 32)
     return fail(K3MOE_ESHAPE, "d = %d: need 32 <= d <= 16384, d %% 32 == 0", s->d);
   if (s->f < 32 || s->f > 16384 || s->f % 32)
@@ -112,8 +118,12 @@ k3moe_status check_ws(void* ws, size_t have, size_t need) {
 
 k3moe_status check_routed_bank(const k3moe_shape& s, const k3moe_expert_bank* b) {
   if (!b) return fail(K3MOE_EINVAL, "expert bank is NULL");
-  if (b->format != K3MOE_FMT_MXFP4)
-    return fail(K3MOE_EUNSUPPORTED, "routed experts must be MXFP4 (format %d)", b->format);
+  if (b->format != K3MOE_FMT_MXFP4 && b->format != K3MOE_FMT_RVQ3)
+    return fail(K3MOE_EUNSUPPORTED, "routed experts must be MXFP4 or RVQ3 (format %d)",
+                b->format);
+  if (b->format != s.routed_format)
+    return fail(K3MOE_EINVAL, "routed bank format %d differs from shape routed_format %d",
+                b->format, s.routed_format);
   if (b->n_experts != s.E || b->d != s.d || b->f != s.f)
     return fail(K3MOE_EINVAL, "routed bank (n=%d, d=%d, f=%d) does not match shape (E=%d, d=%d, f=%d)",
                 b->n_experts, b->d, b->f, s.E, s.d, s.f);
@@ -175,6 +185,7 @@ ExpertWs carve_gateup(const k3moe_shape& s, void* ws, size_t* bytes) {
   ExpertWs r;
   r.h = nullptr;
   r.xq = routed_scaled(s) ? c.take<uint8_t>(xq_bytes(s)) : nullptr;
+  r.part = s.routed_format == K3MOE_FMT_RVQ3 ? c.take<float>(rvq_part_floats(s)) : nullptr;
   if (bytes) *bytes = c.off;
   return r;
 }
@@ -184,6 +195,7 @@ ExpertWs carve_expert(const k3moe_shape& s, void* ws, size_t* bytes) {
   ExpertWs r;
   r.h = c.take<float>((size_t)s.T * s.k * s.f);
   r.xq = routed_scaled(s) ? c.take<uint8_t>(xq_bytes(s)) : nullptr;
+  r.part = s.routed_format == K3MOE_FMT_RVQ3 ? c.take<float>(rvq_part_floats(s)) : nullptr;
   if (bytes) *bytes = c.off;
   return r;
 }
@@ -461,7 +473,7 @@ k3moe_status k3moe_expert_gateup(const k3moe_shape* shape, const k3moe_expert_ba
   carve_gateup(s, nullptr, &need);
   K3_CHECK(check_ws(workspace, workspace_bytes, need));
   const ExpertWs ws = carve_gateup(s, workspace, nullptr);
-  return hip_status(launch_expert_gateup(s, *bank, x, offsets, sorted_pair, h, ws.xq,
+  return hip_status(launch_expert_gateup(s, *bank, x, offsets, sorted_pair, h, ws,
                                          static_cast<hipStream_t>(stream)),
                     "k3moe_expert_gateup launch");
 }
@@ -471,6 +483,9 @@ k3moe_status k3moe_expert_down(const k3moe_shape* shape, const k3moe_expert_bank
   K3_CHECK(check_shape(shape));
   const k3moe_shape& s = *shape;
   K3_CHECK(check_routed_bank(s, bank));
+  if (bank->format == K3MOE_FMT_RVQ3)
+    return fail(K3MOE_EUNSUPPORTED,
+                "the RVQ3 down product needs a workspace: use k3moe_expert_ffn");
   if (s.T == 0) return ok();
   K3_CHECK(need_ptr(h, "h"));
   K3_CHECK(need_ptr(offsets, "offsets"));

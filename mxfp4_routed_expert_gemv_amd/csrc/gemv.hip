@@ -819,9 +819,12 @@ void down_launch(const k3moe_shape& s, const k3moe_expert_bank& bank, const floa
 
 hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& bank,
                                 const void* x, const int32_t* offsets,
-                                const int32_t* sorted_pair, float* h, uint8_t* xq,
+                                const int32_t* sorted_pair, float* h, const ExpertWs& ws,
                                 hipStream_t st) {
-  if (routed_scaled(s)) return launch_gateup_scaled(s, bank, x, offsets, sorted_pair, h, xq, st);
+  if (bank.format == K3MOE_FMT_RVQ3)
+    return launch_gateup_rvq(s, bank, x, offsets, sorted_pair, h, ws.part, st);
+  if (routed_scaled(s))
+    return launch_gateup_scaled(s, bank, x, offsets, sorted_pair, h, ws.xq, st);
   // One token: its row is staged in LDS (up to 32 KB).  Items loop over their
   // expert's tokens one at a time with the weight rows held in registers.
   const bool f32 = s.x_dtype == K3MOE_F32;
@@ -860,8 +863,9 @@ hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& ban
 hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                              const int32_t* offsets, const int32_t* sorted_pair, float* y,
                              const ExpertWs& ws, hipStream_t st) {
-  hipError_t err = launch_expert_gateup(s, bank, x, offsets, sorted_pair, ws.h, ws.xq, st);
+  hipError_t err = launch_expert_gateup(s, bank, x, offsets, sorted_pair, ws.h, ws, st);
   if (err != hipSuccess) return err;
+  if (bank.format == K3MOE_FMT_RVQ3) return launch_down_rvq(s, bank, ws.h, offsets, y, ws.part, st);
   return launch_expert_down(s, bank, ws.h, offsets, y, st);
 }
 

@@ -19,7 +19,9 @@ inline bool use_mfma(const k3moe_shape& s) { return s.T >= kMfmaMinT && mfma_sha
 // token count when the shape allows it (one token included: the instruction
 // takes the stored E2M1 bytes as they are, which leaves the vector ALU free),
 // so a token's routed outputs do not depend on the batch size at all there.
-inline bool routed_scaled(const k3moe_shape& s) { return mfma_shape_ok(s); }
+inline bool routed_scaled(const k3moe_shape& s) {
+  return mfma_shape_ok(s) && s.routed_format == K3MOE_FMT_MXFP4;
+}
 // Tokens per chunk of the large-batch permute (one bit per token in LDS masks).
 int permute_chunk_tokens(int k);
 
@@ -49,7 +51,10 @@ struct PermuteWs {
 struct ExpertWs {
   float* h;           // [P][f] 32-bit words (GEMV class: fp32 h; MFMA class: h in passes)
   uint8_t* xq;        // MFMA class: x in E4M3 passes, xq_bytes(s); else nullptr
+  float* part;        // RVQ3 experts: slice partial sums, rvq_part_floats(s); else nullptr
 };
+// Floats of the RVQ3 experts' slice partial sums (the larger of gate/up and down).
+size_t rvq_part_floats(const k3moe_shape& s);
 // Bytes of the quantised activations of the MFMA class (0 in the GEMV class).
 size_t xq_bytes(const k3moe_shape& s);
 ExpertWs carve_gateup(const k3moe_shape& s, void* ws, size_t* bytes);
@@ -120,8 +125,14 @@ hipError_t launch_permute(const k3moe_shape& s, const int32_t* idx, int32_t* cou
                           int32_t* diag, const PermuteWs& ws, hipStream_t st);
 hipError_t launch_expert_gateup(const k3moe_shape& s, const k3moe_expert_bank& bank,
                                 const void* x, const int32_t* offsets,
-                                const int32_t* sorted_pair, float* h, uint8_t* xq,
+                                const int32_t* sorted_pair, float* h, const ExpertWs& ws,
                                 hipStream_t st);
+// RVQ3 experts: table-based gate/up (+ SiLU-GLU, h fp32) and down.
+hipError_t launch_gateup_rvq(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
+                             const int32_t* offsets, const int32_t* sorted_pair, float* h,
+                             float* part, hipStream_t st);
+hipError_t launch_down_rvq(const k3moe_shape& s, const k3moe_expert_bank& b, const float* h,
+                           const int32_t* offsets, float* y, float* part, hipStream_t st);
 hipError_t launch_expert_down(const k3moe_shape& s, const k3moe_expert_bank& bank, const float* h,
                               const int32_t* offsets, float* y, hipStream_t st);
 // Scaled-MXFP4 matrix-core path (MFMA class): x quantisation + gate/up, down.

@@ -3,7 +3,7 @@ allocates outputs and workspaces with torch, and calls the library.  Every
 computation happens in libk3moe's kernels; this file only marshals."""
 import torch
 
-from . import (BF16, DIAG_COUNT, F32, FMT_BF16, FMT_MXFP4, OP_EXPERT_FFN, OP_EXPERT_GATEUP,
+from . import (BF16, DIAG_COUNT, F32, FMT_BF16, FMT_MXFP4, FMT_RVQ3, OP_EXPERT_FFN, OP_EXPERT_GATEUP,
                OP_LAYER, OP_PERMUTE, OP_ROUTE, OP_SHARED_FFN, ACTS, ROUTERS, k3moe_combine,
                k3moe_expert_down,
                k3moe_expert_ffn, k3moe_expert_gateup, k3moe_layer, k3moe_path_class,
@@ -14,7 +14,9 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
 class MoELayer:
     """One routed MoE FFN layer.  routed: dict of uint8 tensors w13 [E][2f][d/2],
-    w13_scale [E][2f][d/32], w2 [E][d][f/2], w2_scale [E][d][f/32]; shared:
+    w13_scale [E][2f][d/32], w2 [E][d][f/2], w2_scale [E][d][f/32] (MXFP4), or
+    w13 [E][3][d/128][2f][16], w2 [E][3][f/128][d][16] uint8 indices with fp32
+    codebooks w13_cb, w2_cb [E][3][256][8] (RVQ3); shared:
     dict of bf16 tensors w13 [S][2fs][d], w2 [S][d][fs] (or empty); router:
     "softmax", "sigmoid" or "sigmoid_norm", with router_bias an fp32 [E]
     tensor (or None) for the sigmoid routers; act: "exact" or "mxfp4" (the
@@ -26,8 +28,14 @@ class MoELayer:
         self.w_router = w_router
         self.routed = routed
         self.shared = shared
-        self.E, two_f, half_d = routed["w13"].shape
-        self.f, self.d = two_f // 2, half_d * 2
+        if "w13_cb" in routed:     # RVQ3: [E][3][d/128][2f][16]
+            self.fmt = FMT_RVQ3
+            self.E, _, nsl, two_f, _ = routed["w13"].shape
+            self.f, self.d = two_f // 2, nsl * 128
+        else:
+            self.fmt = FMT_MXFP4
+            self.E, two_f, half_d = routed["w13"].shape
+            self.f, self.d = two_f // 2, half_d * 2
         self.k = k
         self.n_shared = shared["w13"].shape[0] if shared else 0
         self.f_shared = shared["w13"].shape[1] // 2 if shared else 0
@@ -35,8 +43,12 @@ class MoELayer:
         self.router = ROUTERS[router]
         self.router_bias = router_bias
         self.act = ACTS[act]
-        self.routed_bank = make_bank(FMT_MXFP4, self.E, self.d, self.f, routed["w13"],
-                                     routed["w13_scale"], routed["w2"], routed["w2_scale"])
+        if self.fmt == FMT_RVQ3:
+            self.routed_bank = make_bank(FMT_RVQ3, self.E, self.d, self.f, routed["w13"],
+                                         routed["w13_cb"], routed["w2"], routed["w2_cb"])
+        else:
+            self.routed_bank = make_bank(FMT_MXFP4, self.E, self.d, self.f, routed["w13"],
+                                         routed["w13_scale"], routed["w2"], routed["w2_scale"])
         self.shared_bank = make_bank(FMT_BF16, self.n_shared, self.d, self.f_shared,
                                      shared.get("w13"), None, shared.get("w2"), None)
         self.weights = make_weights(w_router, self.routed_bank, self.shared_bank, router_bias)
@@ -45,7 +57,7 @@ class MoELayer:
     def shape(self, T: int, x_dtype=torch.bfloat16, out_dtype=None):
         out_dtype = self.out_dtype if out_dtype is None else out_dtype
         return make_shape(T, self.d, self.f, self.E, self.k, self.n_shared, self.f_shared,
-                          _DT[x_dtype], _DT[out_dtype], self.router, self.act)
+                          _DT[x_dtype], _DT[out_dtype], self.router, self.act, self.fmt)
 
     def workspace(self, shape, op):
         n = k3moe_workspace_bytes(shape, op)

@@ -192,6 +192,29 @@ def test_noalloc_layer_validation():
     assert call(big_shape(T=0)) == 0
 
 
+def test_rvq_validation():
+    """RVQ3 experts: the shape names the routed format, which the bank must
+    match; d and f multiples of 128; exact activations only; the down half
+    alone is refused (its slice partial sums need k3moe_expert_ffn's
+    workspace); the expert workspace holds the partial sums."""
+    rvq = k3.make_bank(k3.FMT_RVQ3, 896, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
+    mx = k3.make_bank(k3.FMT_MXFP4, 896, 7168, 2048, FAKE, FAKE, FAKE, FAKE)
+    s_rvq = big_shape(routed_format=k3.FMT_RVQ3)
+
+    def ffn(shape, bank):
+        return k3.lib.k3moe_expert_ffn(ctypes.byref(shape), ctypes.byref(bank), FAKE, FAKE, FAKE,
+                                       FAKE, FAKE * 256, 1 << 40, None)
+    assert ffn(big_shape(), rvq) == EINVAL            # bank RVQ3, shape MXFP4
+    assert ffn(s_rvq, mx) == EINVAL
+    assert ffn(big_shape(routed_format=7), rvq) == EUNSUPPORTED
+    assert ffn(big_shape(routed_format=k3.FMT_RVQ3, d=7168 + 64), rvq) == ESHAPE
+    assert ffn(big_shape(routed_format=k3.FMT_RVQ3, act=k3.ACT_MXFP4), rvq) == EUNSUPPORTED
+    assert k3.lib.k3moe_expert_down(ctypes.byref(s_rvq), ctypes.byref(rvq), FAKE, FAKE, FAKE,
+                                    None) == EUNSUPPORTED
+    # h (16 pairs x f fp32) and 16 pairs x 2f rows x d/128 slice sums of 4 bytes
+    assert k3.k3moe_workspace_bytes(s_rvq, k3.OP_EXPERT_FFN) >= 16 * 2048 * 4 + 16 * 4096 * 56 * 4
+
+
 def test_permute_and_combine_validation():
     s = big_shape(T=4)
     assert k3.lib.k3moe_permute(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, None, FAKE * 256,
