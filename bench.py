@@ -15,7 +15,10 @@ and the two prefill batches again with the quantised-activation mode
 approximation of the layer, reported beside the exact one, never in its place;
 and the decode batches with the routed experts in the pages' second format,
 RVQ3 (three 256-entry codebooks per 8-weight vector, 3.00 bits per weight),
-multiplied through per-token partial-dot tables.
+multiplied through per-token partial-dot tables; and decode at batch 1 with
+the routed experts in pinned host memory, taken through an HBM cache of 128
+expert slots (misses copied over PCIe on a second stream while the shared
+experts run), once on uniform routing and once on Zipf(1.1)-skewed routing.
 Decode steps each take fresh tokens, so every step routes to another expert
 set and the routed weights stream from HBM, not from a cache warmed by the
 previous step; prefill batches touch every expert at every step.
@@ -49,10 +52,13 @@ SPIN_CYCLES = 20_000_000           # ~10 ms of GPU spin ahead of a timed run of 
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (MXFP4 bytes) at batch 1/64/4096"
 WORKLOADS = ["decode_b1", "decode_b64", "prefill_4096", "prefill_16384_zipf",
              "prefill_4096_mxfp4act", "prefill_16384_zipf_mxfp4act", "decode_b1_rvq3",
-             "decode_b64_rvq3"]
+             "decode_b64_rvq3", "decode_b1_hostcache"]
 QACT = "_mxfp4act"   # suffix: the routed experts' activations quantised to MXFP4
 RVQ = "_rvq3"        # suffix: the routed experts in the RVQ3 format (3.00 bits per weight)
 RVQ_CODEBOOK_BYTES = 3 * 256 * 8 * 4   # per expert matrix
+HOST = "_hostcache"  # suffix: routed experts in pinned host memory behind an HBM expert cache
+CACHE_SLOTS = 128
+PCIE_PEAK_GBS = 64.0               # PCIe 5.0 x16, one direction (the host link's published rate)
 KERNEL_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "mxscale.hip")
 
 
@@ -188,6 +194,125 @@ def cpu_baseline_batch(cfg, budget_s: float, act: str = "exact"):
 
 
 # --------------------------------------------------------------- GPU timing
+def run_cache_workload(name, args, weights):
+    """Decode at batch 1 through the expert cache: the routed bank in pinned
+    host memory, CACHE_SLOTS expert slots in HBM.  A step is one
+    k3moe_cache_layer call on a fresh token (route, ids to the host, misses
+    copied on the copy stream while the shared experts run, routed experts on
+    the slots, combine); its outputs are the resident layer's bits."""
+    import torch
+
+    import gen
+    import gen.device
+    import mxfp4_routed_expert_gemv_amd as k3
+    from mxfp4_routed_expert_gemv_amd.layer import MoELayer
+
+    cfg = gen.get(name[:-len(HOST)])
+    K = args.steps if args.steps is not None else 50
+    W = args.warmup if args.warmup is not None else 5
+    log(f"workload {name}: T={cfg.T}, {CACHE_SLOTS} slots, {K} steps after {W}")
+    if "host_bank" not in weights.extra:
+        log("  pinning a host copy of the routed bank")
+        host = {}
+        for n, t in weights.routed.items():
+            host[n] = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+            host[n].copy_(t)
+        weights.extra["host_bank"] = host
+    host = weights.extra["host_bank"]
+    per_expert = sum(t[0].numel() for t in host.values())
+    slot = {n: torch.empty((CACHE_SLOTS,) + tuple(t.shape[1:]), dtype=t.dtype, device="cuda")
+            for n, t in host.items()}
+    # the plain host-to-device rate of this link: one 1 GiB pinned copy
+    probe = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    src = host["w13"].view(-1)[:1 << 30]
+    probe.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    probe.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    pcie_gbs = (1 << 30) / (time.perf_counter() - t0) / 1e9
+    del probe
+    log(f"  pinned host-to-device copy: {pcie_gbs:.1f} GB/s")
+    copy_stream = torch.cuda.Stream()
+    runs = {}
+    for routing in ("uniform", "zipf1.1"):
+        rc = cfg if routing == "uniform" else gen.get("prefill_16384_zipf").with_tokens(1)
+        w_router = (weights.w_router if routing == "uniform"
+                    else gen.device._to_dev_bf16(gen.router(rc), "cuda"))
+        layer = MoELayer(w_router, weights.routed, weights.shared, cfg.k,
+                         out_dtype=torch.bfloat16)
+        hb = k3.make_bank(k3.FMT_MXFP4, cfg.E, cfg.d, cfg.f, host["w13"], host["w13_scale"],
+                          host["w2"], host["w2_scale"])
+        db = k3.make_bank(k3.FMT_MXFP4, CACHE_SLOTS, cfg.d, cfg.f, slot["w13"],
+                          slot["w13_scale"], slot["w2"], slot["w2_scale"])
+        cache = k3.ExpertCache(layer.shape(1), hb, db)
+        xs = gen.device.activations(rc.with_tokens(K + W))
+        shape = layer.shape(1, xs.dtype)
+        ws = torch.empty(cache.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+        out = torch.empty((1, cfg.d), dtype=torch.bfloat16, device="cuda")
+        for i in range(W):
+            cache.layer(shape, layer.weights, xs[i:i + 1], out, workspace=ws,
+                        copy_stream=copy_stream)
+        torch.cuda.synchronize()
+        st0 = cache.stats()
+        t0 = time.perf_counter()
+        for i in range(W, W + K):
+            cache.layer(shape, layer.weights, xs[i:i + 1], out, workspace=ws,
+                        copy_stream=copy_stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st1 = cache.stats()
+        d = {n: st1[n] - st0[n] for n in st1}
+        # the resident layer on the same tokens, for the cost of the cache
+        t0 = time.perf_counter()
+        for i in range(W, W + K):
+            layer(xs[i:i + 1], out=out)
+        torch.cuda.synchronize()
+        resident = (time.perf_counter() - t0) / K
+        runs[routing] = {
+            "tokens_per_s": K / wall, "ms_per_step": wall / K * 1e3,
+            "hit_rate": d["hits"] / max(d["lookups"], 1),
+            "misses_per_step": d["misses"] / K, "evictions_per_step": d["evictions"] / K,
+            "h2d_bytes_per_step": d["bytes_copied"] / K,
+            "h2d_gbs": d["bytes_copied"] / wall / 1e9,
+            "resident_layer_ms_per_step_wall": resident * 1e3,
+        }
+        log(f"  {routing}: {wall / K * 1e3:.2f} ms/step, hit rate "
+            f"{runs[routing]['hit_rate']:.3f}, {runs[routing]['h2d_gbs']:.1f} GB/s over PCIe "
+            f"(resident layer {resident * 1e3:.3f} ms/step)")
+        cache.close()
+        del xs, ws
+    u = runs["uniform"]
+    result = {
+        "metric": METRIC,
+        "value": u["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": u["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "tokens_per_step": cfg.T, "d": cfg.d, "f": cfg.f,
+                   "experts": cfg.E, "top_k": cfg.k, "shared_experts": cfg.n_shared,
+                   "weights": "routed MXFP4 in pinned host memory, shared and router bf16 in HBM",
+                   "cache_slots": CACHE_SLOTS, "expert_bytes": per_expert,
+                   "parallelism": "single GPU"},
+        # the step is bound by the expert copies over the host link, not by a kernel
+        "roofline": {"bound": "pcie", "achieved": u["h2d_gbs"], "peak": PCIE_PEAK_GBS,
+                     "unit": "GB/s", "frac": u["h2d_gbs"] / PCIE_PEAK_GBS, "traffic": None,
+                     "kernel": "hipMemcpyAsync host-to-device (expert misses)",
+                     "measured_copy_gbs": pcie_gbs},
+        "routing": runs,
+    }
+    del slot
+    torch.cuda.empty_cache()
+    return result
+
+
 def run_workload(name, args, weights):
     import torch
 
@@ -415,7 +540,9 @@ def main():
     weights = gen.device.build(gen.get("decode_b1"), routed_on_device=True)
     torch.cuda.synchronize()
     log("weights resident")
-    results = {n: run_workload(n, args, weights) for n in names}
+    results = {n: (run_cache_workload if n.endswith(HOST) else run_workload)(n, args, weights)
+               for n in names}
+    weights.extra.pop("host_bank", None)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -426,6 +553,14 @@ def main():
         log(f"calibration copy of {args.calib_copy_mib} MiB done")
     if not args.no_cpu_baseline:
         for n in names:
+            if n.endswith(HOST):
+                # the cache changes where the weights live, not what is computed:
+                # the oracle's decode is the same
+                base = n[:-len(HOST)]
+                results[n]["cpu_baseline"] = (results[base]["cpu_baseline"] if base in results
+                                              else cpu_baseline_one_token(gen.get(base),
+                                                                          args.cpu_seconds))
+                continue
             log(f"timing the CPU oracle on {n}")
             qact, rvq = n.endswith(QACT), n.endswith(RVQ)
             cfg = gen.get(n[:-len(QACT)] if qact else n[:-len(RVQ)] if rvq else n)

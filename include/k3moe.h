@@ -366,6 +366,75 @@ k3moe_status k3moe_layer(const k3moe_shape* shape, const k3moe_layer_weights* we
 k3moe_status k3moe_layer_noalloc(const k3moe_shape* shape, const k3moe_layer_weights* weights,
                                  const void* x, void* out, int32_t* diag, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Host-resident routed experts streamed into an HBM expert cache.  Passage:
+ * the pages' engines keep the routed experts out of fast memory and the hot
+ * ones in an LRU cache whose size is a dial with the same outputs at every
+ * budget (kimi-k3-in-c review page, "at a glance" list and memory ladder;
+ * explainer page, "le cache LRU"); WASTE overlaps expert reads with compute
+ * and prefetches with a router run one layer early (WASTE article page,
+ * section "속도는 어디서 나왔나").  Here the experts sit in pinned host
+ * memory, the cache is a bank of `slots` experts in HBM (caller-owned, MXFP4
+ * layout with n_experts = slots), and misses travel over PCIe on a copy
+ * stream while the shared experts run.  Outputs are the same bits as
+ * k3moe_layer's on a resident bank, at every cache size.
+ * The cache object is host state created by the library (the only host
+ * allocation it makes); one call at a time uses a cache (calls on one cache
+ * from several threads are serialised).
+ * ------------------------------------------------------------------------- */
+typedef struct k3moe_expert_cache k3moe_expert_cache;
+typedef struct k3moe_cache_stats {
+  int64_t lookups;        /* one per distinct expert of a batch (prefetches are not lookups) */
+  int64_t hits;           /* lookups found resident */
+  int64_t misses;         /* lookups copied in */
+  int64_t prefetched;     /* experts copied in by k3moe_cache_prefetch */
+  int64_t prefetch_hits;  /* hits on an expert a prefetch brought in */
+  int64_t evictions;      /* resident experts replaced */
+  int64_t bytes_copied;   /* host-to-device bytes (including planned-only copies) */
+} k3moe_cache_stats;
+
+/* Creates a cache for `shape` (T ignored; MXFP4 routed experts, exact
+ * activations) over host_bank (HOST pointers to pinned memory, n_experts = E,
+ * caller-owned) and slot_bank (DEVICE pointers, n_experts = slots with
+ * k <= slots <= 1024, caller-owned; its contents are the cache's).  No GPU
+ * work.  Errors: EINVAL, ESHAPE, EALIGN, EUNSUPPORTED (not MXFP4). */
+k3moe_status k3moe_cache_create(const k3moe_shape* shape, const k3moe_expert_bank* host_bank,
+                                const k3moe_expert_bank* slot_bank, k3moe_expert_cache** cache);
+void k3moe_cache_destroy(k3moe_expert_cache* cache);
+/* Workspace of k3moe_cache_layer for `shape` and `slots` (0 if invalid). */
+size_t k3moe_cache_workspace_bytes(const k3moe_shape* shape, int32_t slots);
+/* The whole layer with the routed experts taken through the cache: routes on
+ * `stream`, synchronises `stream` once to read the expert ids, makes every
+ * distinct expert resident (hits refresh their slot; misses replace the
+ * least recently used slot this batch does not need, copied on copy_stream,
+ * or on `stream` when copy_stream is NULL), runs the shared experts while
+ * the copies fly, then the routed experts on slot ids and the combine.
+ * A slot is refilled only after the kernels of the previous layer call and
+ * the copies enqueued before have finished with it, whatever the streams
+ * (events; the host also waits for the previous call's kernels before it
+ * plans).  weights->routed is ignored (the cache's banks serve instead).
+ * Errors: those
+ * of k3moe_layer; K3MOE_ESHAPE when the batch routes to more distinct experts
+ * than there are slots (the route kernels have run then, nothing else). */
+k3moe_status k3moe_cache_layer(k3moe_expert_cache* cache, const k3moe_shape* shape,
+                               const k3moe_layer_weights* weights, const void* x, void* out,
+                               int32_t* diag, void* workspace, size_t workspace_bytes,
+                               void* stream, void* copy_stream);
+/* Brings the experts `ids` (HOST array) in ahead of use, copies on
+ * copy_stream: the lookahead of the pages (the caller predicts, for example
+ * with a router run early; the routing itself still decides).  The copies
+ * wait on the GPU for the last layer call's kernels; the host does not wait.
+ * Stops early, without error, when every slot is taken by this prefetch. */
+k3moe_status k3moe_cache_prefetch(k3moe_expert_cache* cache, const int32_t* ids, int32_t n,
+                                  void* copy_stream);
+/* Host-only planning, no copies and no GPU work: makes the distinct experts
+ * `ids` resident as one batch would and writes their slots (for tests of the
+ * replacement policy).  Errors: EINVAL, ESHAPE (more ids than slots). */
+k3moe_status k3moe_cache_plan(k3moe_expert_cache* cache, const int32_t* ids, int32_t n,
+                              int32_t* slot_of);
+/* Counters since creation. */
+k3moe_status k3moe_cache_stats_get(const k3moe_expert_cache* cache, k3moe_cache_stats* stats);
+
 /* Static description of a status code. */
 const char* k3moe_status_str(k3moe_status status);
 /* Detail of the last non-OK status returned on the calling thread. */

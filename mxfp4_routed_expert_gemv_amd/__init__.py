@@ -36,7 +36,9 @@ STATUS = {0: "K3MOE_OK", 1: "K3MOE_EINVAL", 2: "K3MOE_ESHAPE", 3: "K3MOE_EALIGN"
 EXPORTS = ["k3moe_workspace_bytes", "k3moe_mxfp4_bytes", "k3moe_path_class", "k3moe_route",
            "k3moe_permute", "k3moe_expert_ffn", "k3moe_expert_gateup", "k3moe_expert_down",
            "k3moe_shared_ffn", "k3moe_combine", "k3moe_layer", "k3moe_layer_noalloc",
-           "k3moe_status_str", "k3moe_last_error"]
+           "k3moe_status_str", "k3moe_last_error", "k3moe_cache_create", "k3moe_cache_destroy",
+           "k3moe_cache_workspace_bytes", "k3moe_cache_layer", "k3moe_cache_prefetch",
+           "k3moe_cache_plan", "k3moe_cache_stats_get"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -58,6 +60,11 @@ class ExpertBank(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("routed", ExpertBank), ("shared", ExpertBank),
                 ("router_bias", ctypes.c_void_p)]
+
+
+class CacheStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("lookups", "hits", "misses", "prefetched",
+                                              "prefetch_hits", "evictions", "bytes_copied")]
 
 
 class K3moeError(RuntimeError):
@@ -101,6 +108,21 @@ def _load():
     lib.k3moe_layer.argtypes = [SP, ctypes.POINTER(LayerWeights), P, P, P, P, S, P]
     lib.k3moe_layer_noalloc.restype = ctypes.c_int
     lib.k3moe_layer_noalloc.argtypes = [SP, ctypes.POINTER(LayerWeights), P, P, P, P]
+    BP = ctypes.POINTER(ExpertBank)
+    lib.k3moe_cache_create.restype = ctypes.c_int
+    lib.k3moe_cache_create.argtypes = [SP, BP, BP, ctypes.POINTER(P)]
+    lib.k3moe_cache_destroy.restype = None
+    lib.k3moe_cache_destroy.argtypes = [P]
+    lib.k3moe_cache_workspace_bytes.restype = S
+    lib.k3moe_cache_workspace_bytes.argtypes = [SP, I32]
+    lib.k3moe_cache_layer.restype = ctypes.c_int
+    lib.k3moe_cache_layer.argtypes = [P, SP, ctypes.POINTER(LayerWeights), P, P, P, P, S, P, P]
+    lib.k3moe_cache_prefetch.restype = ctypes.c_int
+    lib.k3moe_cache_prefetch.argtypes = [P, P, I32, P]
+    lib.k3moe_cache_plan.restype = ctypes.c_int
+    lib.k3moe_cache_plan.argtypes = [P, P, I32, P]
+    lib.k3moe_cache_stats_get.restype = ctypes.c_int
+    lib.k3moe_cache_stats_get.argtypes = [P, ctypes.POINTER(CacheStats)]
     lib.k3moe_status_str.restype = ctypes.c_char_p
     lib.k3moe_status_str.argtypes = [ctypes.c_int]
     lib.k3moe_last_error.restype = ctypes.c_char_p
@@ -214,6 +236,55 @@ def k3moe_layer_noalloc(shape, weights: LayerWeights, x, out, diag=None, stream=
     workspace, no allocation)."""
     _check(lib.k3moe_layer_noalloc(ctypes.byref(shape), ctypes.byref(weights), _addr(x),
                                    _addr(out), _addr(diag), _stream(stream)))
+
+
+class ExpertCache:
+    """An HBM cache of host-resident routed experts (k3moe_cache_*): host_bank
+    holds pinned host tensors, slot_bank device tensors of `slots` experts;
+    the caller keeps both alive while the cache lives."""
+
+    def __init__(self, shape: Shape, host_bank: ExpertBank, slot_bank: ExpertBank):
+        self.handle = ctypes.c_void_p()
+        _check(lib.k3moe_cache_create(ctypes.byref(shape), ctypes.byref(host_bank),
+                                      ctypes.byref(slot_bank), ctypes.byref(self.handle)))
+        self.slots = slot_bank.n_experts
+
+    def close(self):
+        if self.handle:
+            lib.k3moe_cache_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        self.close()
+
+    def workspace_bytes(self, shape: Shape) -> int:
+        return lib.k3moe_cache_workspace_bytes(ctypes.byref(shape), self.slots)
+
+    def layer(self, shape, weights: LayerWeights, x, out, diag=None, workspace=None,
+              stream=None, copy_stream=None):
+        wp, wb = _ws(workspace)
+        cs = None if copy_stream is None else _stream(copy_stream)
+        _check(lib.k3moe_cache_layer(self.handle, ctypes.byref(shape), ctypes.byref(weights),
+                                     _addr(x), _addr(out), _addr(diag), wp, wb, _stream(stream),
+                                     cs))
+
+    def prefetch(self, ids, copy_stream=None):
+        import numpy as np
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        cs = None if copy_stream is None else _stream(copy_stream)
+        _check(lib.k3moe_cache_prefetch(self.handle, a.ctypes.data, a.size, cs))
+
+    def plan(self, ids):
+        import numpy as np
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        out = np.empty(a.size, dtype=np.int32)
+        _check(lib.k3moe_cache_plan(self.handle, a.ctypes.data, a.size, out.ctypes.data))
+        return out
+
+    def stats(self) -> dict:
+        st = CacheStats()
+        _check(lib.k3moe_cache_stats_get(self.handle, ctypes.byref(st)))
+        return {n: getattr(st, n) for n, _ in CacheStats._fields_}
 
 
 # --------------------------------------------------------- struct builders

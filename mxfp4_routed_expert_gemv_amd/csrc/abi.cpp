@@ -261,6 +261,8 @@ k3moe_status layer_validate(const k3moe_shape* shape, const k3moe_layer_weights*
 }
 
 k3moe_status hip_failure(hipError_t e, const char* what) { return hip_status(e, what); }
+k3moe_status shape_status(const k3moe_shape* shape) { return check_shape(shape); }
+k3moe_status fail_status(k3moe_status st, const char* msg) { return fail(st, "%s", msg); }
 
 k3moe_status workspace_too_small(size_t have, size_t need) {
   return fail(K3MOE_EWORKSPACE, "the call needs %zu bytes of workspace; %zu are available", need,

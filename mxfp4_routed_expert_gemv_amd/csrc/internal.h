@@ -172,6 +172,9 @@ k3moe_status layer_validate(const k3moe_shape* shape, const k3moe_layer_weights*
 k3moe_status workspace_too_small(size_t have, size_t need);
 // K3MOE_EHIP with the HIP error's text as the last error.
 k3moe_status hip_failure(hipError_t e, const char* what);
+// The shape checks of every entry point; a status with `msg` as the last error.
+k3moe_status shape_status(const k3moe_shape* shape);
+k3moe_status fail_status(k3moe_status st, const char* msg);
 k3moe_status layer_run(const k3moe_shape& s, const k3moe_layer_weights& weights, const void* x,
                        void* out, int32_t* diag, void* workspace, hipStream_t st);
 
