@@ -1164,8 +1164,10 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   // with deep rings on both operands (a wave waits for its copies in issue
   // order, so the activation ring's lead also bounds the weights').  Taller
   // ones: 96-row m-tiles, so that an expert's weights are streamed once for
-  // up to 96 of its pairs, with pair-wide weight copies too (half as many
-  // cache-line requests per stage for the same bytes).
+  // up to 96 of its pairs, with a ring of 4 one-stage weight slots: three
+  // stages of weights in flight (a skewed batch, whose hot experts' later
+  // m-tiles find their weights in the L2, gains 9% over two-stage slots;
+  // a uniform one is unchanged).
   // With MXFP4 activations a stage holds a quarter of the matrix-core work
   // of the exact passes, so the 96-row tiles take deeper rings (3 activation
   // stages, 4 weight stages) to keep more copies in flight.
@@ -1174,7 +1176,7 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   else if (q4)
     mx_gemm_scaled<6, 4, 3, 4, false, true, true><<<g, 512, 0, st>>>(
         xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k, G);
-  else K3_SC(6, 4, 2, 2, true);
+  else K3_SC(6, 4, 2, 4, false);
 #undef K3_SC
   return hipGetLastError();
 }
