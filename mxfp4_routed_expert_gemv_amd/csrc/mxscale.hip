@@ -804,7 +804,12 @@ __device__ int expert_at(const int32_t* __restrict__ offsets, int E, int j, int*
   return *s_e;
 }
 
-constexpr int kDn1Ring = 2, kGu1ScaleRing = 3;
+constexpr int kDn1Ring = 2;
+// One-token gate/up scales: a group is 16 stages (64 bytes) of each of the
+// wave's 64 rows, read 4 lanes a row (16 rows and 16 to 32 cache lines per
+// copy instruction; 16 bytes of each of 64 rows cost 64 lines per copy, which
+// made the scale stream a tenth of the kernel's time); two group slots.
+constexpr int kGu1ScaleGroup = 16, kGu1ScaleSlot = 64 * kGu1ScaleGroup * 4;
 
 // Quantises one step of the token's row (stages 2t, 2t+1: 8 blocks of 32)
 // into two stage records at rec (the layout quant_x writes) with one wave:
@@ -846,7 +851,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
     uint8_t* __restrict__ hq, int d, int f, int E) {
   constexpr int NF = 4, NP = 2, NPH = 3, UA = NP * 8 + 1, REC = UA * 16;
-  constexpr int ROWS = NF * 16, SLOT = ROWS * 128, NCI = ROWS / 8, SG = kGu1ScaleRing;
+  constexpr int ROWS = NF * 16, SLOT = ROWS * 128, NCI = ROWS / 8;
+  constexpr int GSTEPS = kGu1ScaleGroup / 2;    // steps per scale group
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int s_e;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ln = lane & 15, lg = lane >> 4;
@@ -857,8 +863,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int x_pad = (2 * d + 1023) / 1024 * 1024;
   uint8_t* s_x = lds;                                        // the bf16 row
   uint8_t* s_xq = lds + x_pad + wv * 2 * (2 * REC);          // the wave's 2 step records
-  uint8_t* s_sc = lds + x_pad + 8 * (2 * REC) + wv * SG * 1024;
-  uint8_t* s_ring = lds + x_pad + 8 * (2 * REC) + 4 * SG * 1024 + wv * D * SLOT;
+  uint8_t* s_sc = lds + x_pad + 8 * (2 * REC) + wv * 2 * kGu1ScaleSlot;
+  uint8_t* s_ring = lds + x_pad + 8 * (2 * REC) + 4 * 2 * kGu1ScaleSlot + wv * D * SLOT;
   // the token's row by LDS-DMA (1 KB per instruction, the waves in turn),
   // beside the offsets scan
   {
@@ -868,9 +874,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       dma16_raw(xs + min(u * 64 + lane, units - 1) * 16, lds_addr(s_x) + (uint32_t)(u * 1024));
   }
   const int e = expert_at(offsets, E, j, &s_e);
-  wait_vmem<0>();
-  if (e < 0) return;
-  __syncthreads();
+  if (e < 0) {   // no expert at this rank: the row's copies land before the exit
+    wait_vmem<0>();
+    return;
+  }
   // the wave's rows: 0 .. 31 gate rows F + r, 32 .. 63 the up rows; fragment
   // nf holds rows nf * 16 + [0, 16)
   const int F = nt * 128 + wv * 32;
@@ -882,18 +889,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int r = i * 8 + (lane >> 3);
     cp[i] = wq + wrow(r) * w_row + (((lane & 7) ^ step_swz(r)) << 4);
   }
-  // scales: one 16-byte unit (4 stages) per row and pair of steps, lane = row
-  const uint8_t* sp = wsc + wrow(lane) * s_row;
+  // scales: group g (stages 16 g .. 16 g + 15) into slot g % 2 as
+  // [row][64 bytes]; copy k covers rows 16 k .. 16 k + 15, lane l row
+  // 16 k + l / 4, 16-byte unit l % 4 (clamped to the row's last unit past its
+  // end: the last group of a row shorter than 64 bytes).  Group g + 1 is
+  // copied as soon as group g - 1's slot is free: with the codes of the
+  // step D - 1 after group g's first.
+  const uint8_t* sp[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sp[k] = wsc + wrow(16 * k + (lane >> 2)) * s_row;
   const uint32_t ring_l = lds_addr(s_ring), sc_l = lds_addr(s_sc);
+  const int ngroups = (nsp + GSTEPS - 1) / GSTEPS;
+  auto issue_group = [&](int g) {
+    if (g >= ngroups) return;
+    const int off = min(g * (kGu1ScaleGroup * 4) + (lane & 3) * 16, nb - 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dma16_raw(sp[k] + off, sc_l + (uint32_t)((g & 1) * kGu1ScaleSlot + k * 1024));
+  };
+  issue_group(0);
   auto issue = [&](int t) {
     if (t >= nsp) return;
-    if ((t & 1) == 0) dma16_raw(sp + t * 8, sc_l + (uint32_t)(((t >> 1) % SG) * 1024));
+    if (t % GSTEPS == D - 1) issue_group(t / GSTEPS + 1);
     const uint32_t slot = ring_l + (uint32_t)((t % D) * SLOT);
 #pragma unroll
     for (int i = 0; i < NCI; ++i) dma16_raw_nt(cp[i] + t * 128, slot + i * 1024);
   };
 #pragma unroll
   for (int t = 0; t < D - 1; ++t) issue(t);
+  // The row's copies are older than the 4 scale and (D - 1) NCI code copies
+  // issued since (the weight stream starts without waiting for the row); the
+  // barrier shares each wave's part of the row.
+  if (nsp >= D - 1) wait_vmem<4 + (D - 1) * NCI>();
+  else wait_vmem<0>();
+  __syncthreads();
   // Each wave quantises the row itself, one step ahead of use, while its
   // copies fly (spread over the stream, the quantisation costs the stream
   // less than one pass over the whole row up front).
@@ -906,18 +935,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int t = 0; t < nsp; ++t) {
     issue(t + D - 1);
     if (t + 1 < nsp) quant_x_step(s_x + (t + 1) * 512 + lane * 8, s_xq + ((t + 1) & 1) * (2 * REC), lane);
-    // copies still allowed in flight: steps t+1 .. t+D-1, NCI each, plus a
-    // scale unit for each even one of them
-    if (t + D - 1 < nsp) {
-      static_assert(D >= 2 && D <= 4, "wait counts cover rings of 2 to 4 steps");
-      if constexpr (D == 3) wait_vmem<2 * NCI + 1>();
-      else if (t & 1) wait_vmem<(D - 1) * NCI + D / 2>();
-      else wait_vmem<(D - 1) * NCI + (D - 2) / 2>();
-    } else {
-      wait_vmem<0>();
-    }
+    // copies still allowed in flight: steps t+1 .. t+D-1, NCI each (the scale
+    // copies issued with them are not counted: fewer counted copies only make
+    // the wait stricter); a scale group was copied with codes of an earlier
+    // step than its first, so that step's wait covers it
+    static_assert(D >= 2 && D <= 4 && D - 1 < GSTEPS, "rings of 2 to 4 steps");
+    if (t + D - 1 < nsp) wait_vmem<(D - 1) * NCI>();
+    else wait_vmem<0>();
     const uint8_t* slot = s_ring + (t % D) * SLOT;
-    const uint8_t* sc = s_sc + ((t >> 1) % SG) * 1024;
+    const uint8_t* sc = s_sc + ((t / GSTEPS) & 1) * kGu1ScaleSlot;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       i32x8_t bq[NF];
@@ -927,7 +953,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int rw = nf * 16 + ln;
         const uint4 c = *reinterpret_cast<const uint4*>(slot + step_block_off(rw, q, lg));
         bq[nf] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        bs[nf] = sc[rw * 16 + ((t & 1) * 2 + q) * 4 + lg];
+        bs[nf] = sc[rw * (kGu1ScaleGroup * 4) + ((t % GSTEPS) * 2 + q) * 4 + lg];
       }
       const uint8_t* arow = s_xq + (t & 1) * (2 * REC) + q * REC;
       i32x8_t a[NP];
@@ -1089,7 +1115,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 // LDS bytes of the one-token kernels (0 when the shape does not fit).
 int gateup_1tok_lds(const k3moe_shape& s, int ring) {
-  const int n = (2 * s.d + 1023) / 1024 * 1024 + 8 * 2 * 272 + 4 * kGu1ScaleRing * 1024 +
+  const int n = (2 * s.d + 1023) / 1024 * 1024 + 8 * 2 * 272 + 4 * 2 * kGu1ScaleSlot +
                 4 * ring * 64 * 128;
   return n <= 160 * 1024 - 256 ? n : 0;
 }
