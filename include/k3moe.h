@@ -192,10 +192,15 @@ uint64_t k3moe_mxfp4_bytes(int64_t rows, int64_t cols);
 
 /* Which path class a call with this shape takes (a token's output bits
  * depend on which class its batch falls in, never on anything else about the
- * batch).  The class is K3MOE_PATH_MFMA when T >= 32, x is bf16,
+ * batch; within the MFMA class, on whether T is below 512 or not, see the
+ * router).  The class is K3MOE_PATH_MFMA when T >= 32, x is bf16,
  * d % 512 == 0 and f % 512 == 0, and K3MOE_PATH_GEMV otherwise.
- *   - Router: fp64 matrix-core tiles in the MFMA class, fp64 GEMVs in the
- *     GEMV class (same bits for the chosen set either way, see k3moe_route).
+ *   - Router: fp64 GEMVs in the GEMV class; fp64 matrix-core tiles in the
+ *     MFMA class below 512 tokens; from 512 tokens bf16 matrix-core logits
+ *     with a bound, the experts that can still reach the top k re-evaluated
+ *     in fp64.  The chosen set is the same bits every way (see k3moe_route);
+ *     the weights come from fp64 logits of three arrangements, so they can
+ *     differ in the last bits across these lines.
  *   - Shared experts: bf16 matrix-core GEMMs in the MFMA class when
  *     f_shared % 128 == 0; otherwise (GEMV class, or another f_shared) GEMVs
  *     with fp32 dot products, one pass over the weights per token.
@@ -221,7 +226,9 @@ int k3moe_path_class(const k3moe_shape* shape);
  *   topk_idx [T][k] int32, each row in ascending expert id;
  *   topk_w   [T][k] fp32, aligned with topk_idx (summing to 1 per token for
  *            the softmax and renormalised sigmoid routers);
- *   logits   [T][E] fp32 (optional, NULL = not written).
+ *   logits   [T][E] fp32 (optional, NULL = not written; the fp64 logits of
+ *            every expert, which from 512 tokens in the MFMA class costs an
+ *            extra pass of the fp64 matrix-core router).
  * The chosen set equals the set an exact evaluation of the logits in fp64
  * (ascending i) picks: near-ties at the k/k+1 boundary are re-evaluated
  * exactly on the device (counted in diag[K3MOE_DIAG_RECHECKED_TOKENS]).  For

@@ -166,6 +166,7 @@ RouteWs carve_route(const k3moe_shape& s, void* ws, size_t* bytes) {
   RouteWs r;
   r.logits = c.take<double>((size_t)s.T * s.E);
   r.lbound = c.take<float>((size_t)s.T * s.E);
+  r.wnorm = use_mfma(s) ? c.take<float>((size_t)s.E) : nullptr;
   if (bytes) *bytes = c.off;
   return r;
 }

@@ -44,6 +44,7 @@ struct Carver {
 struct RouteWs {
   double* logits;   // [T][E] fp64
   float* lbound;    // [T][E] bound on |logit - exact fp64 sequential logit|
+  float* wnorm;     // [E] |w_e| (matrix-core class: the bf16 logits' bounds); else nullptr
 };
 struct PermuteWs {
   int32_t* chunk_base;  // [nchunks][E]

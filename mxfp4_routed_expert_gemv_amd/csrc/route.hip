@@ -523,6 +523,400 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
                    logits_out, diag, d, E, k, perm, rm);
 }
 
+// ------------------------------------------------- large batches: bf16 logits
+// From kBf16RouterMinT tokens the fp64 logits above cost the layer more than
+// this route does (52.6 GFLOP of fp64 matrix work at 4096 tokens: 0.97 against
+// 0.63 ms for the whole route; below 512 tokens the fp64 route is the faster
+// one).  The ids are the oracle's on both sides of the threshold; the weights
+// come from fp64 logits of two arrangements (the fp64 matrix cores below it,
+// the GEMV arrangement above), which can differ in the last bits.  The
+// selection only needs
+// fp64 values for the experts that can still reach the top k, so:
+//   1. router_bf16: every logit on the bf16 matrix cores
+//      (v_mfma_f32_16x16x32_bf16, fp32 accumulation), written as fp32;
+//   2. route_refine (one wave per token): each fp32 logit gets a bound on
+//      its distance to the oracle's value; the experts whose upper bound
+//      reaches the k-th largest lower bound (k + a few) are recomputed in
+//      fp64 with the GEMV router's arithmetic and bound, the others keep the
+//      fp32 value and its bound;
+//   3. topk_softmax as for the fp64 logits: its certificate and exact recheck
+//      make the ids the oracle's whatever the bounds' widths, and the chosen
+//      experts (all refined) give the weights.
+// The fp32 bound: products of bf16 values are exact in fp32, and every
+// addition of the matrix core's fp32 accumulation is taken to round once
+// (to nearest or directed, relative error at most 2^-23), in any internal
+// order: along any path of the sum a product meets at most d + d/32 + 8
+// additions, so |l - exact| <= (d + d/32 + 8) 2^-23 S, with
+// S = sum |x_i w_i| <= |x| |w| (Cauchy-Schwarz); the oracle's own distance to
+// the exact sum, d 2^-53 S, is added, and d 2^-125 covers products that
+// underflow fp32.
+
+// |w_e| for every expert row (fp64 sum of exact bf16 squares, rounded up to
+// fp32 with margin); one wave per row.
+__global__ __launch_bounds__(256) void router_wnorm(const uint16_t* __restrict__ wr,
+                                                    float* __restrict__ wnorm, int d, int E) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const uint16_t* row = wr + (size_t)e * d;
+  double s = 0.0;
+  for (int c = lane; c < d / 8; c += kWave) {
+    const uint4 v = ldg16(row + (size_t)c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double a = (double)bf16_lo(w[q]), b = (double)bf16_hi(w[q]);
+      s = __builtin_fma(a, a, s);
+      s = __builtin_fma(b, b, s);
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) wnorm[e] = (float)(sqrt(s) * (1.0 + 0x1p-20));
+}
+
+// Logits of 32 FA tokens x 32 FB experts per workgroup; wave (wt = wv & 1,
+// we = wv >> 1) computes tokens 16 FA wt + [0, 16 FA) x experts
+// 16 FB we + [0, 16 FB) as FA x FB fragments.  Per contraction step of 32,
+// lane (i = lane % 16,
+// g = lane / 16) loads elements 8 g .. 8 g + 7 of its fragment rows (token
+// rows for A, expert rows for B) straight from global memory (the L2), PD
+// steps ahead.  Rows past T or E are clamped (their outputs are not stored).
+constexpr int kBf16RouterMinT = 512;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void router_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ logits32,
+    int T, int d, int E) {
+  constexpr int PD = 3;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int t0 = blockIdx.x * (32 * FA) + (wv & 1) * (16 * FA);
+  const int e0 = blockIdx.y * (32 * FB) + (wv >> 1) * (16 * FB);
+  const uint16_t* ar[FA];
+  const uint16_t* br[FB];
+#pragma unroll
+  for (int f = 0; f < FA; ++f) ar[f] = x + (size_t)min(t0 + f * 16 + li, T - 1) * d + lg * 8;
+#pragma unroll
+  for (int f = 0; f < FB; ++f) br[f] = wr + (size_t)min(e0 + f * 16 + li, E - 1) * d + lg * 8;
+  f32x4_t acc[FA][FB];
+#pragma unroll
+  for (int a = 0; a < FA; ++a)
+#pragma unroll
+    for (int b = 0; b < FB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int ns = d / 32;
+  uint4 av[PD][FA], bv[PD][FB];
+  auto load = [&](int s, int slot) {
+#pragma unroll
+    for (int f = 0; f < FA; ++f) av[slot][f] = ldg16(ar[f] + (size_t)s * 32);
+#pragma unroll
+    for (int f = 0; f < FB; ++f) bv[slot][f] = ldg16(br[f] + (size_t)s * 32);
+  };
+#pragma unroll
+  for (int q = 0; q < PD; ++q) load(min(q, ns - 1), q);
+#pragma unroll 1
+  for (int s0 = 0; s0 < ns; s0 += PD) {
+#pragma unroll
+    for (int q = 0; q < PD; ++q) {
+      if (s0 + q < ns) {
+        bf16x8_t a[FA], b[FB];
+#pragma unroll
+        for (int f = 0; f < FA; ++f) a[f] = as_bf16x8(av[q][f]);
+#pragma unroll
+        for (int f = 0; f < FB; ++f) b[f] = as_bf16x8(bv[q][f]);
+        load(min(s0 + q + PD, ns - 1), q);   // past the end: a repeat, unused
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+#pragma unroll
+          for (int j = 0; j < FB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  // element r of fragment (i, j): token 16 i + 4 g + r, expert 16 j + lane % 16
+#pragma unroll
+  for (int i = 0; i < FA; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + i * 16 + lg * 4 + r;
+      if (t < T) {
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+          const int e = e0 + j * 16 + li;
+          if (e < E) logits32[(size_t)t * E + e] = acc[i][j][r];
+        }
+      }
+    }
+}
+
+// Mid-size batches: a workgroup computes 16 TA tokens x 16 EB experts, each
+// wave over a quarter of the contraction, the four partial sums added in
+// wave order (the bound above covers this order too), so that the grid fills
+// the chip (448 workgroups at 512 tokens and 896 experts).
+template <int TA, int EB>
+__global__ __launch_bounds__(256) void router_bf16_ks(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ wr,
+                                                      float* __restrict__ logits32, int T, int d,
+                                                      int E) {
+  constexpr int BT = 16 * TA, BE = 16 * EB, PD = 4;
+  __shared__ float part[4][BT][BE + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
+  const int kq = d / 4;                 // contraction slice per wave (multiple of 128)
+  const uint16_t* ar[TA];
+  const uint16_t* br[EB];
+#pragma unroll
+  for (int f = 0; f < TA; ++f) ar[f] = x + (size_t)min(t0 + f * 16 + li, T - 1) * d + wv * kq + lg * 8;
+#pragma unroll
+  for (int f = 0; f < EB; ++f) br[f] = wr + (size_t)min(e0 + f * 16 + li, E - 1) * d + wv * kq + lg * 8;
+  f32x4_t acc[TA][EB];
+#pragma unroll
+  for (int a = 0; a < TA; ++a)
+#pragma unroll
+    for (int b = 0; b < EB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int ns = kq / 32;
+  uint4 av[PD][TA], bv[PD][EB];
+  auto load = [&](int st, int slot) {
+#pragma unroll
+    for (int f = 0; f < TA; ++f) av[slot][f] = ldg16(ar[f] + (size_t)st * 32);
+#pragma unroll
+    for (int f = 0; f < EB; ++f) bv[slot][f] = ldg16(br[f] + (size_t)st * 32);
+  };
+#pragma unroll
+  for (int q = 0; q < PD; ++q) load(min(q, ns - 1), q);
+#pragma unroll 1
+  for (int s0 = 0; s0 < ns; s0 += PD) {
+#pragma unroll
+    for (int q = 0; q < PD; ++q) {
+      if (s0 + q < ns) {
+        bf16x8_t a[TA], b[EB];
+#pragma unroll
+        for (int f = 0; f < TA; ++f) a[f] = as_bf16x8(av[q][f]);
+#pragma unroll
+        for (int f = 0; f < EB; ++f) b[f] = as_bf16x8(bv[q][f]);
+        load(min(s0 + q + PD, ns - 1), q);   // past the end: a repeat, unused
+#pragma unroll
+        for (int i = 0; i < TA; ++i)
+#pragma unroll
+          for (int j = 0; j < EB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TA; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[wv][i * 16 + lg * 4 + r][j * 16 + li] = acc[i][j][r];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < (BT * BE + 255) / 256; ++u) {
+    const int o = tid + 256 * u;
+    const int tt = o / BE, ee = o % BE;
+    const int t = t0 + tt, e = e0 + ee;
+    if (tt < BT && t < T && e < E)
+      logits32[(size_t)t * E + e] =
+          ((part[0][tt][ee] + part[1][tt][ee]) + part[2][tt][ee]) + part[3][tt][ee];
+  }
+}
+
+// A token's candidates are re-evaluated two rows at a time: fp64 products
+// and sums in the GEMV router's arrangement.  (lbound holds the fp32 logits on
+// entry; the token's workgroup reads them before it writes the row.)
+__device__ __forceinline__ void refine_dot(const uint16_t* __restrict__ xr,
+                                           const uint16_t* __restrict__ w0,
+                                           const uint16_t* __restrict__ w1, int d, int lane,
+                                           double (&acc)[2], float (&aabs)[2]) {
+  constexpr int U = 8;
+  const int nc = d / 8;
+  double a4[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  float sa[2] = {0.0f, 0.0f};
+  for (int c0 = 0; c0 < nc; c0 += kWave * U) {
+    uint4 xv[U], wv0[U], wv1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = min(c0 + lane + kWave * u, nc - 1);
+      xv[u] = ldg16(xr + (size_t)c * 8);
+      wv0[u] = ldg16(w0 + (size_t)c * 8);
+      wv1[u] = ldg16(w1 + (size_t)c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = c0 + lane + kWave * u < nc;
+      const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+      const uint32_t w[2][4] = {{wv0[u].x, wv0[u].y, wv0[u].z, wv0[u].w},
+                                {wv1[u].x, wv1[u].y, wv1[u].z, wv1[u].w}};
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        double a = a4[p][u & 3];
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = bf16_lo(xw[q]), x1 = bf16_hi(xw[q]);
+          const float v0 = bf16_lo(w[p][q]), v1 = bf16_hi(w[p][q]);
+          a = __builtin_fma((double)x0, (double)v0, a);      // exact products
+          a = __builtin_fma((double)x1, (double)v1, a);
+          s = s + fabsf(x0 * v0) + fabsf(x1 * v1);
+        }
+        a4[p][u & 3] = ok ? a : a4[p][u & 3];
+        sa[p] = ok ? sa[p] + s : sa[p];
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    acc[p] = wave_sum((a4[p][0] + a4[p][1]) + (a4[p][2] + a4[p][3]));
+    aabs[p] = wave_sum(sa[p]);
+  }
+}
+
+// One workgroup of NW waves per token.  Wave 0: bounds, the k-th largest
+// lower end, the candidate list (LDS), and the non-candidates' values and
+// bounds; then every wave re-evaluates candidate pairs in fp64.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void route_refine(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ wr,
+                                                        const float* __restrict__ wnorm,
+                                                        double* __restrict__ logits,
+                                                        float* __restrict__ lbound, int T, int d,
+                                                        int E, int k, RouterMode rm) {
+  __shared__ int s_cand[1024];
+  __shared__ int s_n;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const uint16_t* xr = x + (size_t)t * d;
+  if (wv == 0) {
+    const bool sig = rm.mode != K3MOE_ROUTER_SOFTMAX;
+    const int nj = (E + kWave - 1) / kWave;
+    // |x_t|, fp64 sum of exact squares
+    double nx = 0.0;
+    for (int c = lane; c < d / 8; c += kWave) {
+      const uint4 v = ldg16(xr + (size_t)c * 8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double a = (double)bf16_lo(w[q]), b = (double)bf16_hi(w[q]);
+        nx = __builtin_fma(a, a, nx);
+        nx = __builtin_fma(b, b, nx);
+      }
+    }
+    const double xn = sqrt(wave_sum(nx)) * (1.0 + 0x1p-40);
+    const double c1 = ((double)d + d / 32 + 8.0) * 0x1p-23 + (double)d * 0x1p-53;
+    const double c2 = (double)d * 0x1p-125;
+    float l32[kMaxJ];
+    double lo[kMaxJ], hi[kMaxJ], bnd[kMaxJ];
+    int bad = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j) {
+      const int e = min(lane + kWave * j, E - 1);
+      l32[j] = lbound[(size_t)t * E + e];
+      const double wn = (double)wnorm[e];
+      const double bias = rm.bias ? (double)rm.bias[e] : 0.0;
+      bnd[j] = (c1 * xn * wn + c2) * 1.02;
+      const double l = (double)l32[j];
+      const bool ok = j < nj && lane + kWave * j < E;
+      if (ok && !(isfinite(l) && isfinite(bnd[j]) && isfinite(bias))) bad = 1;
+      if (sig) {   // the selection score's range, with the evaluation margins
+        const double m = 4.0 * kScoreEps * (1.0 + fabs(bias));
+        lo[j] = sigmoid_score(l - bnd[j]) + bias - m;
+        hi[j] = sigmoid_score(l + bnd[j]) + bias + m;
+      } else {
+        lo[j] = l - bnd[j];
+        hi[j] = l + bnd[j];
+      }
+      if (!ok) lo[j] = hi[j] = -INFINITY;
+    }
+    bad = wave_sum(bad);
+    // the k-th largest lower end: k rounds of the wave maximum, each dropping
+    // one holder's entry
+    double lk = -INFINITY;
+    {
+      double v[kMaxJ];
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) v[j] = lo[j];
+      for (int r = 0; r < k; ++r) {
+        double mv = -INFINITY;
+        int mj = -1;
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j)
+          if (v[j] > mv) { mv = v[j]; mj = j; }
+        lk = wave_max(mv);
+        const unsigned long long h = __ballot(mj >= 0 && mv == lk);
+        const int wl = h ? __ffsll((long long)h) - 1 : -1;
+        if (lane == wl) {
+#pragma unroll
+          for (int j = 0; j < kMaxJ; ++j)
+            if (j == mj) v[j] = -INFINITY;
+        }
+      }
+    }
+    // candidates: every expert whose upper end reaches lk (all of them if a
+    // value or bound is not finite), listed in (j, lane) order; the others
+    // keep the fp32 value and its bound (rounded up to fp32)
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j) {
+      const int e = lane + kWave * j;
+      const bool valid = j < nj && e < E;
+      const bool mine = valid && (bad || hi[j] >= lk);
+      const unsigned long long bal = __ballot(mine);
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (mine) s_cand[n + before] = e;
+      n += __popcll(bal);
+      if (valid && !mine) {
+        logits[(size_t)t * E + e] = (double)l32[j];
+        lbound[(size_t)t * E + e] = (float)(bnd[j] * (1.0 + 0x1p-20));
+      }
+    }
+    if (lane == 0) s_n = n;
+  }
+  __syncthreads();
+  // the candidates' fp64 values and bounds (the GEMV router's arithmetic:
+  // |acc - exact| <= (d/64 + 8) u S, |oracle - exact| <= d u S, u = 2^-53,
+  // S <= 1.01 aabs), two rows per pass, the passes shared by the waves
+  const int n = s_n;
+  for (int q = 2 * wv; q < n; q += 2 * NW) {
+    const int e0 = s_cand[q], e1 = q + 1 < n ? s_cand[q + 1] : e0;
+    double acc[2];
+    float aabs[2];
+    refine_dot(xr, wr + (size_t)e0 * d, wr + (size_t)e1 * d, d, lane, acc, aabs);
+    if (lane == 0) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int e = p ? e1 : e0;
+        logits[(size_t)t * E + e] = acc[p];
+        lbound[(size_t)t * E + e] = (float)((2.0 * d + 64.0) * 0x1p-53 * (double)aabs[p] * 1.02);
+      }
+    }
+  }
+}
+
+void launch_router_bf16(const uint16_t* x, const uint16_t* wr, const RouteWs& ws, int T, int d,
+                        int E, int k, const RouterMode& rm, hipStream_t st) {
+  router_wnorm<<<(E + 3) / 4, 256, 0, st>>>(wr, ws.wnorm, d, E);
+  // tiles by batch size, so that the grid fills the chip
+  if (T < 2048)
+    router_bf16_ks<2, 2><<<dim3((T + 31) / 32, (E + 31) / 32), 256, 0, st>>>(x, wr, ws.lbound, T,
+                                                                            d, E);
+  else
+    router_bf16<4, 4><<<dim3((T + 127) / 128, (E + 127) / 128), 256, 0, st>>>(x, wr, ws.lbound, T,
+                                                                             d, E);
+  route_refine<4><<<T, 256, 0, st>>>(x, wr, ws.wnorm, ws.logits, ws.lbound, T, d, E, k, rm);
+}
+
+// fp64 logits to the fp32 output
+__global__ __launch_bounds__(256) void logits_to_f32(const double* __restrict__ l,
+                                                     float* __restrict__ o, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) o[i] = (float)l[i];
+}
+
 // fp64 router tiles: 16 x 16 up to 64 tokens, 32 x 16 up to 256, else 32 x 32,
 // so that small batches still spread the fp64 matrix work over the CUs
 // (at 64 tokens and 896 experts: 224 workgroups instead of 56).
@@ -608,6 +1002,20 @@ hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr,
   const int T = (int)s.T;
   const bool xf32 = s.x_dtype == K3MOE_F32;
   const dim3 g1((s.E + 3) / 4);
+  if (use_mfma(s) && T >= kBf16RouterMinT) {
+    // bf16 logits, the candidates refined in fp64, the selection; the fp64
+    // logits of every expert only when the caller asks for them
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    launch_router_bf16(xb, wr, ws, T, s.d, s.E, s.k, rm, st);
+    topk_softmax<false><<<T, 64, 0, st>>>(ws.logits, ws.lbound, x, wr, idx, w, nullptr, diag, T,
+                                          s.d, s.E, s.k, perm, rm);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || !logits_out) return err;
+    launch_router_mfma(xb, wr, ws.logits, ws.lbound, T, s.d, s.E, st);
+    const int64_t n = (int64_t)T * s.E;
+    logits_to_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(ws.logits, logits_out, n);
+    return hipGetLastError();
+  }
   if (use_mfma(s))
     launch_router_mfma(static_cast<const uint16_t*>(x), wr, ws.logits, ws.lbound, T, s.d, s.E, st);
   else if (xf32)

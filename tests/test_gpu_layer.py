@@ -478,6 +478,26 @@ def test_nonfinite_logits_are_counted():
     assert to_np(diag)[1] > 0
 
 
+def test_nonfinite_logits_bf16_route():
+    """From 512 tokens the matrix-core class routes on bf16 logits: a token
+    with an infinite activation has every expert re-evaluated in fp64 (its
+    logits are not finite and are counted), and every other token keeps the
+    ids of the clean batch."""
+    require_gpu()
+    cfg = MED.with_tokens(600)
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    clean, _, _ = L.route(wl.x)
+    x = wl.x.clone()
+    x[1, 5] = float("inf")
+    diag = torch.zeros(4, dtype=torch.int32, device="cuda")
+    idx, _, _ = L.route(x, diag=diag)
+    torch.cuda.synchronize()
+    assert to_np(diag)[1] > 0
+    others = np.array([t for t in range(cfg.T) if t != 1])
+    assert np.array_equal(to_np(idx)[others], to_np(clean)[others])
+
+
 def test_device_generator_matches_host():
     """The device fill of the routed bank equals the host generator byte for
     byte (sampled experts of the full-size bank)."""

@@ -251,14 +251,17 @@ def test_hand_tie_fixture(orc):
     assert_close(to_np(r["out"]), ref["out"], "out")
 
 
-# ------------------------------------- matrix-core router (bf16, 40 tokens)
-def test_ties_mfma_router(orc):
-    """fp64 matrix-core router tiles (40 tokens, bf16 x, d = 512): ties,
-    near-ties and a zero token inside one batch of the MFMA path class."""
+# ------------------------------ matrix-core class routers (bf16, d = 512)
+@pytest.mark.parametrize("T", [40, 600])
+def test_ties_mfma_router(orc, T):
+    """The matrix-core class's two routers: the fp64 matrix-core logits
+    (40 tokens) and, from 512 tokens, bf16 matrix-core logits whose
+    candidates are refined in fp64 (600): ties, near-ties and a zero token
+    inside one batch."""
     require_gpu()
     from mxfp4_routed_expert_gemv_amd import PATH_MFMA
-    E, k, T = 32, 8, 40
-    cfg = gen.configs.LayerConfig(name="ties_mfma_T40", T=T, d=512, f=512, E=E, k=k, n_shared=2,
+    E, k = 32, 8
+    cfg = gen.configs.LayerConfig(name=f"ties_mfma_T{T}", T=T, d=512, f=512, E=E, k=k, n_shared=2,
                                   f_shared=256, x_dtype="bf16", out_dtype="f32", scale_lo=-8,
                                   scale_hi=0)
     modes = ["next_lane", "near_up", "near_down", "near_ulp", "zero"]

@@ -100,7 +100,7 @@ def _check_layer(orc, cfg, wl, router, bias, out_dtype="f32"):
 
 
 @pytest.mark.parametrize("router", ["sigmoid", "sigmoid_norm"])
-@pytest.mark.parametrize("name,T", [("tiny", 37), ("medium", 40)])
+@pytest.mark.parametrize("name,T", [("tiny", 37), ("medium", 40), ("medium", 600)])
 def test_sigmoid_router_layer(orc, router, name, T):
     require_gpu()
     if name == "tiny":
