@@ -1034,9 +1034,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       dma16_raw(hs + min(u * 64 + lane, units - 1) * 16, lds_addr(s_hq) + (uint32_t)(u * 1024));
   }
   const int e = expert_at(offsets, E, j, &s_e);
-  wait_vmem<0>();
-  if (e < 0) return;
-  __syncthreads();
+  if (e < 0) {   // no expert at this rank: the row's copies land before the exit
+    wait_vmem<0>();
+    return;
+  }
   const int o0 = c * (4 * ROWS) + wv * ROWS;   // the wave's first output row
   const size_t row0 = (size_t)e * d + o0;
   const uint8_t* cp[NCI];
@@ -1052,20 +1053,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < NCI; ++i) dma16_raw_nt(cp[i] + t * 128, slot + i * 1024);
   };
-  // scales of the wave's rows, 16-byte units (4 stages of a row) laid out
-  // [unit k][row]: the 16 rows a scale read spans then sit in 16 distinct
-  // 4-bank groups (row-major, 16 rows of nb bytes alias onto 4 groups)
+  // scales of the wave's rows (ROWS rows of nb bytes, one contiguous run),
+  // 1 KB per copy into [row][16-byte unit] with unit k of row r at position
+  // (k + r / 4) mod (nb / 16): the 16 rows a scale read spans then sit in 16
+  // distinct 4-bank groups (unrotated, rows 64 bytes apart alias onto 4)
   {
     const int ku = nb / 16, units = ROWS * ku;
     const uint8_t* sbase = wsc + row0 * s_row;
     for (int u = 0; u * 64 < units; ++u) {
-      const int P = min(u * 64 + lane, units - 1);
-      const int k = P / ROWS, rw = P - k * ROWS;
-      dma16_raw(sbase + (size_t)rw * s_row + k * 16, lds_addr(s_sc) + (uint32_t)(u * 1024));
+      const int S = min(u * 64 + lane, units - 1);
+      const int r = S / ku;
+      int k = S - r * ku - (r >> 2) % ku;
+      if (k < 0) k += ku;
+      dma16_raw(sbase + (size_t)(r * ku + k) * 16, lds_addr(s_sc) + (uint32_t)(u * 1024));
     }
   }
 #pragma unroll
   for (int t = 0; t < D - 1; ++t) issue(t);
+  // The weight stream starts before the h row is awaited: the row's (and the
+  // scales') copies are older than the first step's NCI code copies (when
+  // nsp < D - 1 fewer were issued: wait for everything); the barrier shares
+  // each wave's part of the row.
+  if (nsp >= D - 1) wait_vmem<(D - 1) * NCI>();
+  else wait_vmem<0>();
+  __syncthreads();
 
   f32x4_t acc[NF];
 #pragma unroll
@@ -1086,7 +1097,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int rw = nf * 16 + ln;
         const uint4 cc = *reinterpret_cast<const uint4*>(slot + step_block_off(rw, q, lg));
         bq[nf] = i32x8_t{(int)cc.x, (int)cc.y, (int)cc.z, (int)cc.w, 0, 0, 0, 0};
-        bs[nf] = s_sc[((st >> 2) * ROWS + rw) * 16 + (st & 3) * 4 + lg];
+        int kk = (st >> 2) + (rw >> 2) % (nb / 16);
+        if (kk >= nb / 16) kk -= nb / 16;
+        bs[nf] = s_sc[rw * nb + kk * 16 + (st & 3) * 4 + lg];
       }
       const uint8_t* arow = s_hq + st * (UA * 16);
       i32x8_t a[NP];

@@ -211,6 +211,38 @@ def test_scaled_routed_experts_any_batch(orc, d, T):
     assert_close(h_gpu, h_ref, "h (scaled form)")
 
 
+
+@pytest.mark.parametrize("d,f,E,k", [(512, 512, 32, 8), (3584, 1024, 32, 8), (512, 512, 64, 64)])
+def test_one_token_ffn_empty_ranks(d, f, E, k):
+    """The one-token routed FFN with ranks left empty by a repeated and an
+    out-of-range id (the kernels find no expert there and write nothing):
+    k3moe_expert_ffn equals gate/up then down bit for bit on the filled
+    ranks, with finite values, on two calls in a row with other experts; k up
+    to 64 (every expert of E = 64)."""
+    require_gpu()
+    import dataclasses
+    cfg = gen.configs.LayerConfig(**{**MED.__dict__, "T": 1, "d": d, "f": f, "E": E, "k": k,
+                                     "name": f"ffn1_d{d}_E{E}_k{k}"})
+    log(f"case {cfg.name}")
+    wl = gen.device.build(cfg)
+    L = k3layer(wl, "f32")
+    rng = np.random.default_rng(d + E + k)
+    for trial in range(2):
+        ids = rng.permutation(E)[:k].astype(np.int32)
+        ids[1] = ids[0]        # repeated: dropped
+        ids[k - 1] = E + 3     # out of range: dropped
+        x = gen.device.activations(dataclasses.replace(cfg, seed=300 + trial))
+        idx = torch.from_numpy(ids[None, :].copy()).to("cuda")
+        _, offsets, sp, _ = L.permute(idx)
+        y = L.expert_ffn(x, offsets, sp)
+        h = L.expert_gateup(x, offsets, sp)
+        y2 = L.expert_down(h, offsets, 1)
+        torch.cuda.synchronize()
+        n = int(to_np(offsets)[-1])
+        assert n == k - 2, n
+        assert torch.isfinite(y[:n]).all(), trial
+        assert torch.equal(y[:n], y2[:n]), trial
+
 def _e4m3_rne(v: np.ndarray):
     """OCP E4M3 code of each value rounded to nearest even (|v| <= 448), and
     the value the code stands for; written from the format's definition."""
