@@ -278,6 +278,31 @@ __device__ __forceinline__ void lane_best(const uint64_t (&key)[kMaxJ], uint32_t
     if (!((taken >> j) & 1u) && key[j] > kb) { kb = key[j]; jb = j; }
 }
 
+// Sorts one (key, id) pair per lane across the wave by the selection's order
+// (larger key first, equal keys by lower id): lane 0 ends with the first.
+// A bitonic network over the 64 lanes: for each subsequence size and
+// stride, the lower lane of a pair keeps the earlier element in an
+// ascending block and the later one in a descending block (the upper lane
+// the other); ids are distinct, so the order is total.
+__device__ __forceinline__ void wave_sort_first(uint64_t& key, int& id, int lane) {
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)key, stride, kWave);
+      const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), stride, kWave);
+      const uint64_t ok = ((uint64_t)ohi << 32) | olo;
+      const int oi = __shfl_xor(id, stride, kWave);
+      const bool other_first = ok > key || (ok == key && oi < id);
+      const bool asc = (lane & size) == 0, lower = (lane & stride) == 0;
+      if (lower == asc ? other_first : !other_first) {
+        key = ok;
+        id = oi;
+      }
+    }
+  }
+}
+
 // LDS of one token's selection (one wave).
 struct TopkLds {
   double candL[1024];
@@ -366,8 +391,56 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
   uint32_t taken = 0;
   uint64_t kb;
   int jb;
+  int k_rounds = k;
   lane_best(key, taken, kb, jb);
-  for (int r = 0; r < k; ++r) {
+  // Sample select: the k-th of the 64 lane maxima (in the selection's order)
+  // bounds the k-th key from below (the k lanes with the largest maxima hold
+  // k keys at least as large), so the chosen ones are among the keys at or
+  // above it, k of them at least and usually a few more; when at most 64,
+  // one sort across the wave orders them and the first k are the chosen ones
+  // (the order of k rounds of the wave maximum with the lowest id on ties).
+  {
+    uint64_t sk = kb;
+    int si = jb >= 0 ? lane + kWave * jb : 1024 + lane;
+    wave_sort_first(sk, si, lane);
+    const uint32_t tlo = (uint32_t)__shfl((int)(uint32_t)sk, k - 1, kWave);
+    const uint32_t thi = (uint32_t)__shfl((int)(uint32_t)(sk >> 32), k - 1, kWave);
+    const uint64_t thr = ((uint64_t)thi << 32) | tlo;
+    uint32_t cm = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j)
+      if (key[j] != 0 && key[j] >= thr) cm |= 1u << j;
+    const int nc = wave_sum((int)__popc(cm));
+    if (nc <= kWave) {
+      int n = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) {
+        const bool mine = (cm >> j) & 1u;
+        const unsigned long long bal = __ballot(mine);
+        const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
+        if (mine) {
+          candL[pos] = __longlong_as_double((long long)key[j]);
+          candId[pos] = lane + kWave * j;
+        }
+        n += __popcll(bal);
+      }
+      for (int q = lane; q < 1024; q += kWave) chosen[q] = 0;
+      wave_sync();
+      uint64_t ck = lane < nc ? (uint64_t)__double_as_longlong(candL[lane]) : 0;
+      int ci = lane < nc ? candId[lane] : 1024 + lane;
+      wave_sort_first(ck, ci, lane);
+      if (lane < k) chosen[ci] = 1;
+      wave_sync();
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j)
+        if (j < nj && lane + kWave * j < E && chosen[lane + kWave * j]) taken |= 1u << j;
+      wave_sync();
+      k_rounds = 0;
+    }
+  }
+  // Otherwise (more than 64 keys reach the bound: ties or near ties), k
+  // rounds of the wave maximum.
+  for (int r = 0; r < k_rounds; ++r) {
     const uint64_t m = wave_max_u64(kb);
     const unsigned long long tied = __ballot(jb >= 0 && kb == m);
     int wl, wj;
@@ -479,7 +552,9 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
     const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
     if (mine) {
       chosen[pos] = lane + kWave * j;
-      candL[pos] = sig ? lv[j] : key_value(key[j]);
+      // (sigmoid routing: the logit itself, read again rather than kept in
+      // registers through the selection)
+      candL[pos] = sig ? lrow[lane + kWave * j] : key_value(key[j]);
     }
     // one token: expert e = lane + 64 j has count 0/1 and offset = the
     // number of chosen experts below it (ids run j-major, then lane)
