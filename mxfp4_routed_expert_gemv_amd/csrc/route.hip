@@ -278,29 +278,28 @@ __device__ __forceinline__ void lane_best(const uint64_t (&key)[kMaxJ], uint32_t
     if (!((taken >> j) & 1u) && key[j] > kb) { kb = key[j]; jb = j; }
 }
 
-// Sorts one (key, id) pair per lane across the wave by the selection's order
-// (larger key first, equal keys by lower id): lane 0 ends with the first.
-// A bitonic network over the 64 lanes: for each subsequence size and
-// stride, the lower lane of a pair keeps the earlier element in an
-// ascending block and the later one in a descending block (the upper lane
-// the other); ids are distinct, so the order is total.
-__device__ __forceinline__ void wave_sort_first(uint64_t& key, int& id, int lane) {
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)key, stride, kWave);
-      const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), stride, kWave);
-      const uint64_t ok = ((uint64_t)ohi << 32) | olo;
-      const int oi = __shfl_xor(id, stride, kWave);
-      const bool other_first = ok > key || (ok == key && oi < id);
-      const bool asc = (lane & size) == 0, lower = (lane & stride) == 0;
-      if (lower == asc ? other_first : !other_first) {
-        key = ok;
-        id = oi;
-      }
+// The k-th largest (1 <= k <= popcount(active)) of the values v of the lanes
+// in the wave-uniform mask active, counted with multiplicity: a descent over
+// the bits from the top, keeping the lanes that agree with the answer on the
+// bits above (set) and the answer's rank among them (need); it ends as soon
+// as one lane is left.
+__device__ __forceinline__ uint64_t kth_largest_u64(uint64_t v, uint64_t active, int k) {
+  uint64_t set = active;
+  int need = k;
+  for (int b = 63; b >= 0 && __popcll(set) > 1; --b) {
+    const uint64_t ones = __ballot((v >> b) & 1u) & set;
+    const int c = __popcll(ones);
+    if (c >= need) {
+      set = ones;
+    } else {
+      need -= c;
+      set &= ~ones;
     }
   }
+  const int l = __ffsll((long long)set) - 1;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // LDS of one token's selection (one wave).
@@ -393,26 +392,25 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
   int jb;
   int k_rounds = k;
   lane_best(key, taken, kb, jb);
-  // Sample select: the k-th of the 64 lane maxima (in the selection's order)
-  // bounds the k-th key from below (the k lanes with the largest maxima hold
-  // k keys at least as large), so the chosen ones are among the keys at or
-  // above it, k of them at least and usually a few more; when at most 64,
-  // one sort across the wave orders them and the first k are the chosen ones
-  // (the order of k rounds of the wave maximum with the lowest id on ties).
+  // Sample select: the k-th of the 64 lane maxima bounds the k-th key from
+  // below (the k lanes with the largest maxima hold k keys at least as
+  // large), so the chosen ones are among the keys at or above it, k of them
+  // at least and usually a few more.  When at most 64, they are compacted one
+  // per lane in ascending id, the k-th largest of them is found exactly, and
+  // the chosen ones are those above it plus, among those equal to it, the
+  // lowest ids (the order of k rounds of the wave maximum with the lowest id
+  // on ties).
   {
-    uint64_t sk = kb;
-    int si = jb >= 0 ? lane + kWave * jb : 1024 + lane;
-    wave_sort_first(sk, si, lane);
-    const uint32_t tlo = (uint32_t)__shfl((int)(uint32_t)sk, k - 1, kWave);
-    const uint32_t thi = (uint32_t)__shfl((int)(uint32_t)(sk >> 32), k - 1, kWave);
-    const uint64_t thr = ((uint64_t)thi << 32) | tlo;
+    const uint64_t thr = kth_largest_u64(kb, __ballot(kb != 0), k);
     uint32_t cm = 0;
 #pragma unroll
     for (int j = 0; j < kMaxJ; ++j)
       if (key[j] != 0 && key[j] >= thr) cm |= 1u << j;
     const int nc = wave_sum((int)__popc(cm));
     if (nc <= kWave) {
-      int n = 0;
+      // compaction: j-major, then lane, which is ascending id
+      uint64_t ck = 0;
+      int ci = -1, n = 0;
 #pragma unroll
       for (int j = 0; j < kMaxJ; ++j) {
         const bool mine = (cm >> j) & 1u;
@@ -426,10 +424,18 @@ __device__ void topk_token(int t, int lane, TopkLds& sm, const double* __restric
       }
       for (int q = lane; q < 1024; q += kWave) chosen[q] = 0;
       wave_sync();
-      uint64_t ck = lane < nc ? (uint64_t)__double_as_longlong(candL[lane]) : 0;
-      int ci = lane < nc ? candId[lane] : 1024 + lane;
-      wave_sort_first(ck, ci, lane);
-      if (lane < k) chosen[ci] = 1;
+      if (lane < nc) {
+        ck = (uint64_t)__double_as_longlong(candL[lane]);
+        ci = candId[lane];
+      }
+      const uint64_t live = nc >= kWave ? ~0ull : (1ull << nc) - 1ull;
+      const uint64_t tk = kth_largest_u64(ck, live, k);
+      const uint64_t above = __ballot(lane < nc && ck > tk);
+      const uint64_t tie = __ballot(lane < nc && ck == tk);
+      const int room = k - __popcll(above);   // tied ones to take, lowest ids first
+      const bool pick = ((above >> lane) & 1ull) ||
+                        (((tie >> lane) & 1ull) && __popcll(tie & ((1ull << lane) - 1ull)) < room);
+      if (pick) chosen[ci] = 1;
       wave_sync();
 #pragma unroll
       for (int j = 0; j < kMaxJ; ++j)
