@@ -647,17 +647,39 @@ __global__ __launch_bounds__(256) void shared_gateup_t1(const uint16_t* __restri
 // multiply-adds over the lane's chunks in order, the fixed transposed
 // butterfly over the wave, then the experts added in order.  Requires
 // f_shared == 2048 (4 chunks of 8 per lane) and at most 2 shared experts.
+// h (16 KB, the same for every wave) is staged once per workgroup in LDS:
+// its loads go out first, then the weights', which stay in flight while h
+// is written to LDS.  With the combine, lane s < k loads slot s's weight,
+// position and routed outputs of the wave's rows beside the weights (not
+// after the sums: two dependent round trips at the end of every wave), and
+// the finishing lanes take them in slot order as combine_one does.
 constexpr int kSdRows = 2, kSdU = 4, kSdMaxS = 2;
 __global__ __launch_bounds__(256) void shared_down_t1(const uint16_t* __restrict__ w2,
                                                       const float* __restrict__ hs,
                                                       float* __restrict__ y, int d, int fs, int S,
                                                       CombineArgs comb) {
   constexpr int R = kSdRows, U = kSdU, MS = kSdMaxS;
+  constexpr int HU = MS * U * kWave * 2 / 256;   // 16-byte units of h per thread
+  static_assert(R == 2, "two rows per wave (lane groups 0 and 1 finish them)");
+  __shared__ uint4 s_h[MS * U * kWave * 2];      // [expert][chunk c][2 halves]
   const int lane = threadIdx.x & 63;
   const int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
-  if (o0 >= d) return;
+  uint4 hv[HU];
+#pragma unroll
+  for (int q = 0; q < HU; ++q) {
+    const int n = threadIdx.x + 256 * q, se = min(n / (U * kWave * 2), S - 1);
+    hv[q] = ldg16(hs + (size_t)se * fs + (size_t)(n % (U * kWave * 2)) * 4);
+  }
+  const bool live = o0 < d;
+  const int ob = live ? o0 : 0;
+  float cw = 0.0f, cy[R];
+  int cp = -1;
+  const bool comb_lane = live && comb.y_perm && lane < comb.k;
+  if (comb_lane) {
+    cw = comb.topk_w[lane];
+    cp = comb.pair_pos[lane];
+  }
   uint4 wv[MS][R][U];
-  uint4 ha[MS][U], hb[MS][U];
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
     const int sc = min(s, S - 1);
@@ -666,11 +688,16 @@ __global__ __launch_bounds__(256) void shared_down_t1(const uint16_t* __restrict
       const int c = lane + kWave * u;
 #pragma unroll
       for (int i = 0; i < R; ++i)
-        wv[s][i][u] = ldg16(w2 + ((size_t)sc * d + o0 + i) * fs + (size_t)c * 8);
-      ha[s][u] = ldg16(hs + (size_t)sc * fs + (size_t)c * 8);
-      hb[s][u] = ldg16(hs + (size_t)sc * fs + (size_t)c * 8 + 4);
+        wv[s][i][u] = ldg16(w2 + ((size_t)sc * d + ob + i) * fs + (size_t)c * 8);
     }
   }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    cy[i] = comb_lane ? comb.y_perm[(size_t)(cp >= 0 ? cp : 0) * d + ob + i] : 0.0f;
+#pragma unroll
+  for (int q = 0; q < HU; ++q) s_h[threadIdx.x + 256 * q] = hv[q];
+  __syncthreads();
+  if (!live) return;
   float v[MS * R];
 #pragma unroll
   for (int s = 0; s < MS; ++s)
@@ -679,11 +706,13 @@ __global__ __launch_bounds__(256) void shared_down_t1(const uint16_t* __restrict
       float a = 0.0f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        const int c = lane + kWave * u;
+        const uint4 ha = s_h[(s * U * kWave + c) * 2], hb = s_h[(s * U * kWave + c) * 2 + 1];
         const uint32_t ww[4] = {wv[s][i][u].x, wv[s][i][u].y, wv[s][i][u].z, wv[s][i][u].w};
-        const float hh[8] = {__uint_as_float(ha[s][u].x), __uint_as_float(ha[s][u].y),
-                             __uint_as_float(ha[s][u].z), __uint_as_float(ha[s][u].w),
-                             __uint_as_float(hb[s][u].x), __uint_as_float(hb[s][u].y),
-                             __uint_as_float(hb[s][u].z), __uint_as_float(hb[s][u].w)};
+        const float hh[8] = {__uint_as_float(ha.x), __uint_as_float(ha.y),
+                             __uint_as_float(ha.z), __uint_as_float(ha.w),
+                             __uint_as_float(hb.x), __uint_as_float(hb.y),
+                             __uint_as_float(hb.z), __uint_as_float(hb.w)};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           a = __builtin_fmaf(bf16_lo(ww[q]), hh[2 * q], a);
@@ -698,16 +727,31 @@ __global__ __launch_bounds__(256) void shared_down_t1(const uint16_t* __restrict
   float tot = v[0];
   // experts added in order: row i's total = t(s=0, i) + t(s=1, i)
   const float other = __shfl(tot, (lane + 16 * R) & 63, kWave);
-  if ((lane & 15) == 0 && g < R) {
-    const float total = S > 1 ? tot + other : tot;
-    const int o = o0 + g;
-    if (comb.y_perm) {
-      const float r = combine_one(total, comb.y_perm, comb.pair_pos, comb.topk_w, 0, comb.k, d, o);
-      if (comb.out_bf16) static_cast<uint16_t*>(comb.out)[o] = f32_to_bf16(r);
-      else static_cast<float*>(comb.out)[o] = r;
-    } else {
-      y[o] = total;
+  const float total = S > 1 ? tot + other : tot;
+  if (comb.y_perm) {
+    // the slots in order, as combine_one: skipped when the weight is 0 or
+    // the pair was dropped
+    float r[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) r[i] = total;
+    for (int s = 0; s < comb.k; ++s) {
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cw), s));
+      const int ps = __builtin_amdgcn_readlane(cp, s);
+      if (ws != 0.0f && ps >= 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          r[i] = __builtin_fmaf(ws, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cy[i]), s)),
+                                r[i]);
+      }
     }
+    if ((lane & 15) == 0 && g < R) {
+      const int o = o0 + g;
+      const float rg = g == 0 ? r[0] : r[R - 1];
+      if (comb.out_bf16) static_cast<uint16_t*>(comb.out)[o] = f32_to_bf16(rg);
+      else static_cast<float*>(comb.out)[o] = rg;
+    }
+  } else if ((lane & 15) == 0 && g < R) {
+    y[o0 + g] = total;
   }
 }
 
