@@ -746,14 +746,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // 1 .. MF live blocks (an m-tile holds 1 .. BM rows); clamped, so that
     // every item runs its nst stages and barriers
     const int nmb = max(1, min(MF, (rows + 15) >> 4));
-    static_assert(MF <= 6, "item dispatch covers up to 6 m-blocks");
+    static_assert(MF <= 8, "item dispatch covers up to 8 m-blocks");
     switch (nmb) {
       case 1: run_item(std::integral_constant<int, 1>(), nt, row0, rows); break;
       case 2: if constexpr (MF >= 2) run_item(std::integral_constant<int, 2>(), nt, row0, rows); break;
       case 3: if constexpr (MF >= 3) run_item(std::integral_constant<int, 3>(), nt, row0, rows); break;
       case 4: if constexpr (MF >= 4) run_item(std::integral_constant<int, 4>(), nt, row0, rows); break;
       case 5: if constexpr (MF >= 5) run_item(std::integral_constant<int, 5>(), nt, row0, rows); break;
-      default: if constexpr (MF >= 6) run_item(std::integral_constant<int, 6>(), nt, row0, rows); break;
+      case 6: if constexpr (MF >= 6) run_item(std::integral_constant<int, 6>(), nt, row0, rows); break;
+      case 7: if constexpr (MF >= 7) run_item(std::integral_constant<int, 7>(), nt, row0, rows); break;
+      default: if constexpr (MF >= 8) run_item(std::integral_constant<int, 8>(), nt, row0, rows); break;
     }
   }
 }
@@ -1155,6 +1157,15 @@ namespace {
 int pick_g(const k3moe_shape& s, int mf) {
   return s.act == K3MOE_ACT_MXFP4 && (double)s.T * s.k / s.E > 16.0 * mf ? 8 : 1;
 }
+// With MXFP4 activations the tall tiles are 128 rows instead of 96: the A
+// slot of a stage is the same size (rows round up to whole copies), and a
+// stage's matrix work (a quarter of the exact passes') grows by a third
+// against the same copy latency (skewed prefill gate/up 9.37 -> 8.51 ms,
+// down 5.85 -> 5.14 ms; uniform 4096-token batch 3.38 -> 3.32 and 1.95 ->
+// 1.90 ms).
+int q4_tile(const k3moe_shape& s, int mf) {
+  return s.act == K3MOE_ACT_MXFP4 && mf > 3 ? 8 : mf;
+}
 }  // namespace
 
 hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
@@ -1188,7 +1199,7 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   const uint8_t* w = static_cast<const uint8_t*>(b.w13);
   const uint8_t* ws = static_cast<const uint8_t*>(b.w13_scale);
   const dim3 g(grouped_grid());   // one workgroup per CU
-  const int mf = pick_mf(s, 6);
+  const int mf = q4_tile(s, pick_mf(s, 6));
   const int G = pick_g(s, mf);
 #define K3_SC(MF, NF, RA, RB, PB)                                                            \
   do {                                                                                        \
@@ -1208,12 +1219,13 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   // m-tiles find their weights in the L2, gains 9% over two-stage slots;
   // a uniform one is unchanged).
   // With MXFP4 activations a stage holds a quarter of the matrix-core work
-  // of the exact passes, so the 96-row tiles take deeper rings (3 activation
-  // stages, 4 weight stages) to keep more copies in flight.
+  // of the exact passes, so the tall tiles (128 rows, q4_tile) take deeper
+  // rings (3 activation stages, 4 weight stages) to keep more copies in
+  // flight.
   if (mf <= 1) K3_SC(1, 4, 4, 4, true);
   else if (mf <= 3) K3_SC(3, 4, 2, 5, false);
   else if (q4)
-    mx_gemm_scaled<6, 4, 3, 4, false, true, true><<<g, 512, 0, st>>>(
+    mx_gemm_scaled<8, 4, 3, 4, false, true, true><<<g, 512, 0, st>>>(
         xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k, G);
   else K3_SC(6, 4, 2, 4, false);
 #undef K3_SC
@@ -1242,7 +1254,7 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
     }
   }
   const dim3 g(grouped_grid());
-  const int mf = pick_mf(s, 6);
+  const int mf = q4_tile(s, pick_mf(s, 6));
   const int G = pick_g(s, mf);
 #define K3_SD(MF, NF, RA, RB, PB)                                                            \
   do {                                                                                        \
@@ -1256,7 +1268,7 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
   if (mf <= 1) K3_SD(1, 4, 4, 4, true);
   else if (mf <= 3) K3_SD(3, 4, 2, 5, false);
   else if (q4)
-    mx_gemm_scaled<6, 4, 3, 4, true, true, true><<<g, 512, 0, st>>>(
+    mx_gemm_scaled<8, 4, 3, 4, true, true, true><<<g, 512, 0, st>>>(
         hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);
   else K3_SD(6, 4, 2, 3, false);
 #undef K3_SD
