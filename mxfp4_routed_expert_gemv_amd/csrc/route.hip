@@ -869,6 +869,7 @@ __global__ __launch_bounds__(64 * NW) void route_refine(const uint16_t* __restri
                                                         int E, int k, RouterMode rm) {
   __shared__ int s_cand[1024];
   __shared__ int s_n;
+  __shared__ uint64_t s_key[kWave];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x;
   const uint16_t* xr = x + (size_t)t * d;
@@ -914,26 +915,58 @@ __global__ __launch_bounds__(64 * NW) void route_refine(const uint16_t* __restri
       if (!ok) lo[j] = hi[j] = -INFINITY;
     }
     bad = wave_sum(bad);
-    // the k-th largest lower end: k rounds of the wave maximum, each dropping
-    // one holder's entry
+    // the k-th largest lower end (with multiplicity, -inf for the lanes'
+    // empty slots, NaN as -inf): the sample select of topk_token (the k-th
+    // lane maximum bounds it from below; the entries at or above that bound,
+    // when at most 64, give it exactly by a radix descent), else k rounds of
+    // the wave maximum, each dropping one holder's entry
     double lk = -INFINITY;
     {
-      double v[kMaxJ];
+      uint64_t key[kMaxJ], kb = 0;
 #pragma unroll
-      for (int j = 0; j < kMaxJ; ++j) v[j] = lo[j];
-      for (int r = 0; r < k; ++r) {
-        double mv = -INFINITY;
-        int mj = -1;
+      for (int j = 0; j < kMaxJ; ++j) {
+        key[j] = order_key(isnan(lo[j]) ? -INFINITY : lo[j]);
+        kb = key[j] > kb ? key[j] : kb;
+      }
+      const uint64_t thr = kth_largest_u64(kb, ~0ull, k);
+      uint32_t cm = 0;
 #pragma unroll
-        for (int j = 0; j < kMaxJ; ++j)
-          if (v[j] > mv) { mv = v[j]; mj = j; }
-        lk = wave_max(mv);
-        const unsigned long long h = __ballot(mj >= 0 && mv == lk);
-        const int wl = h ? __ffsll((long long)h) - 1 : -1;
-        if (lane == wl) {
+      for (int j = 0; j < kMaxJ; ++j)
+        if (key[j] >= thr) cm |= 1u << j;
+      const int nc = wave_sum((int)__popc(cm));
+      if (nc <= kWave) {
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) {
+          const bool mine = (cm >> j) & 1u;
+          const unsigned long long bal = __ballot(mine);
+          if (mine) s_key[n + __popcll(bal & ((1ull << lane) - 1ull))] = key[j];
+          n += __popcll(bal);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint64_t ck = lane < nc ? s_key[lane] : 0;
+        const uint64_t live = nc >= kWave ? ~0ull : (1ull << nc) - 1ull;
+        lk = key_value(kth_largest_u64(ck, live, k));
+      } else {
+        double v[kMaxJ];
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) v[j] = lo[j];
+        for (int r = 0; r < k; ++r) {
+          double mv = -INFINITY;
+          int mj = -1;
 #pragma unroll
           for (int j = 0; j < kMaxJ; ++j)
-            if (j == mj) v[j] = -INFINITY;
+            if (v[j] > mv) { mv = v[j]; mj = j; }
+          lk = wave_max(mv);
+          const unsigned long long h = __ballot(mj >= 0 && mv == lk);
+          const int wl = h ? __ffsll((long long)h) - 1 : -1;
+          if (lane == wl) {
+#pragma unroll
+            for (int j = 0; j < kMaxJ; ++j)
+              if (j == mj) v[j] = -INFINITY;
+          }
         }
       }
     }
