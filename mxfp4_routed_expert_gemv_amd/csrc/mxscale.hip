@@ -279,15 +279,23 @@ __global__ __launch_bounds__(256) void quant_x4(const uint16_t* __restrict__ x,
 }
 
 // ---------------------------------------------------------- grouped GEMMs
-// Tile of item `it`.  Expert e owns items [s_mt[e] NT, s_mt[e+1] NT): its
-// m-tiles times the NT n-tiles.  Within an expert the items run in blocks of
-// G consecutive m-tiles, the n-tile slowest inside a block.  Consecutive
-// items run at the same time on the workgroups of one XCD, which then share
-// each weight tile (up to G m-tiles of the expert) and each activation tile
-// (consecutive n-tiles) through that XCD's L2.  G = 1 is m-tile-major.
-__device__ __forceinline__ void item_tile(const int* s_mt, int E, int it, int NT, int G, int& mt,
-                                          int& nt) {
-  const int e = mtile_expert(s_mt, E, it / NT);
+// Tile of item `it` and its expert e.  Expert e owns items
+// [s_mt[e] NT, s_mt[e+1] NT): its m-tiles times the NT n-tiles, so the
+// expert of m-tile it / NT is the item's.  Within an expert the items run in
+// blocks of G consecutive m-tiles, the n-tile slowest inside a block.
+// Consecutive items run at the same time on the workgroups of one XCD, which
+// then share each weight tile (up to G m-tiles of the expert) and each
+// activation tile (consecutive n-tiles) through that XCD's L2.  G = 1 is
+// m-tile-major: one search and no division beyond it / NT.
+__device__ __forceinline__ int item_tile(const int* s_mt, int E, int it, int NT, int G, int& mt,
+                                         int& nt) {
+  const int mq = it / NT;
+  const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mq));
+  if (G == 1) {
+    mt = mq;
+    nt = it - mq * NT;
+    return e;
+  }
   const int m0 = s_mt[e], me = s_mt[e + 1] - m0;
   const int li = it - m0 * NT;
   const int blk = li / (G * NT);
@@ -296,6 +304,7 @@ __device__ __forceinline__ void item_tile(const int* s_mt, int E, int it, int NT
   const int r = li - blk * G * NT;
   nt = r / gs;
   mt = m0 + g0 + (r - nt * gs);
+  return e;
 }
 
 // With pair-wide weight copies (PB), the copies a wave issues after the last
@@ -453,8 +462,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto a_setup = [&]() {
     int mt, nt_unused;
-    item_tile(s_mt, E, a_it, NT, G, mt, nt_unused);
-    const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
+    const int e = item_tile(s_mt, E, a_it, NT, G, mt, nt_unused);
     const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
     const int rows = min(BM, offsets[e + 1] - row0);
 #pragma unroll
@@ -471,8 +479,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto b_setup = [&]() {
     int mt, nt;
-    item_tile(s_mt, E, b_it, NT, G, mt, nt);
-    const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
+    const int e = item_tile(s_mt, E, b_it, NT, G, mt, nt);
     const uint8_t* wbase = wq + (size_t)e * e_rows * w_row;
 #pragma unroll
     for (int q = 0; q < NBC; ++q) {
@@ -488,8 +495,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto s_setup = [&]() {
     int mt;
-    item_tile(s_mt, E, s_it, NT, G, mt, s_nt);
-    s_e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
+    s_e = item_tile(s_mt, E, s_it, NT, G, mt, s_nt);
   };
   const uint32_t sA_lds = lds_addr(sA), sB_lds = lds_addr(sB), sS_lds = lds_addr(sS);
   // Scales of group grp (4 stages) of the scale cursor's item, every row of
@@ -555,8 +561,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (s_it < it_end) s_setup();
     // scales of the first item's first group (older than every counted copy)
     int mt, nt;
-    item_tile(s_mt, E, it_first, NT, G, mt, nt);
-    const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
+    const int e = item_tile(s_mt, E, it_first, NT, G, mt, nt);
 #pragma unroll
     for (int q = 0; q < BROWS / 256; ++q) {
       const int r0 = cq * (BROWS / 4) + q * 64;
@@ -739,8 +744,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   for (int it = it_first; it < it_end; it += it_step) {
     int mt, nt;
-    item_tile(s_mt, E, it, NT, G, mt, nt);
-    const int e = __builtin_amdgcn_readfirstlane(mtile_expert(s_mt, E, mt));
+    const int e = item_tile(s_mt, E, it, NT, G, mt, nt);
     const int row0 = offsets[e] + (mt - s_mt[e]) * BM;
     const int rows = min(BM, offsets[e + 1] - row0);
     // 1 .. MF live blocks (an m-tile holds 1 .. BM rows); clamped, so that
