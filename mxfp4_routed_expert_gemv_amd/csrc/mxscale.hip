@@ -330,15 +330,16 @@ __host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2)
   return best;
 }
 
-// One workgroup of 8 waves per CU, two per SIMD: waves 0..3 only compute,
-// waves 4..7 only copy, so a copy that stalls at issue (the memory pipeline's
-// queues are full) does not hold back the matrix-core work of its SIMD.
-//   * item = (m-tile of BM = 16 MF expert-sorted rows, n-tile of 4 * 16 NF
+// One workgroup of NC + 4 waves per CU: waves 0 .. NC-1 only compute (NC = 4
+// or 8: one or two per SIMD), waves NC .. NC+3 only copy (one per SIMD), so a
+// copy that stalls at issue (the memory pipeline's queues are full) does not
+// hold back the matrix-core work of its SIMD.
+//   * item = (m-tile of BM = 16 MF expert-sorted rows, n-tile of NC * 16 NF
 //     weight rows); compute wave w computes all BM rows against weight rows
 //     [16 NF w, 16 NF (w + 1)) of the n-tile;
 //   * each stage (128 contraction elements) of A (activations, from L2) and
 //     B (weight codes and scales, from HBM) is copied into LDS rings of RA
-//     and RB slots by LDS-DMA, copy wave 4 + q issuing quarter q of the
+//     and RB slots by LDS-DMA, copy wave NC + q issuing quarter q of the
 //     copies; the copy cursors run RA - 1 and RB - 1 stages ahead of the
 //     compute and cross item boundaries, so the weight stream does not
 //     drain between items;
@@ -353,31 +354,32 @@ __host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2)
 //     number of 256-unit copy rounds.  The 16-byte fragment reads of 16
 //     rows run at the full LDS rate when the row pitch is an odd multiple
 //     of 32 bytes (18 or 26 units), at half rate at 17 or 25 (measured);
-//   B slot: codes [64 NF rows][4 MX blocks of 16 bytes], block b of row r at
+//   B slot: codes [16 NF NC rows][4 MX blocks of 16 bytes], block b of row r at
 //     position b ^ ((r >> 1) & 3), the swizzle of 64-byte rows that reads
 //     at the full rate (with (r >> 2) & 3 it is half).  Local weight row r belongs to wave
 //     r / (16 NF), fragment (r / 16) % NF, lane r % 16;
-//   scale slot (a ring of SG): [64 NF rows][16 bytes], the scales of 4
+//   scale slot (a ring of SG): [16 NF NC rows][16 bytes], the scales of 4
 //     consecutive stages of the row (4 bytes a stage), as stored.  Copying a
 //     row's scales 4 stages at a time keeps the copy requests per stage a
 //     quarter of the rows; one 4-byte copy per row and stage halves the rate
 //     at which the weight codes stream.
 // Gate/up (DOWN = false): A = xq rows gathered by token, NP = 2; wave w owns
-//   the 8 NF features nt * 32 NF + w * 8 NF + [0, 8 NF): fragments
+//   the 8 NF features nt * 8 NF NC + w * 8 NF + [0, 8 NF): fragments
 //   0 .. NF/2 - 1 are their gate rows, NF/2 .. NF - 1 their up rows; h is
 //   written in 3 passes per 32-feature block (hq [P][f/128][25 units]).
 // Down (DOWN = true): A = hq rows, NP = 3; wave w owns the 16 NF outputs
-//   nt * 64 NF + w * 16 NF + [0, 16 NF); y fp32.
-// A wave computes only the m-blocks (16 rows) that hold rows of the tile,
-// and reads the next m-block's A fragments before issuing this one's MFMAs.
+//   nt * 16 NF NC + w * 16 NF + [0, 16 NF); y fp32.
+// A wave computes only the m-blocks (16 rows) that hold rows of the tile;
+// with one compute wave per SIMD it reads the next m-block's A fragments
+// before issuing this one's MFMAs.
 // PB (pair-wide weight copies): every other stage, each weight row's next 128
 // bytes (two stages) are copied at once, non-temporally, into a ring of
 // (RB + 2) / 2 two-stage slots laid out as the one-token stream's steps:
 // whole 128-byte lines per copy, each read once.
 // Q4: the quantised-activation mode (A in MXFP4, one pass; gate/up writes h
 // in MXFP4); otherwise A in exact E4M3 passes.
-template <int MF, int NF, int RA, int RB, bool DOWN, bool PB, bool Q4>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mx_gemm_scaled(
+template <int MF, int NF, int RA, int RB, bool DOWN, bool PB, bool Q4, int NC>
+__global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(NC / 4 + 1, NC / 4 + 1))) void mx_gemm_scaled(
     const uint8_t* __restrict__ a_src, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pair, void* __restrict__ out, int d, int f, int E,
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int A_SLOT = A_UNITS * 16;
   constexpr int NAW = A_UNITS / 256;            // A copies per wave per stage
   constexpr int WROWS = NF * 16;                // weight rows per wave
-  constexpr int BROWS = 4 * WROWS;              // weight rows per stage
+  constexpr int BROWS = NC * WROWS;             // weight rows per stage
   constexpr int FW = NF * 8;                    // gate/up: features per wave
   constexpr int B_SLOT = BROWS * 64;            // weight codes of one stage
   constexpr int S_SLOT = BROWS * 16;            // weight scales of 4 stages (16 bytes a row)
@@ -416,6 +418,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                            : (NEWER_A < NEWER_B ? NEWER_A : NEWER_B);
   constexpr int RMAX = RA > RB ? RA : RB;
   static_assert(NF == 4 || NF == 8, "4 or 8 fragments per wave");
+  static_assert(NC == 4 || NC == 8, "4 or 8 compute waves");
   static_assert(RA >= 2 && RB >= 2, "rings need two slots");
   static_assert((RA - 1) * NAW + (PB ? (RB / 2 + 1) * NBC : (RB - 1) * NBCW) + RB / 4 * SCW + SCW <= 63,
                 "memory counter range");
@@ -423,14 +426,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) uint8_t sB[PB ? RBP * B_SLOT_P : RB * B_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sS[SG * S_SLOT];
   __shared__ int s_mt[kMaxE + 1];
-  __shared__ int s_wave[8];
+  __shared__ int s_wave[NC + 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const bool copier = wv >= 4;
+  const bool copier = wv >= NC;
   const int cq = wv & 3;                      // a copy wave's quarter of each stage's copies
-  build_mtiles_n<512>(offsets, E, BM, s_mt, s_wave);
-  const int NT = DOWN ? d / BROWS : f / (4 * FW);
+  build_mtiles_n<64 * (NC + 4)>(offsets, E, BM, s_mt, s_wave);
+  const int NT = DOWN ? d / BROWS : f / (NC * FW);
   const int nst = (DOWN ? f : d) / kBK;
   const ItemRange ir0 = item_range((long)s_mt[E] * NT);
   const int it_first = (int)ir0.first, it_end = (int)ir0.end, it_step = (int)ir0.step;
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto grow = [&](int nt, int r) -> size_t {
     if (DOWN) return (size_t)nt * BROWS + r;
     const int cw = r / WROWS, nf = (r >> 4) % NF;
-    return (size_t)((nf >= NF / 2 ? f : 0) + nt * (4 * FW) + cw * FW + (nf % (NF / 2)) * 16 +
+    return (size_t)((nf >= NF / 2 ? f : 0) + nt * (NC * FW) + cw * FW + (nf % (NF / 2)) * 16 +
                     (r & 15));
   };
   auto a_setup = [&]() {
@@ -621,8 +624,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       // A fragments of m-block i: pass p = bytes [16 lg, +16) and
       // [64 + 16 lg, +16) of the pass's 128, and the scale byte of block lg
-      i32x8_t a[2][NP];
-      int as[2][NP];
+      // two compute waves per SIMD (NC = 8) cover each other's LDS reads, so
+      // an m-block's A fragments are read just before its MFMAs; with one,
+      // the next block's are read ahead
+      constexpr int NAB = NC == 8 ? 1 : 2;
+      i32x8_t a[NAB][NP];
+      int as[NAB][NP];
       auto load_a = [&](int i, i32x8_t (&av)[NP], int (&sv)[NP]) {
         const uint8_t* arow = abase + (i * 16 + ln) * (ULA * 16);
         if constexpr (Q4) {   // the lane's MX block of the row, as a weight lane
@@ -640,16 +647,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
         }
       };
-      load_a(0, a[0], as[0]);
+      if constexpr (NAB == 2) load_a(0, a[0], as[0]);
 #pragma unroll
       for (int i = 0; i < NMB; ++i) {
-        if (i + 1 < NMB) load_a(i + 1, a[(i + 1) & 1], as[(i + 1) & 1]);
+        if constexpr (NAB == 2) {
+          if (i + 1 < NMB) load_a(i + 1, a[(i + 1) & 1], as[(i + 1) & 1]);
+        } else {
+          load_a(i, a[0], as[0]);
+        }
+        const int ab = NAB == 2 ? (i & 1) : 0;
 #pragma unroll
         for (int p = 0; p < NP; ++p)
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
             acc[i][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                a[i & 1][p], bq[nf], acc[i][nf], A_FMT, 4, 0, as[i & 1][p], 0, bs[nf]);
+                a[ab][p], bq[nf], acc[i][nf], A_FMT, 4, 0, as[ab][p], 0, bs[nf]);
       }
     }
     if (DOWN) {
@@ -674,7 +686,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const size_t h_row = (size_t)(f / kBK) * (kQ4Units * 16);
 #pragma unroll
       for (int hb = 0; hb < NF / 4; ++hb) {
-        const int fb = (nt * (4 * FW) + wv * FW) / 32 + hb, hst = fb >> 2, blk = fb & 3;
+        const int fb = (nt * (NC * FW) + wv * FW) / 32 + hb, hst = fb >> 2, blk = fb & 3;
 #pragma unroll
         for (int i = 0; i < NMB; ++i)
 #pragma unroll
@@ -709,7 +721,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const size_t h_row = (size_t)(f / kBK) * (NPH * 128 + 16);
 #pragma unroll
       for (int hb = 0; hb < NF / 4; ++hb) {
-        const int fb = (nt * (4 * FW) + wv * FW) / 32 + hb, hst = fb >> 2, blk = fb & 3;
+        const int fb = (nt * (NC * FW) + wv * FW) / 32 + hb, hst = fb >> 2, blk = fb & 3;
 #pragma unroll
         for (int i = 0; i < NMB; ++i)
 #pragma unroll
@@ -1205,33 +1217,35 @@ hipError_t launch_gateup_scaled(const k3moe_shape& s, const k3moe_expert_bank& b
   const dim3 g(grouped_grid());   // one workgroup per CU
   const int mf = q4_tile(s, pick_mf(s, 6));
   const int G = pick_g(s, mf);
-#define K3_SC(MF, NF, RA, RB, PB)                                                            \
+#define K3_SC(MF, NF, RA, RB, PB, NC)                                                        \
   do {                                                                                        \
     if (q4)                                                                                   \
-      mx_gemm_scaled<MF, NF, RA, RB, false, PB, true><<<g, 512, 0, st>>>(                     \
+      mx_gemm_scaled<MF, NF, RA, RB, false, PB, true, NC><<<g, 64 * (NC + 4), 0, st>>>(       \
           xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k, G);                         \
     else                                                                                      \
-      mx_gemm_scaled<MF, NF, RA, RB, false, PB, false><<<g, 512, 0, st>>>(                    \
+      mx_gemm_scaled<MF, NF, RA, RB, false, PB, false, NC><<<g, 64 * (NC + 4), 0, st>>>(      \
           xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k, G);                         \
   } while (0)
   // Short m-tiles (weight-stream bound): pair-wide non-temporal weight copies
   // with deep rings on both operands (a wave waits for its copies in issue
   // order, so the activation ring's lead also bounds the weights').  Taller
   // ones: 96-row m-tiles, so that an expert's weights are streamed once for
-  // up to 96 of its pairs, with a ring of 4 one-stage weight slots: three
-  // stages of weights in flight (a skewed batch, whose hot experts' later
-  // m-tiles find their weights in the L2, gains 9% over two-stage slots;
-  // a uniform one is unchanged).
+  // up to 96 of its pairs.  Their gate/up takes 8 compute waves (n-tiles of
+  // 512 weight rows), so each activation stage is copied for half as many
+  // n-tiles; LDS then holds two one-stage weight slots (4.99 -> 4.85 ms on a
+  // uniform 4096-token batch, 16.0 -> 14.8 ms on the Zipf-skewed 16384-token
+  // one, against 4 compute waves with 4 weight slots; same bits).
   // With MXFP4 activations a stage holds a quarter of the matrix-core work
   // of the exact passes, so the tall tiles (128 rows, q4_tile) take deeper
   // rings (3 activation stages, 4 weight stages) to keep more copies in
-  // flight.
-  if (mf <= 1) K3_SC(1, 4, 4, 4, true);
-  else if (mf <= 3) K3_SC(3, 4, 2, 5, false);
+  // flight; 8 compute waves, which leave room for 3 weight stages only, were
+  // slower there (skewed batch 8.9 -> 11.3 ms).
+  if (mf <= 1) K3_SC(1, 4, 4, 4, true, 4);
+  else if (mf <= 3) K3_SC(3, 4, 2, 5, false, 4);
   else if (q4)
-    mx_gemm_scaled<8, 4, 3, 4, false, true, true><<<g, 512, 0, st>>>(
+    mx_gemm_scaled<8, 4, 3, 4, false, true, true, 4><<<g, 512, 0, st>>>(
         xq, w, ws, offsets, sorted_pair, h, s.d, s.f, s.E, s.k, G);
-  else K3_SC(6, 4, 2, 4, false);
+  else K3_SC(6, 4, 2, 2, false, 8);
 #undef K3_SC
   return hipGetLastError();
 }
@@ -1260,21 +1274,23 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
   const dim3 g(grouped_grid());
   const int mf = q4_tile(s, pick_mf(s, 6));
   const int G = pick_g(s, mf);
-#define K3_SD(MF, NF, RA, RB, PB)                                                            \
+#define K3_SD(MF, NF, RA, RB, PB, NC)                                                        \
   do {                                                                                        \
     if (q4)                                                                                   \
-      mx_gemm_scaled<MF, NF, RA, RB, true, PB, true><<<g, 512, 0, st>>>(                      \
+      mx_gemm_scaled<MF, NF, RA, RB, true, PB, true, NC><<<g, 64 * (NC + 4), 0, st>>>(        \
           hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);                             \
     else                                                                                      \
-      mx_gemm_scaled<MF, NF, RA, RB, true, PB, false><<<g, 512, 0, st>>>(                     \
+      mx_gemm_scaled<MF, NF, RA, RB, true, PB, false, NC><<<g, 64 * (NC + 4), 0, st>>>(       \
           hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);                             \
   } while (0)
-  if (mf <= 1) K3_SD(1, 4, 4, 4, true);
-  else if (mf <= 3) K3_SD(3, 4, 2, 5, false);
+  // The same tiles as the gate/up; the tall exact ones keep 4 compute waves
+  // (the 3-pass activation slots leave no LDS for 512-row weight stages).
+  if (mf <= 1) K3_SD(1, 4, 4, 4, true, 4);
+  else if (mf <= 3) K3_SD(3, 4, 2, 5, false, 4);
   else if (q4)
-    mx_gemm_scaled<8, 4, 3, 4, true, true, true><<<g, 512, 0, st>>>(
+    mx_gemm_scaled<8, 4, 3, 4, true, true, true, 4><<<g, 512, 0, st>>>(
         hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);
-  else K3_SD(6, 4, 2, 3, false);
+  else K3_SD(6, 4, 2, 3, false, 4);
 #undef K3_SD
   return hipGetLastError();
 }
