@@ -11,7 +11,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libk3moe.so")
 
 SOURCES = ["abi.cpp", "route.hip", "permute.hip", "gemv.hip", "mfma.hip", "mxscale.hip", "combine.hip",
-           "noalloc.hip", "rvq.hip", "cache.hip"]
+           "noalloc.hip", "rvq.hip", "cache.hip", "shared_gemm.hip"]
 
 # -ffp-contract=off: every fused multiply-add is written out, so each template
 # variant rounds identically.  -packed-fp32-ops off: packed fp32 add/mul/fma

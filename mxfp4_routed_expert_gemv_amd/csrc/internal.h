@@ -145,14 +145,19 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& ban
 // Compute units of the current device (queried once per device and cached;
 // safe to call from several threads at once).
 int cu_count();
-// Persistent grids, rounded up to a multiple of the 8 XCDs (the item split
-// of the grouped kernels gives each XCD one contiguous range): two
-// workgroups per CU (shared-expert GEMMs) or one (routed grouped GEMMs).
-int mfma_grid();
+// Persistent grid of one workgroup per CU, rounded up to a multiple of the 8
+// XCDs (the item split of the grouped kernels gives each XCD one contiguous
+// range): the routed grouped GEMMs and the shared experts' LDS-ring GEMMs.
 int grouped_grid();
 // The m-tile height (in 16-row blocks) of the routed grouped GEMMs for a batch.
 int pick_mf(const k3moe_shape& s, int max_mf);
 bool shared_mfma_ok(const k3moe_shape& s);
+// The shared experts' GEMMs with both operands staged through LDS rings
+// (shared_gemm.hip), for the matrix-core class beyond the small-batch
+// kernels; h then holds two bf16 planes (hi, lo) in the same bytes.
+bool shared_lds_ok(const k3moe_shape& s);
+hipError_t launch_shared_lds(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
+                             float* h, float* y, hipStream_t st);
 hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                               float* h, float* y, hipStream_t st, const CombineArgs& comb);
 hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,

@@ -1,0 +1,285 @@
+// Shared (always-on) experts for large batches: bf16 GEMMs on the matrix
+// cores (v_mfma_f32_16x16x32_bf16) with both operands staged through LDS
+// rings by LDS-DMA.
+//
+// The pages keep two shared experts beside the routed ones and run every
+// token through both (the kimi-k3-in-c review, "at a glance" table; the
+// README's shard census): S = sum_j Wd_j (silu(Wg_j x) * (Wu_j x)).  With
+// bf16 weights and thousands of tokens these are two dense GEMMs:
+//   gate/up: [T x d] . [d x 2 S fs]  ->  h = silu(g) * u      [T][S][fs]
+//   down:    [T x S fs] . [S fs x d] ->  y                    [T][d]
+//
+// Structure (one workgroup of 8 waves per CU, two waves per SIMD):
+//   * waves 0..3 only compute, waves 4..7 only copy: each stage (64
+//     contraction elements) of the activation tile and of the weight tile is
+//     copied into a ring of kRing LDS slots, copy wave 4 + q issuing quarter
+//     q of the copies, kRing - 1 stages ahead of the compute; one s_barrier
+//     per stage is passed by both roles (a copy wave first waits for its own
+//     copies of that stage, a compute wave for its LDS reads of the previous
+//     one), and after it the copy waves refill the previous stage's slot;
+//   * items are (n-tile, m-tile of 128 tokens) in 8 contiguous ranges (one
+//     per XCD), ordered so that the workgroups of an XCD work on 8 m-tiles x
+//     4 n-tiles at a time and share both operands through their L2;
+//   * LDS rows are 128 bytes (64 bf16); 16-byte unit u of row r sits at
+//     position u ^ ((r >> 1) & 7), so the 16 rows that one fragment read
+//     touches fall on 16 distinct 4-bank groups.
+// Every (token, output) value is the chain of the other shared-expert
+// kernels (stages of 64 elements in order, then the two 32-element halves
+// of a stage, and in the down product the hi then the lo bf16 part of h):
+// a token's bits do not depend on the batch or tile around it.
+//   gate/up: waves side by side along the weights, each 128 tokens x 64
+//     weight rows (32 gate rows and the matching 32 up rows); the epilogue
+//     writes h already split for the down product: hi = bf16(h),
+//     lo = bf16(h - hi), two [T][S fs] bf16 planes;
+//   down: waves 2 x 2, each 64 tokens x 64 outputs; A = the hi and lo planes
+//     of h, contracted over both experts in one chain; y fp32.
+#include "internal.h"
+#include "kern_common.h"
+#include "grouped.h"
+
+namespace k3 {
+namespace {
+
+using namespace grouped;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kBK = 64;        // contraction elements per stage
+constexpr int kBM = 128;       // tokens per m-tile
+constexpr int kRing = 3;       // LDS slots per operand ring
+
+__device__ __forceinline__ int row_swz(int r) { return (r >> 1) & 7; }
+
+// Tile of item `it`: groups of kGM consecutive m-tiles, the m-tile fastest
+// within a group, then the n-tile, so that 32 consecutive items (the ones the
+// workgroups of one XCD run at the same time) are 8 m-tiles x 4 n-tiles and
+// share both operands through that XCD's L2.
+constexpr int kGM = 8;
+__device__ __forceinline__ void item_tile(int it, int n_mt, int NT, int& mt, int& nt) {
+  const int grp = it / (kGM * NT), first = grp * kGM;
+  const int gsz = min(n_mt - first, kGM);
+  const int r = it - grp * (kGM * NT);
+  nt = r / gsz;
+  mt = first + (r - nt * gsz);
+}
+// LDS byte offset of unit u (16 bytes: elements 8u .. 8u+7 of the stage) of row r
+__device__ __forceinline__ int unit_off(int r, int u) { return r * 128 + ((u ^ row_swz(r)) << 4); }
+
+__device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int r, int u) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + unit_off(r, u)));
+}
+
+template <bool DOWN>
+struct Tiles {
+  static constexpr int NPL = DOWN ? 2 : 1;        // activation planes (h hi, h lo)
+  static constexpr int WM = DOWN ? 2 : 1;         // compute waves along the tokens
+  static constexpr int WN = 4 / WM;               // ... and along the weight rows
+  static constexpr int MF = kBM / 16 / WM;        // 16-row blocks per compute wave
+  static constexpr int NF = 4;                    // 16-row weight fragments per wave
+  static constexpr int BN = WN * NF * 16;         // weight rows per n-tile
+  static constexpr int A_SLOT = NPL * kBM * 128;
+  static constexpr int B_SLOT = BN * 128;
+  static constexpr int NA = NPL * kBM * 8 / 256;  // A copies per copy wave per stage
+  static constexpr int NB = BN * 8 / 256;         // B copies per copy wave per stage
+  static constexpr int NCP = NA + NB;
+};
+
+// x (gate/up: [T][d] bf16) or h (down: hi and lo planes [T][S fs] bf16) times
+// the shared weights (gate/up: w13 [S][2 fs][d]; down: w2 [S][d][fs]).
+template <bool DOWN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_gemm_lds(
+    const uint16_t* __restrict__ a0, const uint16_t* __restrict__ a1,
+    const uint16_t* __restrict__ w, void* __restrict__ out, int T, int d, int fs, int S) {
+  using C = Tiles<DOWN>;
+  constexpr int MF = C::MF, NF = C::NF;
+  __shared__ __attribute__((aligned(16))) uint8_t sA[kRing * C::A_SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[kRing * C::B_SLOT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const bool copier = wv >= 4;
+  const int K = DOWN ? S * fs : d;                // contraction length
+  const int nst = K / kBK;
+  const int nf_t = fs / 128;                      // gate/up n-tiles per expert
+  const int NT = DOWN ? d / C::BN : S * nf_t;
+  const int n_mt = (T + kBM - 1) / kBM;
+  const ItemRange ir = item_range((long)NT * n_mt);
+  const int it_first = (int)ir.first, it_end = (int)ir.end, it_step = (int)ir.step;
+  const int n_items = it_first < it_end ? (it_end - it_first + it_step - 1) / it_step : 0;
+  const int g_total = n_items * nst;
+  const size_t a_row = (size_t)K;                 // elements per activation row (each plane)
+  const size_t plane = (size_t)T * K;             // elements per activation plane
+
+  // weight row of local row r of n-tile nt (gate/up: wave r / 64 owns gate
+  // rows 0..31 then the matching up rows of its 32 features)
+  auto wrow = [&](int nt, int r) -> size_t {
+    if (DOWN) return (size_t)nt * C::BN + r;
+    const int se = nt / nf_t, ntf = nt - se * nf_t;
+    const int cw = r >> 6, nf = (r >> 4) & 3;
+    return (size_t)se * 2 * fs + (nf >= 2 ? fs : 0) + ntf * 128 + cw * 32 + (nf & 1) * 16 + (r & 15);
+  };
+
+  if (copier) {
+    const int cq = wv - 4;
+    const uint16_t* ap[C::NA];
+    const uint16_t* bp[C::NB];
+    int c_it = it_first, c_st = 0;
+    // per item: this wave's units' source rows (stage 0)
+    auto setup = [&]() {
+      int nt, mt;
+      item_tile(c_it, n_mt, NT, mt, nt);
+      const int row0 = mt * kBM, rows = min(kBM, T - row0);
+#pragma unroll
+      for (int c = 0; c < C::NA; ++c) {
+        const int U = (cq * C::NA + c) * 64 + lane;
+        const int pl = U / (kBM * 8), v = U - pl * (kBM * 8);
+        const int r = v >> 3, u = (v & 7) ^ row_swz(r);
+        ap[c] = (pl ? a1 : a0) + (size_t)(row0 + min(r, rows - 1)) * a_row + u * 8;
+      }
+#pragma unroll
+      for (int c = 0; c < C::NB; ++c) {
+        const int V = (cq * C::NB + c) * 64 + lane;
+        const int r = V >> 3, u = (V & 7) ^ row_swz(r);
+        bp[c] = w + wrow(nt, r) * (DOWN ? (size_t)fs : (size_t)d) + u * 8;
+      }
+    };
+    auto issue = [&](int g) {
+      if (c_it >= it_end) return;
+      const uint32_t abase = lds_addr(sA) + (uint32_t)((g % kRing) * C::A_SLOT);
+      const uint32_t bbase = lds_addr(sB) + (uint32_t)((g % kRing) * C::B_SLOT);
+      const size_t ao = (size_t)c_st * kBK;
+      // down: stage c_st of the chain is expert c_st / spe, elements (c_st % spe) * 64 of its rows
+      const size_t bo = DOWN ? (size_t)(c_st * kBK / fs) * ((size_t)d * fs) + (size_t)(c_st * kBK % fs)
+                             : (size_t)c_st * kBK;
+#pragma unroll
+      for (int c = 0; c < C::NA; ++c)
+        dma16_raw(ap[c] + ao, abase + (uint32_t)((cq * C::NA + c) * 1024));
+#pragma unroll
+      for (int c = 0; c < C::NB; ++c)
+        dma16_raw(bp[c] + bo, bbase + (uint32_t)((cq * C::NB + c) * 1024));
+      if (++c_st == nst) {
+        c_st = 0;
+        c_it += it_step;
+        if (c_it < it_end) setup();
+      }
+    };
+    if (c_it < it_end) setup();
+#pragma unroll
+    for (int j = 0; j < kRing - 1; ++j) issue(j);
+#pragma unroll 1
+    for (int g = 0; g < g_total; ++g) {
+      // the copies of stages g + 1 .. g + kRing - 2 may stay in flight
+      if (g + kRing - 2 < g_total) wait_vmem<(kRing - 2) * C::NCP>();
+      else wait_vmem<0>();
+      wg_barrier();
+      issue(g + kRing - 1);
+    }
+    wait_vmem<0>();
+    return;
+  }
+
+  const int wm = wv / C::WN, wn = wv - wm * C::WN;
+  int g = 0;
+  for (int it = it_first; it < it_end; it += it_step) {
+    int nt, mt;
+    item_tile(it, n_mt, NT, mt, nt);
+    const int row0 = mt * kBM, rows = min(kBM, T - row0);
+    f32x4_t acc[MF][NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) acc[i][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int s = 0; s < nst; ++s, ++g) {
+      wait_lds();
+      wg_barrier();
+      const uint8_t* abase = sA + (g % kRing) * C::A_SLOT;
+      const uint8_t* bbase = sB + (g % kRing) * C::B_SLOT;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int u = 4 * j + lg;   // elements 32 j + 8 lg .. +8 of the stage
+        bf16x8_t b[NF];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) b[nf] = lds_frag(bbase, (wn * NF + nf) * 16 + ln, u);
+        bf16x8_t a[2][C::NPL];
+        auto load_a = [&](int i, bf16x8_t (&av)[C::NPL]) {
+          const int r = (wm * MF + i) * 16 + ln;
+#pragma unroll
+          for (int p = 0; p < C::NPL; ++p) av[p] = lds_frag(abase + p * (kBM * 128), r, u);
+        };
+        load_a(0, a[0]);
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+          if (i + 1 < MF) load_a(i + 1, a[(i + 1) & 1]);
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int p = 0; p < C::NPL; ++p)
+              acc[i][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i & 1][p], b[nf], acc[i][nf],
+                                                                   0, 0, 0);
+        }
+      }
+    }
+    if constexpr (DOWN) {
+      float* y = static_cast<float*>(out);
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = (wm * MF + i) * 16 + lg * 4 + r;
+          if (m < rows) {
+            float* yr = y + (size_t)(row0 + m) * d + nt * C::BN + wn * (NF * 16) + ln;
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) yr[nf * 16] = acc[i][nf][r];
+          }
+        }
+    } else {
+      // h = silu(g) * u of the wave's 32 features, as its hi and lo bf16 parts
+      uint16_t* hh = static_cast<uint16_t*>(out);
+      uint16_t* hl = hh + (size_t)T * S * fs;
+      const int se = nt / nf_t, ntf = nt - se * nf_t;
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = i * 16 + lg * 4 + r;
+          if (m < rows) {
+            const size_t o = (size_t)(row0 + m) * S * fs + (size_t)se * fs + ntf * 128 + wn * 32 + ln;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const float hv = silu_mul(acc[i][q][r], acc[i][q + 2][r]);
+              const uint16_t hi = f32_to_bf16(hv);
+              hh[o + q * 16] = hi;
+              hl[o + q * 16] = f32_to_bf16(hv - __uint_as_float((uint32_t)hi << 16));
+            }
+          }
+        }
+    }
+  }
+}
+
+}  // namespace
+
+bool shared_lds_ok(const k3moe_shape& s) {
+  return s.f_shared % 128 == 0 && s.d % 128 == 0;
+}
+
+// h: T * S * fs * 4 bytes, written by the gate/up as two bf16 planes and
+// read back by the down.
+hipError_t launch_shared_lds(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
+                             float* h, float* y, hipStream_t st) {
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* w13 = static_cast<const uint16_t*>(b.w13);
+  const uint16_t* w2 = static_cast<const uint16_t*>(b.w2);
+  const int T = (int)s.T, S = b.n_experts, fs = b.f;
+  uint16_t* hh = reinterpret_cast<uint16_t*>(h);
+  const dim3 g(grouped_grid());   // one workgroup per CU
+  shared_gemm_lds<false><<<g, 512, 0, st>>>(xb, nullptr, w13, hh, T, s.d, fs, S);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  shared_gemm_lds<true><<<g, 512, 0, st>>>(hh, hh + (size_t)T * S * fs, w2, y, T, s.d, fs, S);
+  return hipGetLastError();
+}
+
+}  // namespace k3
