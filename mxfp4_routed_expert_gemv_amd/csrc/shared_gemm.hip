@@ -46,7 +46,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kBK = 64;        // contraction elements per stage
-constexpr int kBM = 128;       // tokens per m-tile
 constexpr int kRing = 3;       // LDS slots per operand ring
 
 __device__ __forceinline__ int row_swz(int r) { return (r >> 1) & 7; }
@@ -70,29 +69,35 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int r, int u) 
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + unit_off(r, u)));
 }
 
-template <bool DOWN>
+// Tile shape: BM tokens per m-tile, WM compute waves along the tokens and
+// 4 / WM along the weight rows, NF 16-row weight fragments per wave (gate/up:
+// NF / 2 gate fragments, then the matching up fragments).
+template <bool DOWN, int BM_, int WM_, int NF_>
 struct Tiles {
+  static constexpr int BM = BM_, WM = WM_, NF = NF_;
   static constexpr int NPL = DOWN ? 2 : 1;        // activation planes (h hi, h lo)
-  static constexpr int WM = DOWN ? 2 : 1;         // compute waves along the tokens
-  static constexpr int WN = 4 / WM;               // ... and along the weight rows
-  static constexpr int MF = kBM / 16 / WM;        // 16-row blocks per compute wave
-  static constexpr int NF = 4;                    // 16-row weight fragments per wave
+  static constexpr int WN = 4 / WM;
+  static constexpr int MF = BM / 16 / WM;         // 16-row blocks per compute wave
   static constexpr int BN = WN * NF * 16;         // weight rows per n-tile
-  static constexpr int A_SLOT = NPL * kBM * 128;
+  static constexpr int FW = NF * 8;               // gate/up: features per wave
+  static constexpr int A_SLOT = NPL * BM * 128;
   static constexpr int B_SLOT = BN * 128;
-  static constexpr int NA = NPL * kBM * 8 / 256;  // A copies per copy wave per stage
+  static constexpr int NA = NPL * BM * 8 / 256;   // A copies per copy wave per stage
   static constexpr int NB = BN * 8 / 256;         // B copies per copy wave per stage
   static constexpr int NCP = NA + NB;
+  static_assert(MF >= 1 && NA >= 1 && NB >= 1 && NA * 256 == NPL * BM * 8 && NB * 256 == BN * 8,
+                "whole copy rounds");
+  static_assert(DOWN || NF % 2 == 0, "gate/up fragments come in gate/up pairs");
 };
 
 // x (gate/up: [T][d] bf16) or h (down: hi and lo planes [T][S fs] bf16) times
 // the shared weights (gate/up: w13 [S][2 fs][d]; down: w2 [S][d][fs]).
-template <bool DOWN>
+template <bool DOWN, int BM, int WM, int NF>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_gemm_lds(
     const uint16_t* __restrict__ a0, const uint16_t* __restrict__ a1,
     const uint16_t* __restrict__ w, void* __restrict__ out, int T, int d, int fs, int S) {
-  using C = Tiles<DOWN>;
-  constexpr int MF = C::MF, NF = C::NF;
+  using C = Tiles<DOWN, BM, WM, NF>;
+  constexpr int MF = C::MF, kBM = BM, FW = C::FW;
   __shared__ __attribute__((aligned(16))) uint8_t sA[kRing * C::A_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sB[kRing * C::B_SLOT];
 
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool copier = wv >= 4;
   const int K = DOWN ? S * fs : d;                // contraction length
   const int nst = K / kBK;
-  const int nf_t = fs / 128;                      // gate/up n-tiles per expert
+  const int nf_t = fs / (C::WN * FW);             // gate/up n-tiles per expert
   const int NT = DOWN ? d / C::BN : S * nf_t;
   const int n_mt = (T + kBM - 1) / kBM;
   const ItemRange ir = item_range((long)NT * n_mt);
@@ -111,13 +116,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const size_t a_row = (size_t)K;                 // elements per activation row (each plane)
   const size_t plane = (size_t)T * K;             // elements per activation plane
 
-  // weight row of local row r of n-tile nt (gate/up: wave r / 64 owns gate
-  // rows 0..31 then the matching up rows of its 32 features)
+  // weight row of local row r of n-tile nt (gate/up: wave r / (16 NF) owns
+  // the gate rows of its FW features, then the matching up rows)
   auto wrow = [&](int nt, int r) -> size_t {
     if (DOWN) return (size_t)nt * C::BN + r;
     const int se = nt / nf_t, ntf = nt - se * nf_t;
-    const int cw = r >> 6, nf = (r >> 4) & 3;
-    return (size_t)se * 2 * fs + (nf >= 2 ? fs : 0) + ntf * 128 + cw * 32 + (nf & 1) * 16 + (r & 15);
+    const int cw = r / (16 * NF), nf = (r >> 4) % NF;
+    return (size_t)se * 2 * fs + (nf >= NF / 2 ? fs : 0) + ntf * (C::WN * FW) + cw * FW +
+           (nf % (NF / 2)) * 16 + (r & 15);
   };
 
   if (copier) {
@@ -243,12 +249,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = i * 16 + lg * 4 + r;
+          const int m = (wm * MF + i) * 16 + lg * 4 + r;
           if (m < rows) {
-            const size_t o = (size_t)(row0 + m) * S * fs + (size_t)se * fs + ntf * 128 + wn * 32 + ln;
+            const size_t o = (size_t)(row0 + m) * S * fs + (size_t)se * fs + ntf * (C::WN * FW) +
+                             wn * FW + ln;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const float hv = silu_mul(acc[i][q][r], acc[i][q + 2][r]);
+            for (int q = 0; q < NF / 2; ++q) {
+              const float hv = silu_mul(acc[i][q][r], acc[i][q + NF / 2][r]);
               const uint16_t hi = f32_to_bf16(hv);
               hh[o + q * 16] = hi;
               hl[o + q * 16] = f32_to_bf16(hv - __uint_as_float((uint32_t)hi << 16));
@@ -259,27 +266,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-}  // namespace
-
-bool shared_lds_ok(const k3moe_shape& s) {
-  return s.f_shared % 128 == 0 && s.d % 128 == 0;
-}
-
 // h: T * S * fs * 4 bytes, written by the gate/up as two bf16 planes and
 // read back by the down.
-hipError_t launch_shared_lds(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
-                             float* h, float* y, hipStream_t st) {
+template <int BM, int WMG, int NFG, int WMD, int NFD>
+hipError_t shared_lds_pair(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
+                           float* h, float* y, hipStream_t st) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* w13 = static_cast<const uint16_t*>(b.w13);
   const uint16_t* w2 = static_cast<const uint16_t*>(b.w2);
   const int T = (int)s.T, S = b.n_experts, fs = b.f;
   uint16_t* hh = reinterpret_cast<uint16_t*>(h);
   const dim3 g(grouped_grid());   // one workgroup per CU
-  shared_gemm_lds<false><<<g, 512, 0, st>>>(xb, nullptr, w13, hh, T, s.d, fs, S);
+  shared_gemm_lds<false, BM, WMG, NFG><<<g, 512, 0, st>>>(xb, nullptr, w13, hh, T, s.d, fs, S);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  shared_gemm_lds<true><<<g, 512, 0, st>>>(hh, hh + (size_t)T * S * fs, w2, y, T, s.d, fs, S);
+  shared_gemm_lds<true, BM, WMD, NFD><<<g, 512, 0, st>>>(hh, hh + (size_t)T * S * fs, w2, y, T,
+                                                        s.d, fs, S);
   return hipGetLastError();
+}
+
+}  // namespace
+
+bool shared_lds_ok(const k3moe_shape& s) {
+  return s.f_shared % 128 == 0 && s.d % 128 == 0;
+}
+
+// Tile shapes by batch (measured at d 7168, two experts of fs 2048; the
+// shared FFN, gate/up + down):
+//   T <= 64:   64-token tiles, the 4 waves splitting the tokens, n-tiles of
+//              16 features / 32 outputs (256 and 224 items: the weights spread
+//              over every CU): 50-53 us (the register-fed small-batch kernels
+//              took 125-181 us);
+//   T <= 256:  64-token tiles, waves 2 x 2: 69-79 us;
+//   T <= 640:  128-token tiles, waves 2 x 2: 120-128 us at 384-512 tokens;
+//   larger:    128-token tiles, gate/up waves side by side along the weights:
+//              0.24 ms at 1024 tokens, 0.97 ms at 4096, 3.5 ms at 16384.
+hipError_t launch_shared_lds(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
+                             float* h, float* y, hipStream_t st) {
+  if (s.T <= 64) return shared_lds_pair<64, 4, 2, 4, 2>(s, b, x, h, y, st);
+  if (s.T <= 256) return shared_lds_pair<64, 2, 4, 2, 4>(s, b, x, h, y, st);
+  if (s.T <= 640) return shared_lds_pair<128, 2, 4, 2, 4>(s, b, x, h, y, st);
+  return shared_lds_pair<128, 1, 4, 2, 4>(s, b, x, h, y, st);
 }
 
 }  // namespace k3
