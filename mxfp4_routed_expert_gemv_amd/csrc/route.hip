@@ -615,7 +615,7 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
 // fp64 values for the experts that can still reach the top k, so:
 //   1. router_bf16: every logit on the bf16 matrix cores
 //      (v_mfma_f32_16x16x32_bf16, fp32 accumulation), written as fp32;
-//   2. route_refine (one wave per token): each fp32 logit gets a bound on
+//   2. route_refine (one wave per token, four tokens per workgroup): each fp32 logit gets a bound on
 //      its distance to the oracle's value; the experts whose upper bound
 //      reaches the k-th largest lower bound (k + a few) are recomputed in
 //      fp64 with the GEMV router's arithmetic and bound, the others keep the
@@ -857,9 +857,10 @@ __device__ __forceinline__ void refine_dot(const uint16_t* __restrict__ xr,
   }
 }
 
-// One workgroup of NW waves per token.  Wave 0: bounds, the k-th largest
-// lower end, the candidate list (LDS), and the non-candidates' values and
-// bounds; then every wave re-evaluates candidate pairs in fp64.
+// One workgroup of NW waves per NW tokens.  Wave w, for token NW b + w:
+// bounds, the k-th largest lower end, the candidate list (LDS), and the
+// non-candidates' values and bounds; then the waves share the fp64
+// re-evaluation of all the workgroup's candidate pairs.
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void route_refine(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ wr,
@@ -867,13 +868,16 @@ __global__ __launch_bounds__(64 * NW) void route_refine(const uint16_t* __restri
                                                         double* __restrict__ logits,
                                                         float* __restrict__ lbound, int T, int d,
                                                         int E, int k, RouterMode rm) {
-  __shared__ int s_cand[1024];
-  __shared__ int s_n;
-  __shared__ uint64_t s_key[kWave];
+  __shared__ int s_cand_all[NW][1024];
+  __shared__ int s_n_all[NW];
+  __shared__ uint64_t s_key_all[NW][kWave];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = blockIdx.x;
+  const int t = blockIdx.x * NW + wv;
+  int* s_cand = s_cand_all[wv];
+  uint64_t* s_key = s_key_all[wv];
   const uint16_t* xr = x + (size_t)t * d;
-  if (wv == 0) {
+  if (lane == 0) s_n_all[wv] = 0;
+  if (t < T) {
     const bool sig = rm.mode != K3MOE_ROUTER_SOFTMAX;
     const int nj = (E + kWave - 1) / kWave;
     // |x_t|, fp64 sum of exact squares
@@ -988,24 +992,34 @@ __global__ __launch_bounds__(64 * NW) void route_refine(const uint16_t* __restri
         lbound[(size_t)t * E + e] = (float)(bnd[j] * (1.0 + 0x1p-20));
       }
     }
-    if (lane == 0) s_n = n;
+    if (lane == 0) s_n_all[wv] = n;
   }
   __syncthreads();
   // the candidates' fp64 values and bounds (the GEMV router's arithmetic:
   // |acc - exact| <= (d/64 + 8) u S, |oracle - exact| <= d u S, u = 2^-53,
-  // S <= 1.01 aabs), two rows per pass, the passes shared by the waves
-  const int n = s_n;
-  for (int q = 2 * wv; q < n; q += 2 * NW) {
-    const int e0 = s_cand[q], e1 = q + 1 < n ? s_cand[q + 1] : e0;
+  // S <= 1.01 aabs), two rows of one token per pass; pass q of the
+  // workgroup's list (token 0's passes, then token 1's, ...) goes to wave
+  // q % NW
+  int pe[NW + 1];
+  pe[0] = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) pe[i + 1] = pe[i] + (s_n_all[i] + 1) / 2;
+  for (int q = wv; q < pe[NW]; q += NW) {
+    int ti = 0;
+#pragma unroll
+    for (int i = 1; i < NW; ++i) ti += q >= pe[i] ? 1 : 0;
+    const int tt = blockIdx.x * NW + ti, n = s_n_all[ti];
+    const int c = 2 * (q - pe[ti]);
+    const int e0 = s_cand_all[ti][c], e1 = c + 1 < n ? s_cand_all[ti][c + 1] : e0;
     double acc[2];
     float aabs[2];
-    refine_dot(xr, wr + (size_t)e0 * d, wr + (size_t)e1 * d, d, lane, acc, aabs);
+    refine_dot(x + (size_t)tt * d, wr + (size_t)e0 * d, wr + (size_t)e1 * d, d, lane, acc, aabs);
     if (lane == 0) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int e = p ? e1 : e0;
-        logits[(size_t)t * E + e] = acc[p];
-        lbound[(size_t)t * E + e] = (float)((2.0 * d + 64.0) * 0x1p-53 * (double)aabs[p] * 1.02);
+        logits[(size_t)tt * E + e] = acc[p];
+        lbound[(size_t)tt * E + e] = (float)((2.0 * d + 64.0) * 0x1p-53 * (double)aabs[p] * 1.02);
       }
     }
   }
@@ -1021,7 +1035,8 @@ void launch_router_bf16(const uint16_t* x, const uint16_t* wr, const RouteWs& ws
   else
     router_bf16<4, 4><<<dim3((T + 127) / 128, (E + 127) / 128), 256, 0, st>>>(x, wr, ws.lbound, T,
                                                                              d, E);
-  route_refine<4><<<T, 256, 0, st>>>(x, wr, ws.wnorm, ws.logits, ws.lbound, T, d, E, k, rm);
+  route_refine<4><<<(T + 3) / 4, 256, 0, st>>>(x, wr, ws.wnorm, ws.logits, ws.lbound, T, d, E, k,
+                                              rm);
 }
 
 // fp64 logits to the fp32 output
