@@ -158,6 +158,9 @@ bool shared_mfma_ok(const k3moe_shape& s);
 bool shared_lds_ok(const k3moe_shape& s);
 hipError_t launch_shared_lds(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                              float* h, float* y, hipStream_t st);
+// The router's fp32 logits [T][E] on the same LDS-ring GEMM (d % 64 == 0).
+hipError_t launch_router_logits_lds(const uint16_t* x, const uint16_t* wr, float* l, int T, int d,
+                                    int E, hipStream_t st);
 hipError_t launch_shared_mfma(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,
                               float* h, float* y, hipStream_t st, const CombineArgs& comb);
 hipError_t launch_expert_ffn(const k3moe_shape& s, const k3moe_expert_bank& bank, const void* x,

@@ -613,8 +613,9 @@ __global__ __launch_bounds__(64) void topk_softmax(const double* __restrict__ lo
 // the GEMV arrangement above), which can differ in the last bits.  The
 // selection only needs
 // fp64 values for the experts that can still reach the top k, so:
-//   1. router_bf16: every logit on the bf16 matrix cores
-//      (v_mfma_f32_16x16x32_bf16, fp32 accumulation), written as fp32;
+//   1. every logit on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32
+//      accumulation), written as fp32: the shared experts' LDS-ring GEMM
+//      (shared_gemm.hip) with x against the router rows;
 //   2. route_refine (one wave per token, four tokens per workgroup): each fp32 logit gets a bound on
 //      its distance to the oracle's value; the experts whose upper bound
 //      reaches the k-th largest lower bound (k + a few) are recomputed in
@@ -655,157 +656,7 @@ __global__ __launch_bounds__(256) void router_wnorm(const uint16_t* __restrict__
   if (lane == 0) wnorm[e] = (float)(sqrt(s) * (1.0 + 0x1p-20));
 }
 
-// Logits of 32 FA tokens x 32 FB experts per workgroup; wave (wt = wv & 1,
-// we = wv >> 1) computes tokens 16 FA wt + [0, 16 FA) x experts
-// 16 FB we + [0, 16 FB) as FA x FB fragments.  Per contraction step of 32,
-// lane (i = lane % 16,
-// g = lane / 16) loads elements 8 g .. 8 g + 7 of its fragment rows (token
-// rows for A, expert rows for B) straight from global memory (the L2), PD
-// steps ahead.  Rows past T or E are clamped (their outputs are not stored).
 constexpr int kBf16RouterMinT = 512;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-template <int FA, int FB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void router_bf16(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ logits32,
-    int T, int d, int E) {
-  constexpr int PD = 3;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int li = lane & 15, lg = lane >> 4;
-  const int t0 = blockIdx.x * (32 * FA) + (wv & 1) * (16 * FA);
-  const int e0 = blockIdx.y * (32 * FB) + (wv >> 1) * (16 * FB);
-  const uint16_t* ar[FA];
-  const uint16_t* br[FB];
-#pragma unroll
-  for (int f = 0; f < FA; ++f) ar[f] = x + (size_t)min(t0 + f * 16 + li, T - 1) * d + lg * 8;
-#pragma unroll
-  for (int f = 0; f < FB; ++f) br[f] = wr + (size_t)min(e0 + f * 16 + li, E - 1) * d + lg * 8;
-  f32x4_t acc[FA][FB];
-#pragma unroll
-  for (int a = 0; a < FA; ++a)
-#pragma unroll
-    for (int b = 0; b < FB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int ns = d / 32;
-  uint4 av[PD][FA], bv[PD][FB];
-  auto load = [&](int s, int slot) {
-#pragma unroll
-    for (int f = 0; f < FA; ++f) av[slot][f] = ldg16(ar[f] + (size_t)s * 32);
-#pragma unroll
-    for (int f = 0; f < FB; ++f) bv[slot][f] = ldg16(br[f] + (size_t)s * 32);
-  };
-#pragma unroll
-  for (int q = 0; q < PD; ++q) load(min(q, ns - 1), q);
-#pragma unroll 1
-  for (int s0 = 0; s0 < ns; s0 += PD) {
-#pragma unroll
-    for (int q = 0; q < PD; ++q) {
-      if (s0 + q < ns) {
-        bf16x8_t a[FA], b[FB];
-#pragma unroll
-        for (int f = 0; f < FA; ++f) a[f] = as_bf16x8(av[q][f]);
-#pragma unroll
-        for (int f = 0; f < FB; ++f) b[f] = as_bf16x8(bv[q][f]);
-        load(min(s0 + q + PD, ns - 1), q);   // past the end: a repeat, unused
-#pragma unroll
-        for (int i = 0; i < FA; ++i)
-#pragma unroll
-          for (int j = 0; j < FB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-  // element r of fragment (i, j): token 16 i + 4 g + r, expert 16 j + lane % 16
-#pragma unroll
-  for (int i = 0; i < FA; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + i * 16 + lg * 4 + r;
-      if (t < T) {
-#pragma unroll
-        for (int j = 0; j < FB; ++j) {
-          const int e = e0 + j * 16 + li;
-          if (e < E) logits32[(size_t)t * E + e] = acc[i][j][r];
-        }
-      }
-    }
-}
-
-// Mid-size batches: a workgroup computes 16 TA tokens x 16 EB experts, each
-// wave over a quarter of the contraction, the four partial sums added in
-// wave order (the bound above covers this order too), so that the grid fills
-// the chip (448 workgroups at 512 tokens and 896 experts).
-template <int TA, int EB>
-__global__ __launch_bounds__(256) void router_bf16_ks(const uint16_t* __restrict__ x,
-                                                      const uint16_t* __restrict__ wr,
-                                                      float* __restrict__ logits32, int T, int d,
-                                                      int E) {
-  constexpr int BT = 16 * TA, BE = 16 * EB, PD = 4;
-  __shared__ float part[4][BT][BE + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int li = lane & 15, lg = lane >> 4;
-  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
-  const int kq = d / 4;                 // contraction slice per wave (multiple of 128)
-  const uint16_t* ar[TA];
-  const uint16_t* br[EB];
-#pragma unroll
-  for (int f = 0; f < TA; ++f) ar[f] = x + (size_t)min(t0 + f * 16 + li, T - 1) * d + wv * kq + lg * 8;
-#pragma unroll
-  for (int f = 0; f < EB; ++f) br[f] = wr + (size_t)min(e0 + f * 16 + li, E - 1) * d + wv * kq + lg * 8;
-  f32x4_t acc[TA][EB];
-#pragma unroll
-  for (int a = 0; a < TA; ++a)
-#pragma unroll
-    for (int b = 0; b < EB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int ns = kq / 32;
-  uint4 av[PD][TA], bv[PD][EB];
-  auto load = [&](int st, int slot) {
-#pragma unroll
-    for (int f = 0; f < TA; ++f) av[slot][f] = ldg16(ar[f] + (size_t)st * 32);
-#pragma unroll
-    for (int f = 0; f < EB; ++f) bv[slot][f] = ldg16(br[f] + (size_t)st * 32);
-  };
-#pragma unroll
-  for (int q = 0; q < PD; ++q) load(min(q, ns - 1), q);
-#pragma unroll 1
-  for (int s0 = 0; s0 < ns; s0 += PD) {
-#pragma unroll
-    for (int q = 0; q < PD; ++q) {
-      if (s0 + q < ns) {
-        bf16x8_t a[TA], b[EB];
-#pragma unroll
-        for (int f = 0; f < TA; ++f) a[f] = as_bf16x8(av[q][f]);
-#pragma unroll
-        for (int f = 0; f < EB; ++f) b[f] = as_bf16x8(bv[q][f]);
-        load(min(s0 + q + PD, ns - 1), q);   // past the end: a repeat, unused
-#pragma unroll
-        for (int i = 0; i < TA; ++i)
-#pragma unroll
-          for (int j = 0; j < EB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TA; ++i)
-#pragma unroll
-    for (int j = 0; j < EB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part[wv][i * 16 + lg * 4 + r][j * 16 + li] = acc[i][j][r];
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < (BT * BE + 255) / 256; ++u) {
-    const int o = tid + 256 * u;
-    const int tt = o / BE, ee = o % BE;
-    const int t = t0 + tt, e = e0 + ee;
-    if (tt < BT && t < T && e < E)
-      logits32[(size_t)t * E + e] =
-          ((part[0][tt][ee] + part[1][tt][ee]) + part[2][tt][ee]) + part[3][tt][ee];
-  }
-}
 
 // A token's candidates are re-evaluated two rows at a time: fp64 products
 // and sums in the GEMV router's arrangement.  (lbound holds the fp32 logits on
@@ -1028,13 +879,7 @@ __global__ __launch_bounds__(64 * NW) void route_refine(const uint16_t* __restri
 void launch_router_bf16(const uint16_t* x, const uint16_t* wr, const RouteWs& ws, int T, int d,
                         int E, int k, const RouterMode& rm, hipStream_t st) {
   router_wnorm<<<(E + 3) / 4, 256, 0, st>>>(wr, ws.wnorm, d, E);
-  // tiles by batch size, so that the grid fills the chip
-  if (T < 2048)
-    router_bf16_ks<2, 2><<<dim3((T + 31) / 32, (E + 31) / 32), 256, 0, st>>>(x, wr, ws.lbound, T,
-                                                                            d, E);
-  else
-    router_bf16<4, 4><<<dim3((T + 127) / 128, (E + 127) / 128), 256, 0, st>>>(x, wr, ws.lbound, T,
-                                                                             d, E);
+  launch_router_logits_lds(x, wr, ws.lbound, T, d, E, st);
   route_refine<4><<<(T + 3) / 4, 256, 0, st>>>(x, wr, ws.wnorm, ws.logits, ws.lbound, T, d, E, k,
                                               rm);
 }

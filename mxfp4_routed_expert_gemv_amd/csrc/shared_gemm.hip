@@ -1,6 +1,6 @@
-// Shared (always-on) experts for large batches: bf16 GEMMs on the matrix
-// cores (v_mfma_f32_16x16x32_bf16) with both operands staged through LDS
-// rings by LDS-DMA.
+// Shared (always-on) experts in the matrix-core class, and the router's bf16
+// logits there: bf16 GEMMs on the matrix cores (v_mfma_f32_16x16x32_bf16)
+// with both operands staged through LDS rings by LDS-DMA.
 //
 // The pages keep two shared experts beside the routed ones and run every
 // token through both (the kimi-k3-in-c review, "at a glance" table; the
@@ -72,8 +72,13 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int r, int u) 
 // Tile shape: BM tokens per m-tile, WM compute waves along the tokens and
 // 4 / WM along the weight rows, NF 16-row weight fragments per wave (gate/up:
 // NF / 2 gate fragments, then the matching up fragments).
-template <bool DOWN, int BM_, int WM_, int NF_>
+// The products this kernel runs: the shared experts' gate/up and down, and
+// the router's bf16 logits (x [T][d] against w_router [E][d], fp32 out).
+constexpr int kGateUp = 0, kDown = 1, kLogits = 2;
+
+template <int MODE, int BM_, int WM_, int NF_>
 struct Tiles {
+  static constexpr bool DOWN = MODE == kDown;
   static constexpr int BM = BM_, WM = WM_, NF = NF_;
   static constexpr int NPL = DOWN ? 2 : 1;        // activation planes (h hi, h lo)
   static constexpr int WN = 4 / WM;
@@ -87,16 +92,18 @@ struct Tiles {
   static constexpr int NCP = NA + NB;
   static_assert(MF >= 1 && NA >= 1 && NB >= 1 && NA * 256 == NPL * BM * 8 && NB * 256 == BN * 8,
                 "whole copy rounds");
-  static_assert(DOWN || NF % 2 == 0, "gate/up fragments come in gate/up pairs");
+  static_assert(MODE != kGateUp || NF % 2 == 0, "gate/up fragments come in gate/up pairs");
 };
 
-// x (gate/up: [T][d] bf16) or h (down: hi and lo planes [T][S fs] bf16) times
-// the shared weights (gate/up: w13 [S][2 fs][d]; down: w2 [S][d][fs]).
-template <bool DOWN, int BM, int WM, int NF>
+// x (gate/up, logits: [T][d] bf16) or h (down: hi and lo planes [T][S fs]
+// bf16) times the weights (gate/up: w13 [S][2 fs][d]; down: w2 [S][d][fs];
+// logits: w_router [E][d], rows past E read row E - 1 and are not stored).
+template <int MODE, int BM, int WM, int NF>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_gemm_lds(
     const uint16_t* __restrict__ a0, const uint16_t* __restrict__ a1,
-    const uint16_t* __restrict__ w, void* __restrict__ out, int T, int d, int fs, int S) {
-  using C = Tiles<DOWN, BM, WM, NF>;
+    const uint16_t* __restrict__ w, void* __restrict__ out, int T, int d, int fs, int S, int E) {
+  using C = Tiles<MODE, BM, WM, NF>;
+  constexpr bool DOWN = MODE == kDown;
   constexpr int MF = C::MF, kBM = BM, FW = C::FW;
   __shared__ __attribute__((aligned(16))) uint8_t sA[kRing * C::A_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sB[kRing * C::B_SLOT];
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int K = DOWN ? S * fs : d;                // contraction length
   const int nst = K / kBK;
   const int nf_t = fs / (C::WN * FW);             // gate/up n-tiles per expert
-  const int NT = DOWN ? d / C::BN : S * nf_t;
+  const int NT = DOWN ? d / C::BN : MODE == kLogits ? (E + C::BN - 1) / C::BN : S * nf_t;
   const int n_mt = (T + kBM - 1) / kBM;
   const ItemRange ir = item_range((long)NT * n_mt);
   const int it_first = (int)ir.first, it_end = (int)ir.end, it_step = (int)ir.step;
@@ -120,6 +127,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the gate rows of its FW features, then the matching up rows)
   auto wrow = [&](int nt, int r) -> size_t {
     if (DOWN) return (size_t)nt * C::BN + r;
+    if (MODE == kLogits) return (size_t)min(nt * C::BN + r, E - 1);
     const int se = nt / nf_t, ntf = nt - se * nf_t;
     const int cw = r / (16 * NF), nf = (r >> 4) % NF;
     return (size_t)se * 2 * fs + (nf >= NF / 2 ? fs : 0) + ntf * (C::WN * FW) + cw * FW +
@@ -227,7 +235,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-    if constexpr (DOWN) {
+    if constexpr (MODE == kLogits) {
+      float* l = static_cast<float*>(out);
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = (wm * MF + i) * 16 + lg * 4 + r;
+          if (m < rows) {
+            const int e0 = nt * C::BN + wn * (NF * 16) + ln;
+            float* lr = l + (size_t)(row0 + m) * E + e0;
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+              if (e0 + nf * 16 < E) lr[nf * 16] = acc[i][nf][r];
+          }
+        }
+    } else if constexpr (DOWN) {
       float* y = static_cast<float*>(out);
 #pragma unroll
       for (int i = 0; i < MF; ++i)
@@ -277,11 +300,11 @@ hipError_t shared_lds_pair(const k3moe_shape& s, const k3moe_expert_bank& b, con
   const int T = (int)s.T, S = b.n_experts, fs = b.f;
   uint16_t* hh = reinterpret_cast<uint16_t*>(h);
   const dim3 g(grouped_grid());   // one workgroup per CU
-  shared_gemm_lds<false, BM, WMG, NFG><<<g, 512, 0, st>>>(xb, nullptr, w13, hh, T, s.d, fs, S);
+  shared_gemm_lds<kGateUp, BM, WMG, NFG><<<g, 512, 0, st>>>(xb, nullptr, w13, hh, T, s.d, fs, S, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  shared_gemm_lds<true, BM, WMD, NFD><<<g, 512, 0, st>>>(hh, hh + (size_t)T * S * fs, w2, y, T,
-                                                        s.d, fs, S);
+  shared_gemm_lds<kDown, BM, WMD, NFD><<<g, 512, 0, st>>>(hh, hh + (size_t)T * S * fs, w2, y, T,
+                                                          s.d, fs, S, 0);
   return hipGetLastError();
 }
 
@@ -307,6 +330,21 @@ hipError_t launch_shared_lds(const k3moe_shape& s, const k3moe_expert_bank& b, c
   if (s.T <= 256) return shared_lds_pair<64, 2, 4, 2, 4>(s, b, x, h, y, st);
   if (s.T <= 640) return shared_lds_pair<128, 2, 4, 2, 4>(s, b, x, h, y, st);
   return shared_lds_pair<128, 1, 4, 2, 4>(s, b, x, h, y, st);
+}
+
+// The router's fp32 logits on the bf16 matrix cores: l[t][e] = x_t . w_e
+// (their bound does not depend on the order of the sum).  64-token tiles up to
+// 2048 tokens, 128 above (the whole route at 896 experts: 153 us at 512
+// tokens, 189 at 2048, 332 at 4096, 1.30 ms at 16384, against 172, 352, 477
+// and 1904 us with register-fed tiles; same ids and weights).
+hipError_t launch_router_logits_lds(const uint16_t* x, const uint16_t* wr, float* l, int T, int d,
+                                    int E, hipStream_t st) {
+  const dim3 g(grouped_grid());
+  if (T > 2048)
+    shared_gemm_lds<kLogits, 128, 2, 4><<<g, 512, 0, st>>>(x, nullptr, wr, l, T, d, 0, 0, E);
+  else
+    shared_gemm_lds<kLogits, 64, 2, 4><<<g, 512, 0, st>>>(x, nullptr, wr, l, T, d, 0, 0, E);
+  return hipGetLastError();
 }
 
 }  // namespace k3
