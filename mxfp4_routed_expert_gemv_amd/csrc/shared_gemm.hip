@@ -76,12 +76,13 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int r, int u) 
 // the router's bf16 logits (x [T][d] against w_router [E][d], fp32 out).
 constexpr int kGateUp = 0, kDown = 1, kLogits = 2;
 
-template <int MODE, int BM_, int WM_, int NF_>
+template <int MODE, int BM_, int WM_, int NF_, int NC_>
 struct Tiles {
   static constexpr bool DOWN = MODE == kDown;
   static constexpr int BM = BM_, WM = WM_, NF = NF_;
   static constexpr int NPL = DOWN ? 2 : 1;        // activation planes (h hi, h lo)
-  static constexpr int WN = 4 / WM;
+  static constexpr int NC = NC_;                  // compute waves
+  static constexpr int WN = NC / WM;
   static constexpr int MF = BM / 16 / WM;         // 16-row blocks per compute wave
   static constexpr int BN = WN * NF * 16;         // weight rows per n-tile
   static constexpr int FW = NF * 8;               // gate/up: features per wave
@@ -98,19 +99,20 @@ struct Tiles {
 // x (gate/up, logits: [T][d] bf16) or h (down: hi and lo planes [T][S fs]
 // bf16) times the weights (gate/up: w13 [S][2 fs][d]; down: w2 [S][d][fs];
 // logits: w_router [E][d], rows past E read row E - 1 and are not stored).
-template <int MODE, int BM, int WM, int NF>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_gemm_lds(
+template <int MODE, int BM, int WM, int NF, int NC = 4, int RING = kRing>
+__global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(NC / 4 + 1, NC / 4 + 1))) void shared_gemm_lds(
     const uint16_t* __restrict__ a0, const uint16_t* __restrict__ a1,
     const uint16_t* __restrict__ w, void* __restrict__ out, int T, int d, int fs, int S, int E) {
-  using C = Tiles<MODE, BM, WM, NF>;
+  using C = Tiles<MODE, BM, WM, NF, NC>;
   constexpr bool DOWN = MODE == kDown;
   constexpr int MF = C::MF, kBM = BM, FW = C::FW;
+  constexpr int kRing = RING;
   __shared__ __attribute__((aligned(16))) uint8_t sA[kRing * C::A_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sB[kRing * C::B_SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const bool copier = wv >= 4;
+  const bool copier = wv >= NC;
   const int K = DOWN ? S * fs : d;                // contraction length
   const int nst = K / kBK;
   const int nf_t = fs / (C::WN * FW);             // gate/up n-tiles per expert
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   if (copier) {
-    const int cq = wv - 4;
+    const int cq = wv - NC;
     const uint16_t* ap[C::NA];
     const uint16_t* bp[C::NB];
     int c_it = it_first, c_st = 0;
@@ -291,7 +293,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // h: T * S * fs * 4 bytes, written by the gate/up as two bf16 planes and
 // read back by the down.
-template <int BM, int WMG, int NFG, int WMD, int NFD>
+// One (gate/up, down) pair of tile shapes: BM tokens per m-tile, WM waves
+// along the tokens and NF weight fragments per wave for each, NC compute waves
+// (4 or 8; with 8, the rings hold 2 stages instead of 3).
+template <int BMG, int WMG, int NFG, int NCG, int BMD, int WMD, int NFD, int NCD>
 hipError_t shared_lds_pair(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
                            float* h, float* y, hipStream_t st) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
@@ -300,18 +305,20 @@ hipError_t shared_lds_pair(const k3moe_shape& s, const k3moe_expert_bank& b, con
   const int T = (int)s.T, S = b.n_experts, fs = b.f;
   uint16_t* hh = reinterpret_cast<uint16_t*>(h);
   const dim3 g(grouped_grid());   // one workgroup per CU
-  shared_gemm_lds<kGateUp, BM, WMG, NFG><<<g, 512, 0, st>>>(xb, nullptr, w13, hh, T, s.d, fs, S, 0);
+  constexpr int RG = NCG == 8 ? 2 : kRing, RD = NCD == 8 ? 2 : kRing;
+  shared_gemm_lds<kGateUp, BMG, WMG, NFG, NCG, RG><<<g, 64 * (NCG + 4), 0, st>>>(
+      xb, nullptr, w13, hh, T, s.d, fs, S, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  shared_gemm_lds<kDown, BM, WMD, NFD><<<g, 512, 0, st>>>(hh, hh + (size_t)T * S * fs, w2, y, T,
-                                                          s.d, fs, S, 0);
+  shared_gemm_lds<kDown, BMD, WMD, NFD, NCD, RD><<<g, 64 * (NCD + 4), 0, st>>>(
+      hh, hh + (size_t)T * S * fs, w2, y, T, s.d, fs, S, 0);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool shared_lds_ok(const k3moe_shape& s) {
-  return s.f_shared % 128 == 0 && s.d % 128 == 0;
+  return s.f_shared % 128 == 0 && s.d % 256 == 0;
 }
 
 // Tile shapes by batch (measured at d 7168, two experts of fs 2048; the
@@ -322,14 +329,19 @@ bool shared_lds_ok(const k3moe_shape& s) {
 //              took 125-181 us);
 //   T <= 256:  64-token tiles, waves 2 x 2: 69-79 us;
 //   T <= 640:  128-token tiles, waves 2 x 2: 120-128 us at 384-512 tokens;
-//   larger:    128-token tiles, gate/up waves side by side along the weights:
-//              0.24 ms at 1024 tokens, 0.97 ms at 4096, 3.5 ms at 16384.
+//   larger:    gate/up 128-token tiles with the waves side by side along the
+//              weights; down 128-token tiles of 256 outputs on 8 compute waves
+//              (2 x 4); from 2048 tokens the gate/up also takes 8 compute
+//              waves on 256-token tiles (2 x 4, each wave 128 tokens x 64
+//              rows).  0.22 ms at 1024 tokens, 0.90 ms at 4096, 3.2 ms at
+//              16384 (0.24, 1.00 and 3.5 ms with 4 compute waves; same bits).
 hipError_t launch_shared_lds(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
                              float* h, float* y, hipStream_t st) {
-  if (s.T <= 64) return shared_lds_pair<64, 4, 2, 4, 2>(s, b, x, h, y, st);
-  if (s.T <= 256) return shared_lds_pair<64, 2, 4, 2, 4>(s, b, x, h, y, st);
-  if (s.T <= 640) return shared_lds_pair<128, 2, 4, 2, 4>(s, b, x, h, y, st);
-  return shared_lds_pair<128, 1, 4, 2, 4>(s, b, x, h, y, st);
+  if (s.T <= 64) return shared_lds_pair<64, 4, 2, 4, 64, 4, 2, 4>(s, b, x, h, y, st);
+  if (s.T <= 256) return shared_lds_pair<64, 2, 4, 4, 64, 2, 4, 4>(s, b, x, h, y, st);
+  if (s.T <= 640) return shared_lds_pair<128, 2, 4, 4, 128, 2, 4, 4>(s, b, x, h, y, st);
+  if (s.T < 2048) return shared_lds_pair<128, 1, 4, 4, 128, 2, 4, 8>(s, b, x, h, y, st);
+  return shared_lds_pair<256, 2, 4, 8, 128, 2, 4, 8>(s, b, x, h, y, st);
 }
 
 // The router's fp32 logits on the bf16 matrix cores: l[t][e] = x_t . w_e

@@ -156,12 +156,13 @@ def test_mfma_class_batch_composition():
 def test_shared_tiles_keep_the_bits():
     """The shared experts' matrix-core GEMMs pick their tile shape by batch
     size (64-token tiles with the waves splitting the tokens up to 64 tokens,
-    64-token 2 x 2 tiles up to 256, 128-token 2 x 2 tiles up to 640, 128-token
-    tiles with the gate/up waves along the weights above), all on one chain per
-    output: a batch's shared outputs equal its prefixes' bit for bit."""
+    64-token 2 x 2 tiles up to 256, 128-token 2 x 2 tiles up to 640, then
+    8-compute-wave down tiles, and from 2048 tokens 256-token gate/up tiles),
+    all on one chain per output: a batch's shared outputs equal its prefixes'
+    bit for bit."""
     require_gpu()
     from mxfp4_routed_expert_gemv_amd import OP_SHARED_FFN, k3moe_shared_ffn
-    cfg = MED.with_tokens(1000)
+    cfg = MED.with_tokens(2100)
     wl = gen.device.build(cfg)
     L = k3layer(wl, "f32")
 
@@ -172,13 +173,13 @@ def test_shared_tiles_keep_the_bits():
         k3moe_shared_ffn(shape, L.shared_bank, x, y, L.workspace(shape, OP_SHARED_FFN))
         return y
 
-    full = shared(1000)
+    full = shared(2100)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(full).all())
-    for n in (32, 64, 65, 256, 257, 640, 641):
+    for n in (32, 64, 65, 256, 257, 640, 641, 2047):
         part = shared(n)
         torch.cuda.synchronize()
-        log(f"  {n} tokens against the first {n} of 1000")
+        log(f"  {n} tokens against the first {n} of 2100")
         assert torch.equal(part, full[:n]), n
 
 
