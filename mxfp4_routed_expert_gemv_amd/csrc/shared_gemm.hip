@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
 // One (gate/up, down) pair of tile shapes: BM tokens per m-tile, WM waves
 // along the tokens and NF weight fragments per wave for each, NC compute waves
 // (4 or 8; with 8, the rings hold 2 stages instead of 3).
-template <int BMG, int WMG, int NFG, int NCG, int BMD, int WMD, int NFD, int NCD>
+template <int BMG, int WMG, int NFG, int NCG, int BMD, int WMD, int NFD, int NCD, int RS = kRing>
 hipError_t shared_lds_pair(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
                            float* h, float* y, hipStream_t st) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
@@ -305,7 +305,7 @@ hipError_t shared_lds_pair(const k3moe_shape& s, const k3moe_expert_bank& b, con
   const int T = (int)s.T, S = b.n_experts, fs = b.f;
   uint16_t* hh = reinterpret_cast<uint16_t*>(h);
   const dim3 g(grouped_grid());   // one workgroup per CU
-  constexpr int RG = NCG == 8 ? 2 : kRing, RD = NCD == 8 ? 2 : kRing;
+  constexpr int RG = NCG == 8 ? 2 : RS, RD = NCD == 8 ? 2 : RS;
   shared_gemm_lds<kGateUp, BMG, WMG, NFG, NCG, RG><<<g, 64 * (NCG + 4), 0, st>>>(
       xb, nullptr, w13, hh, T, s.d, fs, S, 0);
   hipError_t err = hipGetLastError();
@@ -325,8 +325,9 @@ bool shared_lds_ok(const k3moe_shape& s) {
 // shared FFN, gate/up + down):
 //   T <= 64:   64-token tiles, the 4 waves splitting the tokens, n-tiles of
 //              16 features / 32 outputs (256 and 224 items: the weights spread
-//              over every CU): 50-53 us (the register-fed small-batch kernels
-//              took 125-181 us);
+//              over every CU), 4-slot rings: 42-44 us (50-53 us with 3 slots;
+//              5 to 8 slots gain nothing more; the register-fed small-batch
+//              kernels took 125-181 us);
 //   T <= 256:  64-token tiles, waves 2 x 2: 69-79 us;
 //   T <= 640:  128-token tiles, waves 2 x 2: 120-128 us at 384-512 tokens;
 //   larger:    gate/up 128-token tiles with the waves side by side along the
@@ -337,7 +338,7 @@ bool shared_lds_ok(const k3moe_shape& s) {
 //              16384 (0.24, 1.00 and 3.5 ms with 4 compute waves; same bits).
 hipError_t launch_shared_lds(const k3moe_shape& s, const k3moe_expert_bank& b, const void* x,
                              float* h, float* y, hipStream_t st) {
-  if (s.T <= 64) return shared_lds_pair<64, 4, 2, 4, 64, 4, 2, 4>(s, b, x, h, y, st);
+  if (s.T <= 64) return shared_lds_pair<64, 4, 2, 4, 64, 4, 2, 4, 4>(s, b, x, h, y, st);
   if (s.T <= 256) return shared_lds_pair<64, 2, 4, 4, 64, 2, 4, 4>(s, b, x, h, y, st);
   if (s.T <= 640) return shared_lds_pair<128, 2, 4, 4, 128, 2, 4, 4>(s, b, x, h, y, st);
   if (s.T < 2048) return shared_lds_pair<128, 1, 4, 4, 128, 2, 4, 8>(s, b, x, h, y, st);
