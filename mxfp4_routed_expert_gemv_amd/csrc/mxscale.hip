@@ -378,7 +378,9 @@ __host__ __device__ constexpr int newer_pairs(int RA, int RB, int NAW, int nbc2)
 // whole 128-byte lines per copy, each read once.
 // Q4: the quantised-activation mode (A in MXFP4, one pass; gate/up writes h
 // in MXFP4); otherwise A in exact E4M3 passes.
-template <int MF, int NF, int RA, int RB, bool DOWN, bool PB, bool Q4, int NC>
+// SR: the weight scales bypass LDS: each compute wave loads its rows' 4 scale
+// bytes of the next stage into registers (no scale ring, no scale copies).
+template <int MF, int NF, int RA, int RB, bool DOWN, bool PB, bool Q4, int NC, bool SR = false>
 __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(NC / 4 + 1, NC / 4 + 1))) void mx_gemm_scaled(
     const uint8_t* __restrict__ a_src, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ wsc, const int32_t* __restrict__ offsets,
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
                 "memory counter range");
   __shared__ __attribute__((aligned(16))) uint8_t sA[RA * A_SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t sB[PB ? RBP * B_SLOT_P : RB * B_SLOT];
-  __shared__ __attribute__((aligned(16))) uint8_t sS[SG * S_SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t sS[SR ? 16 : SG * S_SLOT];
   __shared__ int s_mt[kMaxE + 1];
   __shared__ int s_wave[NC + 4];
 
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
       for (int q = 0; q < NBCW; ++q)
         dma16_raw(bp[q] + b_st * (kBK / 2), base + (cq * (NBCW * 64) + q * 64) * 16);
     }
-    if ((s_st & 3) == 0) issue_scales(s_st >> 2, (g / 4 + 1) % SG, s_it < it_end);
+    if (!SR && (s_st & 3) == 0) issue_scales(s_st >> 2, (g / 4 + 1) % SG, s_it < it_end);
     if (++b_st == nst) {
       b_st = 0;
       b_it += it_step;
@@ -563,13 +565,15 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
     b_setup();
     if (s_it < it_end) s_setup();
     // scales of the first item's first group (older than every counted copy)
-    int mt, nt;
-    const int e = item_tile(s_mt, E, it_first, NT, G, mt, nt);
+    if constexpr (!SR) {
+      int mt, nt;
+      const int e = item_tile(s_mt, E, it_first, NT, G, mt, nt);
 #pragma unroll
-    for (int q = 0; q < BROWS / 256; ++q) {
-      const int r0 = cq * (BROWS / 4) + q * 64;
-      dma16_raw(wsc + ((size_t)e * e_rows + grow(nt, r0 + lane)) * s_row,
-                sS_lds + (uint32_t)(r0 * 16));
+      for (int q = 0; q < BROWS / 256; ++q) {
+        const int r0 = cq * (BROWS / 4) + q * 64;
+        dma16_raw(wsc + ((size_t)e * e_rows + grow(nt, r0 + lane)) * s_row,
+                  sS_lds + (uint32_t)(r0 * 16));
+      }
     }
   }
   if (copier) {
@@ -594,6 +598,36 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
   }
 
   int g = 0;   // global stage index of this workgroup
+  // SR: each compute wave loads its own rows' scale words (4 bytes: a row's 4
+  // blocks of one stage) straight into registers, one stage ahead; the
+  // cursor crosses item boundaries.  Fragment nf's rows sit nf_off(nf) rows
+  // after fragment 0's.
+  int sc_it = it_first, sc_st = 0;
+  const uint8_t* scp = nullptr;
+  uint32_t sc_c[NF], sc_n[NF];
+  auto nf_off = [&](int nf) -> int {
+    return DOWN ? nf * 16 : (nf >= NF / 2 ? f : 0) + (nf % (NF / 2)) * 16;
+  };
+  auto sc_setup = [&]() {
+    int mt, nt;
+    const int e = item_tile(s_mt, E, sc_it, NT, G, mt, nt);
+    scp = wsc + ((size_t)e * e_rows + grow(nt, wv * WROWS + ln)) * s_row;
+  };
+  auto sc_load = [&](uint32_t (&w)[NF]) {
+    if (sc_it >= it_end) return;
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf)
+      w[nf] = *reinterpret_cast<const uint32_t*>(scp + (size_t)nf_off(nf) * s_row + sc_st * 4);
+    if (++sc_st == nst) {
+      sc_st = 0;
+      sc_it += it_step;
+      if (sc_it < it_end) sc_setup();
+    }
+  };
+  if constexpr (SR) {
+    if (sc_it < it_end) sc_setup();
+    sc_load(sc_c);
+  }
   // One item with NMB m-blocks (16 rows each) holding rows of the tile: the
   // stage loop and epilogue are specialised on NMB, so the accumulators stay
   // in the matrix-core registers and no MFMA sits behind a branch.
@@ -606,6 +640,7 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
       for (int nf = 0; nf < NF; ++nf) acc[i][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int s = 0; s < nst; ++s, ++g) {
+      if constexpr (SR) sc_load(sc_n);
       wait_lds();
       wg_barrier();
       const uint8_t* abase = sA + (g % RA) * A_SLOT;
@@ -616,7 +651,8 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) {
         const int r = wv * WROWS + nf * 16 + ln;
-        bs[nf] = sbase[r * 16];
+        if constexpr (SR) bs[nf] = (int)((sc_c[nf] >> (8 * lg)) & 0xFFu);
+        else bs[nf] = sbase[r * 16];
         const uint4 c = *reinterpret_cast<const uint4*>(
             PB ? bbase + step_block_off(r, g & 1, lg)
                : bbase + r * 64 + ((lg ^ ((r >> 1) & 3)) * 16));
@@ -662,6 +698,10 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
           for (int nf = 0; nf < NF; ++nf)
             acc[i][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 a[ab][p], bq[nf], acc[i][nf], A_FMT, 4, 0, as[ab][p], 0, bs[nf]);
+      }
+      if constexpr (SR) {
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) sc_c[nf] = sc_n[nf];
       }
     }
     if (DOWN) {
@@ -1283,14 +1323,20 @@ hipError_t launch_down_scaled(const k3moe_shape& s, const k3moe_expert_bank& b, 
       mx_gemm_scaled<MF, NF, RA, RB, true, PB, false, NC><<<g, 64 * (NC + 4), 0, st>>>(       \
           hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);                             \
   } while (0)
-  // The same tiles as the gate/up; the tall exact ones keep 4 compute waves
-  // (the 3-pass activation slots leave no LDS for 512-row weight stages).
+  // The same tiles as the gate/up.  The tall exact ones take 8 compute waves
+  // with their weight scales in registers (SR): the 3-pass activation slots
+  // leave no LDS for a scale ring beside 512-row weight stages (2.98 -> 2.67
+  // ms on a uniform 4096-token batch, 10.75 -> 9.11 ms on the Zipf 16384-token
+  // one, against 4 compute waves; same bits).  Scales in registers slow the
+  // gate/up (4.83 -> 5.62 ms), whose LDS holds its scale ring.
   if (mf <= 1) K3_SD(1, 4, 4, 4, true, 4);
   else if (mf <= 3) K3_SD(3, 4, 2, 5, false, 4);
   else if (q4)
     mx_gemm_scaled<8, 4, 3, 4, true, true, true, 4><<<g, 512, 0, st>>>(
         hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);
-  else K3_SD(6, 4, 2, 3, false, 4);
+  else
+    mx_gemm_scaled<6, 4, 2, 2, true, false, false, 8, true><<<g, 768, 0, st>>>(
+        hb, w, ws, offsets, nullptr, y, s.d, s.f, s.E, s.k, G);
 #undef K3_SD
   return hipGetLastError();
 }
