@@ -876,12 +876,14 @@ __global__ __launch_bounds__(64 * NW) void route_refine(const uint16_t* __restri
   }
 }
 
-void launch_router_bf16(const uint16_t* x, const uint16_t* wr, const RouteWs& ws, int T, int d,
-                        int E, int k, const RouterMode& rm, hipStream_t st) {
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const RouteWs& ws, int T,
+                              int d, int E, int k, const RouterMode& rm, hipStream_t st) {
   router_wnorm<<<(E + 3) / 4, 256, 0, st>>>(wr, ws.wnorm, d, E);
-  launch_router_logits_lds(x, wr, ws.lbound, T, d, E, st);
+  hipError_t err = launch_router_logits_lds(x, wr, ws.lbound, T, d, E, st);
+  if (err != hipSuccess) return err;
   route_refine<4><<<(T + 3) / 4, 256, 0, st>>>(x, wr, ws.wnorm, ws.logits, ws.lbound, T, d, E, k,
                                               rm);
+  return hipGetLastError();
 }
 
 // fp64 logits to the fp32 output
@@ -980,10 +982,11 @@ hipError_t launch_route(const k3moe_shape& s, const void* x, const uint16_t* wr,
     // bf16 logits, the candidates refined in fp64, the selection; the fp64
     // logits of every expert only when the caller asks for them
     const uint16_t* xb = static_cast<const uint16_t*>(x);
-    launch_router_bf16(xb, wr, ws, T, s.d, s.E, s.k, rm, st);
+    hipError_t err = launch_router_bf16(xb, wr, ws, T, s.d, s.E, s.k, rm, st);
+    if (err != hipSuccess) return err;
     topk_softmax<false><<<T, 64, 0, st>>>(ws.logits, ws.lbound, x, wr, idx, w, nullptr, diag, T,
                                           s.d, s.E, s.k, perm, rm);
-    hipError_t err = hipGetLastError();
+    err = hipGetLastError();
     if (err != hipSuccess || !logits_out) return err;
     launch_router_mfma(xb, wr, ws.logits, ws.lbound, T, s.d, s.E, st);
     const int64_t n = (int64_t)T * s.E;

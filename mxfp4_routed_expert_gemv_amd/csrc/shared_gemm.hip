@@ -123,7 +123,6 @@ __global__ __launch_bounds__(64 * (NC + 4)) __attribute__((amdgpu_waves_per_eu(N
   const int n_items = it_first < it_end ? (it_end - it_first + it_step - 1) / it_step : 0;
   const int g_total = n_items * nst;
   const size_t a_row = (size_t)K;                 // elements per activation row (each plane)
-  const size_t plane = (size_t)T * K;             // elements per activation plane
 
   // weight row of local row r of n-tile nt (gate/up: wave r / (16 NF) owns
   // the gate rows of its FW features, then the matching up rows)
