@@ -74,6 +74,20 @@ __global__ __launch_bounds__(256) void rvq_partial(const void* __restrict__ v_sr
   __syncthreads();
   const int e = s_e;
   const float* cbe = cb + (size_t)e * 3 * 256 * 8;
+  const size_t mat = (size_t)e * 3 * nsl * rows;     // this expert's first index chunk
+  const uint8_t* ib = idx + mat * 16;
+  // rows r = tid + 256 i, their 3 x 16 index bytes DQ rows ahead of use; the
+  // first DQ rows' are requested before the table is built
+  constexpr int DQ = 4;
+  auto load_row = [&](int r, uint4 (&iv)[3]) {
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      iv[s] = *reinterpret_cast<const uint4*>(ib + (((size_t)s * nsl + slice) * rows + r) * 16);
+  };
+  uint4 buf[DQ][3];
+#pragma unroll
+  for (int j = 0; j < DQ; ++j)
+    if (tid + 256 * j < rows) load_row(tid + 256 * j, buf[j]);
   // table: entry (s * 16 + g) * 256 + j.  Thread t loads codeword (s, j) once
   // (3 of the 768 per thread) and writes its 16 dot products, one per group.
   for (int c = tid; c < 3 * 256; c += 256) {
@@ -95,33 +109,26 @@ __global__ __launch_bounds__(256) void rvq_partial(const void* __restrict__ v_sr
     }
   }
   __syncthreads();
-  const size_t mat = (size_t)e * 3 * nsl * rows;     // this expert's first index chunk
-  const uint8_t* ib = idx + mat * 16;
-  // rows r = tid + 256 i; the next row's index loads are issued before this
-  // row's lookups
-  auto load_row = [&](int r, uint4 (&iv)[3]) {
+  for (int r0 = tid; r0 < rows; r0 += 256 * DQ) {
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
-      iv[s] = *reinterpret_cast<const uint4*>(ib + (((size_t)s * nsl + slice) * rows + r) * 16);
-  };
-  uint4 cur[3], nxt[3];
-  int r = tid;
-  if (r < rows) load_row(r, cur);
-  for (; r < rows; r += 256) {
-    if (r + 256 < rows) load_row(r + 256, nxt);
-    float acc = 0.0f;
+    for (int jq = 0; jq < DQ; ++jq) {
+      const int r = r0 + 256 * jq;
+      if (r < rows) {
+        const uint4 cur[3] = {buf[jq][0], buf[jq][1], buf[jq][2]};
+        if (r + 256 * DQ < rows) load_row(r + 256 * DQ, buf[jq]);
+        float acc = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const uint32_t w4[4] = {cur[s].x, cur[s].y, cur[s].z, cur[s].w};
+        for (int s = 0; s < 3; ++s) {
+          const uint32_t w4[4] = {cur[s].x, cur[s].y, cur[s].z, cur[s].w};
 #pragma unroll
-      for (int g = 0; g < kRvqGroups; ++g) {
-        const uint32_t i = (w4[g >> 2] >> (8 * (g & 3))) & 0xFFu;
-        acc += tab[(s * kRvqGroups + g) * 256 + i];
+          for (int g = 0; g < kRvqGroups; ++g) {
+            const uint32_t i = (w4[g >> 2] >> (8 * (g & 3))) & 0xFFu;
+            acc += tab[(s * kRvqGroups + g) * 256 + i];
+          }
+        }
+        part[((size_t)q * nsl + slice) * rows + r] = acc;
       }
     }
-    part[((size_t)q * nsl + slice) * rows + r] = acc;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) cur[s] = nxt[s];
   }
 }
 
