@@ -909,10 +909,11 @@ void launch_router_mfma(const uint16_t* x, const uint16_t* wr, double* logits, f
                                                                              lbound, T, d, E);
 }
 
-// One token: the selection (wave 0 of workgroup 0) runs beside the shared
-// experts' gate/up (every other wave takes one (expert, feature) item), which
-// does not depend on the routing.  Workgroups of 4 waves; x is staged in LDS
-// by every workgroup before the roles split, and no barrier follows.
+// One token: the selection (wave 0 of workgroup 0, the workgroup's only
+// working wave) runs beside the shared experts' gate/up (every wave of the
+// other workgroups takes one (expert, feature) item), which does not depend
+// on the routing.  Workgroups of 4 waves; the streaming workgroups stage x in
+// LDS, pass one barrier, and no barrier follows.
 __global__ __launch_bounds__(256) void topk_shared_t1(
     const double* __restrict__ logits, const float* __restrict__ lbound,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
@@ -921,16 +922,19 @@ __global__ __launch_bounds__(256) void topk_shared_t1(
     int S, RouterMode rm) {
   __shared__ TopkLds sm;
   __shared__ uint4 xs[kSgU * kWave];
+  const int lane = threadIdx.x & 63;
+  // workgroup 0: the selection alone (its wave 0), without the x staging and
+  // barrier the streaming workgroups need (layer 105.6 -> 103.6 us)
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < kWave)
+      topk_token<false>(0, lane, sm, logits, lbound, x, wr, idx_out, w_out, nullptr, diag, d, E,
+                        k, perm, rm);
+    return;
+  }
   stage_row(reinterpret_cast<const uint4*>(x), d / 8, xs);
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (gw == 0) {
-    topk_token<false>(0, lane, sm, logits, lbound, x, wr, idx_out, w_out, nullptr, diag, d, E, k,
-                      perm, rm);
-  } else if (gw - 1 < S * fs) {
-    shared_gateup_item(gw - 1, w13s, xs, hs, d, fs, lane);
-  }
+  const int gw = (blockIdx.x - 1) * 4 + (threadIdx.x >> 6);
+  if (gw < S * fs) shared_gateup_item(gw, w13s, xs, hs, d, fs, lane);
 }
 
 }  // namespace
@@ -962,7 +966,7 @@ hipError_t launch_topk_shared_t1(const k3moe_shape& s, const void* x, const uint
   RouterMode rm;
   rm.mode = s.router;
   rm.bias = bias;
-  topk_shared_t1<<<(items + 1 + 3) / 4, 256, 0, st>>>(
+  topk_shared_t1<<<1 + (items + 3) / 4, 256, 0, st>>>(
       ws.logits, ws.lbound, static_cast<const uint16_t*>(x), wr, idx, w, diag, s.d, s.E, s.k, perm,
       static_cast<const uint16_t*>(shared.w13), hs, shared.f, shared.n_experts, rm);
   return hipGetLastError();
