@@ -132,6 +132,102 @@ __global__ __launch_bounds__(256) void rvq_partial(const void* __restrict__ v_sr
   }
 }
 
+// The same partial sums with one stage's table in LDS at a time (16 KB, so
+// that 4 workgroups fit a CU and a one-token batch's workgroups all run at
+// once): the table of stage s is built, every row of the thread adds its 16
+// entries of stage s to its running sum (registers, up to 16 rows a thread),
+// then the next stage's table replaces it.  Each row's sum takes the same
+// entries in the same order as rvq_partial, so the bits are the same.  Used
+// for the gate/up (2f <= 4096 rows); the down keeps rvq_partial.
+constexpr int kRvqRowsPerThread = 16;   // rows <= 256 * kRvqRowsPerThread
+template <bool GATEUP, bool XF32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void rvq_partial_staged(const void* __restrict__ v_src,
+                                                          const uint8_t* __restrict__ idx,
+                                                          const float* __restrict__ cb,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ sorted_pair,
+                                                          float* __restrict__ part, int rows,
+                                                          int cols, int E, int k) {
+  constexpr int RB = 8;                     // rows whose indices are loaded together
+  constexpr int RMAX = kRvqRowsPerThread;
+  __shared__ float tab[kRvqGroups * 256];
+  __shared__ float vs[kRvqSlice];
+  __shared__ int s_e;
+  const int q = blockIdx.x, slice = blockIdx.y, tid = threadIdx.x;
+  const int nsl = cols / kRvqSlice;
+  if (tid == 0) s_e = q < offsets[E] ? rvq_expert_of(offsets, E, q) : -1;
+  __syncthreads();
+  if (s_e < 0) return;
+  if (tid < kRvqSlice) {
+    const int c = slice * kRvqSlice + tid;
+    float val;
+    if (GATEUP) {
+      const size_t t = (size_t)(sorted_pair[q] / k);
+      val = XF32 ? static_cast<const float*>(v_src)[t * cols + c]
+                 : __uint_as_float((uint32_t)static_cast<const uint16_t*>(v_src)[t * cols + c]
+                                   << 16);
+    } else {
+      val = static_cast<const float*>(v_src)[(size_t)q * cols + c];
+    }
+    vs[tid] = val;
+  }
+  const int e = s_e;
+  const float* cbe = cb + (size_t)e * 3 * 256 * 8;
+  const uint8_t* ib = idx + (size_t)e * 3 * nsl * rows * 16;
+  const int nr = (rows + 255) / 256;
+  float acc[RMAX];
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) acc[i] = 0.0f;
+  for (int s = 0; s < 3; ++s) {
+    __syncthreads();   // vs written (s = 0); the previous stage's lookups done
+    {
+      // entry g * 256 + j of stage s: thread j's codeword against group g
+      const float4 c0 = *reinterpret_cast<const float4*>(cbe + (size_t)(s * 256 + tid) * 8);
+      const float4 c1 = *reinterpret_cast<const float4*>(cbe + (size_t)(s * 256 + tid) * 8 + 4);
+#pragma unroll 4
+      for (int g = 0; g < kRvqGroups; ++g) {
+        const float* vg = vs + g * 8;
+        float a = c0.x * vg[0];
+        a = __builtin_fmaf(c0.y, vg[1], a);
+        a = __builtin_fmaf(c0.z, vg[2], a);
+        a = __builtin_fmaf(c0.w, vg[3], a);
+        a = __builtin_fmaf(c1.x, vg[4], a);
+        a = __builtin_fmaf(c1.y, vg[5], a);
+        a = __builtin_fmaf(c1.z, vg[6], a);
+        a = __builtin_fmaf(c1.w, vg[7], a);
+        tab[g * 256 + tid] = a;
+      }
+    }
+    __syncthreads();
+    const uint8_t* is = ib + ((size_t)s * nsl + slice) * rows * 16;
+#pragma unroll
+    for (int i0 = 0; i0 < RMAX; i0 += RB) {
+      if (i0 < nr) {
+        uint4 iv[RB];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          const int r = min(tid + 256 * (i0 + j), rows - 1);
+          iv[j] = *reinterpret_cast<const uint4*>(is + (size_t)r * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          const uint32_t w4[4] = {iv[j].x, iv[j].y, iv[j].z, iv[j].w};
+          float a = acc[i0 + j];
+#pragma unroll
+          for (int g = 0; g < kRvqGroups; ++g)
+            a += tab[g * 256 + ((w4[g >> 2] >> (8 * (g & 3))) & 0xFFu)];
+          acc[i0 + j] = a;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) {
+    const int r = tid + 256 * i;
+    if (i < nr && r < rows) part[((size_t)q * nsl + slice) * rows + r] = acc[i];
+  }
+}
+
 // h[q][j] = silu(g) * u with g, u the slice sums (in slice order) of rows j
 // and f + j; the loads of 8 slices are issued before they are added.
 __global__ __launch_bounds__(64) void rvq_reduce_gateup(const float* __restrict__ part,
@@ -197,7 +293,18 @@ hipError_t launch_gateup_rvq(const k3moe_shape& s, const k3moe_expert_bank& b, c
   const dim3 g((unsigned)P, s.d / kRvqSlice);
   const uint8_t* idx = static_cast<const uint8_t*>(b.w13);
   const float* cb = static_cast<const float*>(b.w13_scale);
-  if (s.x_dtype == K3MOE_F32)
+  // one stage's table at a time where the rows fit the registers: 4
+  // workgroups a CU instead of 3, so a one-token batch's 896 workgroups run
+  // in one round (gate/up 0.366 -> 0.392 of the HBM peak at one token;
+  // decode_b64 layer 3.56 -> 3.50 ms; same bits)
+  const bool staged = 2 * s.f <= 256 * kRvqRowsPerThread;
+  if (staged && s.x_dtype == K3MOE_F32)
+    rvq_partial_staged<true, true><<<g, 256, 0, st>>>(x, idx, cb, offsets, sorted_pair, part,
+                                                     2 * s.f, s.d, s.E, s.k);
+  else if (staged)
+    rvq_partial_staged<true, false><<<g, 256, 0, st>>>(x, idx, cb, offsets, sorted_pair, part,
+                                                      2 * s.f, s.d, s.E, s.k);
+  else if (s.x_dtype == K3MOE_F32)
     rvq_partial<true, true><<<g, 256, 0, st>>>(x, idx, cb, offsets, sorted_pair, part, 2 * s.f,
                                               s.d, s.E, s.k);
   else
@@ -215,8 +322,8 @@ hipError_t launch_down_rvq(const k3moe_shape& s, const k3moe_expert_bank& b, con
   const int64_t P = s.T * s.k;
   const dim3 g((unsigned)P, s.f / kRvqSlice);
   rvq_partial<false, true><<<g, 256, 0, st>>>(h, static_cast<const uint8_t*>(b.w2),
-                                             static_cast<const float*>(b.w2_scale), offsets,
-                                             nullptr, part, s.d, s.f, s.E, s.k);
+                                               static_cast<const float*>(b.w2_scale), offsets,
+                                               nullptr, part, s.d, s.f, s.E, s.k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t n = P * s.d;
