@@ -60,6 +60,7 @@ HOST = "_hostcache"  # suffix: routed experts in pinned host memory behind an HB
 CACHE_SLOTS = 128
 PCIE_PEAK_GBS = 64.0               # PCIe 5.0 x16, one direction (the host link's published rate)
 KERNEL_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "mxscale.hip")
+RVQ_SRC = os.path.join(ROOT, "mxfp4_routed_expert_gemv_amd", "csrc", "rvq.hip")
 
 
 def log(msg):
@@ -67,12 +68,13 @@ def log(msg):
 
 
 def pmc_file(workload: str) -> str:
-    kernel = "gateup_1tok" if workload == "decode_b1" else "mx_gemm_scaled"
+    kernel = ("gateup_1tok" if workload == "decode_b1" else
+              "rvq_partial" if workload.endswith(RVQ) else "mx_gemm_scaled")
     return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
+def kernel_source_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
@@ -86,7 +88,8 @@ def stored_traffic(workload: str):
     text = open(path).read()
     m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_h or not m_t or m_h.group(1) != kernel_source_hash():
+    src = RVQ_SRC if workload.endswith(RVQ) else KERNEL_SRC
+    if not m_h or not m_t or m_h.group(1) != kernel_source_hash(src):
         return None
     return float(m_t.group(1))
 
@@ -460,7 +463,7 @@ def run_workload(name, args, weights):
     else:
         roof = {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": ("rvq_partial + rvq_reduce_gateup" if rvq
+                "kernel": ("rvq_partial_staged + rvq_reduce_gateup" if rvq
                            else "gateup_1tok" if T == 1 and routed_scaled
                            else "mx_gemm_scaled (gate/up)" if routed_scaled
                            else "gateup_persistent"),
